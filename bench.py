@@ -1,0 +1,196 @@
+#!/usr/bin/env python3
+"""Benchmark of the deterministic attention backward on one MI355X.
+
+A step is one call of the backward (preprocess D = rowsum(dO*O), the main
+kernel with the ordered dQ reduction, and for the atomic variant the dQ
+finalize) over the workload's synthetic inputs, which are resident in HBM
+before timing starts.  The forward pass that produces O and lse runs once,
+untimed.  Throughput uses the FlashAttention FLOP convention
+(5 contractions x 2*s*s*d per head, halved under the causal mask).
+
+Prints ONE JSON line on stdout; progress goes to stderr.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
+PEAK_FP32_MFMA_TFLOPS = 157.3
+METRIC = "deterministic attn-bwd TFLOPS (bf16, 1 GPU) & % of MFMA peak; vs non-det"
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_bwd_main_s8k_d128_full_shift.json")
+KERNEL_SOURCE = os.path.join(ROOT, "tile_scheduling_attn_amd", "csrc", "bwd_kernels.hip")
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+def kernel_source_sha():
+    with open(KERNEL_SOURCE, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()
+
+
+def traffic_per_launch(workload, schedule):
+    """HBM bytes per launch of the main kernel from the committed rocprofv3
+    PMC summary, if it was taken on the current kernel source."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if t.get("source_sha256") != kernel_source_sha():
+        return None
+    if t.get("workload") != workload or t.get("schedule") != schedule:
+        return None
+    return t.get("hbm_bytes_per_launch")
+
+
+def time_calls(tsa, pb, schedule, steps, warmup, torch):
+    out = [torch.empty_like(pb.q) for _ in range(3)]
+    stream = torch.cuda.current_stream()
+    for _ in range(warmup):
+        pb.run(schedule, out=out)
+    torch.cuda.synchronize()
+    tsa.attn_bwd_set_timing(True)
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    start.record(stream)
+    for _ in range(steps):
+        pb.run(schedule, out=out)
+    end.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    tsa.attn_bwd_set_timing(False)
+    pre, main, fin = tsa.attn_bwd_get_kernel_times()
+    rc = tsa.attn_bwd_query_status()
+    if rc != 0:
+        raise RuntimeError(f"device status {rc}: {tsa.last_error()}")
+    return {"ms_per_step": start.elapsed_time(end) / steps, "wall_s": wall,
+            "ms_preprocess": pre, "ms_main": main, "ms_finalize": fin}
+
+
+def cpu_baseline(pb, heads, flops_per_head):
+    """The fp64 oracle backward (as it stands) on `heads` heads of the same
+    workload, using the O and lse of the forward pass; backward stage only."""
+    import numpy as np
+    import oracle
+    oracle.build(force=False)
+    H = pb.b * pb.h
+    sel = list(range(min(heads, H)))
+    g = lambda x: x.reshape(H, pb.s, pb.d)[sel]
+    o = pb.o.float().cpu().numpy().reshape(H, pb.s, pb.d)[sel]
+    lse = pb.lse.cpu().numpy().reshape(H, pb.s)[sel]
+    t0 = time.perf_counter()
+    oracle.attn_bwd(g(pb.qn), g(pb.kn), g(pb.vn), o, g(pb.don), lse, pb.causal, pb.scale)
+    dt = time.perf_counter() - t0
+    return {"value": round(flops_per_head * len(sel) / dt / 1e12, 6), "unit": "TFLOPS",
+            "cores": oracle.num_threads(), "kind": "oracle",
+            "sample": f"{len(sel)} of {H} heads (s={pb.s}, d={pb.d}, "
+                      f"{'causal' if pb.causal else 'full'} mask), fp64 backward stage only, "
+                      f"{dt:.1f} s; same FLOP convention"}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="s8k_d128_full")
+    ap.add_argument("--causal", type=int, default=None, help="override the workload's mask")
+    ap.add_argument("--schedule", default=None, help="default: shift (full) / descending (causal)")
+    ap.add_argument("--compare", default="naive,atomic",
+                    help="comma list of schedules also timed for context ('' for none)")
+    ap.add_argument("--cpu-heads", type=int, default=4, help="heads in the CPU oracle sample (0: skip)")
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one GPU only: this path has no multi-GPU mode "
+              "(heads shard across GPUs without communication; see the design notes).",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import tile_scheduling_attn_amd as tsa
+    import workloads
+    from tests.support import Problem
+
+    wl = workloads.WORKLOADS[args.workload]
+    causal = (wl.masks[0] == "causal") if args.causal is None else bool(args.causal)
+    schedule = args.schedule or ("descending" if causal else "shift")
+    log(f"workload {wl.name}: b={wl.b} h={wl.h} s={wl.s} d={wl.d} {wl.dtype} "
+        f"{'causal' if causal else 'full'}; schedule {schedule}")
+    pb = Problem(wl.b, wl.h, wl.s, wl.d, wl.dtype, wl.seed, causal)
+    torch.cuda.synchronize()
+    flops = wl.flops(causal)
+
+    res = time_calls(tsa, pb, schedule, args.steps, args.warmup, torch)
+    tflops = flops / (res["ms_per_step"] * 1e-3) / 1e12
+    main_tflops = flops / (res["ms_main"] * 1e-3) / 1e12
+    log(f"{schedule}: {res['ms_per_step']:.3f} ms/step, {tflops:.1f} TFLOPS "
+        f"(main kernel {res['ms_main']:.3f} ms, {main_tflops:.1f} TFLOPS)")
+
+    extra = {}
+    for other in [x for x in args.compare.split(",") if x and x != schedule]:
+        if other == "symmetric_shift" and causal and (wl.s // 128) % 2:
+            continue
+        r2 = time_calls(tsa, pb, other, max(5, args.steps // 2), 2, torch)
+        t2 = flops / (r2["ms_per_step"] * 1e-3) / 1e12
+        extra[other] = {"ms_per_step": round(r2["ms_per_step"], 4), "tflops": round(t2, 2),
+                        "ms_main": round(r2["ms_main"], 4)}
+        log(f"{other}: {r2['ms_per_step']:.3f} ms/step, {t2:.1f} TFLOPS")
+
+    peak = PEAK_BF16_TFLOPS if wl.dtype == "bf16" else PEAK_FP32_MFMA_TFLOPS
+    roofline = {"bound": "mfma", "achieved": round(main_tflops, 2), "peak": peak,
+                "unit": "TFLOP/s", "frac": round(main_tflops / peak, 4),
+                "traffic": traffic_per_launch(wl.name, schedule),
+                "kernel": "bwd_main_kernel",
+                "algorithmic_flop_per_launch": flops}
+
+    cpu = None
+    if args.cpu_heads > 0:
+        log(f"timing the CPU oracle on {args.cpu_heads} head(s)")
+        cpu = cpu_baseline(pb, args.cpu_heads, flops / (wl.b * wl.h))
+        log(f"cpu oracle: {cpu['value']} TFLOPS on {cpu['cores']} threads")
+
+    line = {
+        "metric": METRIC,
+        "value": round(tflops, 2),
+        "unit": "TFLOPS",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(res["ms_per_step"], 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": wl.dtype,
+        "data": "synthetic: Q,K,V,dO ~ N(0,1) (PCG64, seeded), O and lse from an fp32 forward",
+        "config": {"workload": f"{wl.name}: b={wl.b} h={wl.h} s={wl.s} d={wl.d} "
+                               f"{'causal' if causal else 'full'} mask, schedule {schedule}",
+                   "b": wl.b, "h": wl.h, "s": wl.s, "d": wl.d, "causal": causal,
+                   "schedule": schedule, "tile": tsa.attn_bwd_tile_size(wl.dtype)},
+        "pct_of_peak": round(100 * tflops / peak, 2),
+        "kernel_ms": {"preprocess": round(res["ms_preprocess"], 4), "main": round(res["ms_main"], 4),
+                      "finalize": round(res["ms_finalize"], 4)},
+        "compare": extra,
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+    }
+    if "atomic" in extra:
+        line["det_over_nondet"] = round(tflops / extra["atomic"]["tflops"], 4)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

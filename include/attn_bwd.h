@@ -1,0 +1,191 @@
+/*
+ * attn_bwd.h - C ABI of libattn_bwd.so, a deterministic attention backward
+ * pass for AMD Instinct MI355X (gfx950) scheduled with DASH.
+ *
+ * Source of the method: "DASH: Deterministic Attention Scheduling for
+ * High-throughput Reproducible LLM Training" (arXiv 2601.21824), as
+ * described by its summary page (sections Problem, Approach, Key results)
+ * and its pith.science review page (sections "What carries the argument",
+ * "Core claim", Axiom ledger, Fig. 1, 3, 4, 6, 7 captions).
+ *
+ * The backward computes, per head, the exact softmax-attention gradient
+ *   D_i = <dO_i, O_i>,  P_ij = exp(scale <q_i,k_j> - lse_i),
+ *   dS_ij = P_ij (<dO_i, v_j> - D_i),
+ *   dV_j = sum_i P_ij dO_i,  dK_j = scale sum_i dS_ij q_i,
+ *   dQ_i = scale sum_j dS_ij k_j
+ * tiled into square T x T tiles (T = 128 for bf16, 64 for fp32).  Each work
+ * group owns one KV tile at a time (Fig. 1: local dK/dV accumulation) and
+ * adds its partial dQ of every Q tile into a global fp32 accumulator in an
+ * order fixed by the schedule (Problem section: the serialised dQ
+ * reduction), so the results are bitwise reproducible.
+ *
+ * Conventions shared by every entry point:
+ *  - Tensors are contiguous [b][h][s][d] (lse is [b][h][s], fp32, natural
+ *    log of the scaled logits, as produced by the forward pass).
+ *  - All tensor pointers are DEVICE pointers of the current HIP device,
+ *    16-byte aligned.  The caller owns every tensor and the stream; the
+ *    library never frees caller memory.  dq, dk, dv are fully overwritten.
+ *  - Under the causal mask query i sees keys j <= i (s_q = s_k).
+ *  - Calls are asynchronous on the stream; device-side failures (a bounded
+ *    flag wait that expired) are reported by attn_bwd_query_status().
+ *  - Return value: ATTN_OK (0) or a negative attn_status_t.  No C++
+ *    exception crosses the ABI.  attn_bwd_last_error() gives a message for
+ *    the last failure on the calling thread.
+ */
+#ifndef ATTN_BWD_H
+#define ATTN_BWD_H
+
+#include <stddef.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Schedules.  NAIVE is the FlashAttention-3 order (Fig. 3: Q tiles ascending,
+ * dQ accumulated in ascending KV order).  DESCENDING is Descending Q-Tile
+ * Iteration (Fig. 4; same dQ order as NAIVE).  SHIFT is Shift Scheduling
+ * (Fig. 6: the owner of KV tile i visits Q tiles i, i+1, ..., wrapping; dQ_j
+ * accumulated in visiting order).  SYMMETRIC_SHIFT is Symmetric Shift
+ * Scheduling with two-phase workload folding for the causal mask (Fig. 7;
+ * equals SHIFT under the full mask; needs an even tile count when causal).
+ * ATOMIC is the non-deterministic comparison point: unordered fp32 atomic
+ * dQ additions (Problem section: the non-deterministic counterpart). */
+typedef enum {
+    ATTN_SCHED_NAIVE = 0,
+    ATTN_SCHED_DESCENDING = 1,
+    ATTN_SCHED_SHIFT = 2,
+    ATTN_SCHED_SYMMETRIC_SHIFT = 3,
+    ATTN_SCHED_ATOMIC = 4
+} attn_schedule_t;
+
+typedef enum { ATTN_BF16 = 0, ATTN_FP32 = 1 } attn_dtype_t;
+
+typedef enum {
+    ATTN_OK = 0,
+    ATTN_ERR_INVALID_ARG = -1,  /* null pointer, negative size, bad enum    */
+    ATTN_ERR_UNSUPPORTED = -2,  /* d not 64/128, odd tile count for the fold */
+    ATTN_ERR_COSCHEDULE = -3,   /* the schedule needs more resident work
+                                   groups than the device can hold at once */
+    ATTN_ERR_HIP = -4,          /* a HIP runtime call failed                */
+    ATTN_ERR_TIMEOUT = -5,      /* a device-side flag wait expired          */
+    ATTN_ERR_WORKSPACE = -6,    /* caller workspace too small               */
+    ATTN_ERR_DEADLOCK = -7      /* simulator: the schedule cannot finish    */
+} attn_status_t;
+
+/* ------------------------------------------------------------------------
+ * Backward pass.
+ * ------------------------------------------------------------------------ */
+
+/* attn_bwd_deterministic - bf16 backward with scale = 1/sqrt(d), on the null
+ * stream, with a library-owned workspace (allocated on first use and grown
+ * as needed; one per device; calls must not overlap on one device).
+ *   q, k, v, o, dO : const bf16 [b][h][s][d]
+ *   lse            : const float [b][h][s]
+ *   dq, dk, dv     : bf16 [b][h][s][d], written
+ *   b, h, s >= 0 (any zero: nothing to do, returns ATTN_OK); d in {64, 128}
+ *   causal         : 0 full mask, 1 causal mask
+ *   schedule       : attn_schedule_t */
+int attn_bwd_deterministic(const void* q, const void* k, const void* v, const void* o,
+                           const void* dO, const float* lse, void* dq, void* dk, void* dv,
+                           int b, int h, int s, int d, int causal, int schedule);
+
+/* attn_bwd_deterministic_ex - as above with explicit element type (tensors
+ * q..dv are bf16 or fp32 per `dtype`; lse is always fp32), softmax scale,
+ * stream (a hipStream_t, NULL for the null stream) and an optional caller
+ * workspace.  workspace == NULL uses the library-owned one; otherwise it
+ * must be device memory of at least attn_bwd_workspace_bytes(...) bytes
+ * (ATTN_ERR_WORKSPACE if smaller), 256-byte aligned, owned by the caller
+ * and not used concurrently by another call. */
+int attn_bwd_deterministic_ex(const void* q, const void* k, const void* v, const void* o,
+                              const void* dO, const float* lse, void* dq, void* dk, void* dv,
+                              int b, int h, int s, int d, int causal, int schedule,
+                              int dtype, float scale, void* workspace, size_t workspace_bytes,
+                              void* stream);
+
+/* Bytes of workspace a call with these sizes needs: fp32 dQ accumulator
+ * (b*h*s_pad*d*4), per-(head, Q tile) flags, D = rowsum(dO*O), counters.
+ * s_pad is s rounded up to 128.  Returns 0 for invalid sizes. */
+size_t attn_bwd_workspace_bytes(int b, int h, int s, int d, int causal, int schedule);
+
+/* Synchronises `stream` (hipStream_t or NULL), then reports and clears the
+ * device status word: ATTN_OK, or ATTN_ERR_TIMEOUT if a bounded flag wait
+ * expired in any call since the last query (results of that call are
+ * invalid), or ATTN_ERR_HIP if the synchronisation failed. */
+int attn_bwd_query_status(void* stream);
+
+/* Message describing the last failure on the calling thread ("" if none).
+ * The string is owned by the library and valid until the next call. */
+const char* attn_bwd_last_error(void);
+
+/* Tile edge T the backward uses for `dtype` (128 for bf16, 64 for fp32). */
+int attn_bwd_tile_size(int dtype);
+
+/* Kernel timing.  attn_bwd_set_timing(1) starts a recording: every later
+ * backward call (up to 4096) records HIP events on its own stream around
+ * each kernel it launches; attn_bwd_set_timing(0) stops recording.
+ * attn_bwd_get_kernel_times waits for the recorded events and writes the
+ * mean milliseconds per call of the preprocess, main and finalize kernels
+ * (finalize: mean over the calls that launched it; 0 if none).  Returns
+ * ATTN_OK, ATTN_ERR_INVALID_ARG (nothing recorded) or ATTN_ERR_HIP. */
+int attn_bwd_set_timing(int on);
+int attn_bwd_get_kernel_times(float* ms_preprocess, float* ms_main, float* ms_finalize);
+
+/* Flag-wait instrumentation.  When enabled, the main kernel of later calls
+ * accumulates, per launch, the clock cycles its work groups spent inside
+ * dQ flag waits, the cycles spent in whole work items, and the number of
+ * wait polls.  attn_bwd_get_wait_stats synchronises the device and returns
+ * the totals of the last call. */
+int attn_bwd_set_wait_stats(int on);
+int attn_bwd_get_wait_stats(unsigned long long* wait_cycles, unsigned long long* item_cycles,
+                            unsigned long long* polls);
+
+/* ------------------------------------------------------------------------
+ * Schedule generator (host, no GPU needed).
+ * Within one head with n = ceil(s/T) tiles, a schedule is a list of work
+ * items; each item is an ordered list of (KV tile, Q tile) tasks and runs on
+ * one work group; all tasks of one KV tile are contiguous in one item
+ * (Axiom ledger: operations of a KV tile run contiguously on one SM).
+ * rank[kv*n + q] is the position of KV tile kv in Q tile q's dQ
+ * accumulation order (-1 for a task the causal mask removes), count[q] the
+ * number of contributors of Q tile q.  Every head uses the same pattern.
+ * ------------------------------------------------------------------------ */
+
+/* Sizes of the schedule: number of work items per head and total tasks per
+ * head.  Returns ATTN_OK, ATTN_ERR_INVALID_ARG or ATTN_ERR_UNSUPPORTED. */
+int attn_sched_size(int n, int causal, int schedule, int* num_items, int* num_tasks);
+
+/* Fills the schedule.  item_begin: num_items+1 ints (task range of each
+ * item); task_kv, task_q: num_tasks ints each; rank: n*n ints; count: n ints.
+ * Any output pointer may be NULL to skip it.  ATTN_SCHED_ATOMIC describes
+ * the NAIVE visiting order with rank = -1 for every task (no order). */
+int attn_sched_get(int n, int causal, int schedule, int* item_begin, int* task_kv, int* task_q,
+                   int* rank, int* count);
+
+/* Smallest number of simultaneously resident work groups with which the
+ * schedule always makes progress when items are handed out in increasing
+ * order: 1 for NAIVE, DESCENDING and ATOMIC (every wait points to an
+ * earlier item), the items per head for SHIFT and SYMMETRIC_SHIFT (cyclic
+ * waits inside a head).  Returns a negative status on bad arguments. */
+int attn_sched_min_workers(int n, int causal, int schedule);
+
+/* ------------------------------------------------------------------------
+ * DAG critical-path simulator (host).  Models the pages' DAG: every task is
+ * a compute phase of cost c followed by a reduction phase of cost r; the
+ * reduction of a task waits for the previous contributor to the same dQ
+ * tile; a worker runs one phase at a time and blocks while waiting (review
+ * page, "What carries the argument" and Axiom ledger).  `heads` copies of
+ * the schedule run on `workers` workers; placement 0 deals items
+ * round-robin in head-major order, placement 1 hands the next item to the
+ * first worker that becomes free (the kernel's ticket queue).
+ * Outputs (any may be NULL): makespan, the summed time workers spent
+ * blocked on waits, and the summed busy time (compute + reduction).
+ * Returns ATTN_OK, ATTN_ERR_DEADLOCK or an argument error.
+ * ------------------------------------------------------------------------ */
+int attn_dagsim(int n, int causal, int schedule, int heads, int workers, int placement,
+                double c, double r, double* makespan, double* wait_time, double* busy_time);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* ATTN_BWD_H */

@@ -1,0 +1,229 @@
+"""GPU parity of the HIP backward with the fp64 oracle, bitwise determinism,
+and schedule invariance, through the C ABI.
+
+Tolerance: per tensor, max|g_gpu - g_oracle| / max|g_oracle| <= 2e-2 for
+bf16 inputs and 1e-4 for fp32 inputs.  The deterministic schedules must give
+bitwise identical dQ, dK, dV over repeated runs (the pages report a maximum
+run-to-run deviation of exactly 0 for deterministic kernels)."""
+import sys
+
+import numpy as np
+import pytest
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+if not torch.cuda.is_available():  # pragma: no cover
+    pytest.skip("no GPU", allow_module_level=True)
+
+import tile_scheduling_attn_amd as tsa  # noqa: E402
+import workloads  # noqa: E402
+from support import Problem, TOL, rel_err, to_np_heads  # noqa: E402
+
+DET = ("naive", "descending", "shift", "symmetric_shift")
+
+
+def _say(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+def _check_parity(pb, grads, heads, tag):
+    ref = pb.oracle(heads)
+    tol = TOL[pb.dtype]
+    errs = {}
+    for name, g in zip(("dq", "dk", "dv"), grads):
+        errs[name] = rel_err(to_np_heads(g, heads), ref[name])
+    _say(f"{tag}: rel errs {errs}")
+    for name, e in errs.items():
+        assert e <= tol, f"{tag} {name}: {e} > {tol}"
+    assert tsa.attn_bwd_query_status() == 0, tsa.last_error()
+
+
+def _schedules_for(pb, names):
+    out = []
+    n = -(-pb.s // tsa.attn_bwd_tile_size(pb.dtype))
+    for name in names:
+        if name == "symmetric_shift" and pb.causal and n % 2:
+            continue
+        out.append(name)
+    return out
+
+
+# ---------------------------------------------------------------- small shapes
+@pytest.mark.parametrize("causal", [False, True])
+def test_tiny_fp32_all_schedules(causal):
+    """b1 h1 s128 d64 fp32, 64x64 tiles (two tiles per side)."""
+    wl = workloads.WORKLOADS["tiny"]
+    pb = Problem(wl.b, wl.h, wl.s, wl.d, "fp32", wl.seed, causal)
+    for sched in DET + ("atomic",):
+        _say(f"tiny fp32 causal={causal} schedule={sched}")
+        torch.cuda.synchronize()
+        g = pb.run(sched)
+        torch.cuda.synchronize()
+        _check_parity(pb, g, range(pb.b * pb.h), f"tiny causal={causal} {sched}")
+
+
+SMALL = [
+    # b, h, s, d, dtype   (several tiles, ragged tails, both head dims)
+    (1, 2, 512, 64, "bf16"),
+    (2, 1, 384, 128, "bf16"),
+    (1, 3, 200, 64, "bf16"),      # ragged: 200 = 128 + 72
+    (1, 2, 300, 128, "bf16"),     # ragged: 3 tiles, last one 44 rows
+    (1, 2, 130, 64, "fp32"),      # ragged fp32: 64 + 64 + 2
+    (2, 2, 256, 128, "fp32"),
+    (1, 1, 1, 64, "bf16"),        # a single row
+    (1, 1, 64, 128, "bf16"),      # one partial tile
+]
+
+
+@pytest.mark.parametrize("shape", SMALL, ids=lambda x: "-".join(map(str, x)))
+@pytest.mark.parametrize("causal", [False, True])
+def test_small_shapes_all_schedules(shape, causal):
+    b, h, s, d, dt = shape
+    pb = Problem(b, h, s, d, dt, 1000 + s + d + b * 7 + h, causal)
+    for sched in _schedules_for(pb, DET + ("atomic",)):
+        _say(f"small {shape} causal={causal} schedule={sched}")
+        g = pb.run(sched)
+        torch.cuda.synchronize()
+        _check_parity(pb, g, range(b * h), f"{shape} causal={causal} {sched}")
+
+
+def test_symmetric_shift_odd_tile_count_is_rejected():
+    pb = Problem(1, 1, 384, 64, "bf16", 5, True)  # 3 tiles
+    with pytest.raises(tsa.AttnError) as e:
+        pb.run("symmetric_shift")
+    assert e.value.code == -2
+
+
+# ---------------------------------------------------------------- configs
+def _run_config(name, causal, schedules, heads=None, tag=""):
+    wl = workloads.WORKLOADS[name]
+    _say(f"config {name} causal={causal}: generating inputs")
+    pb = Problem(wl.b, wl.h, wl.s, wl.d, wl.dtype, wl.seed, causal)
+    H = wl.b * wl.h
+    heads = sorted({0, H // 2, H - 1}) if heads == "sample" else (heads or range(H))
+    results = {}
+    for sched in _schedules_for(pb, schedules):
+        _say(f"config {name} causal={causal} schedule={sched}")
+        g = pb.run(sched)
+        torch.cuda.synchronize()
+        _check_parity(pb, g, heads, f"{name} causal={causal} {sched}")
+        results[sched] = [t.clone() for t in g]
+    return pb, results
+
+
+def test_config_s2k_d64_causal():
+    pb, res = _run_config("s2k_d64_causal", True, ("descending", "symmetric_shift", "naive", "atomic"))
+    # NAIVE and DESCENDING share the dQ order: dQ is bitwise equal
+    assert torch.equal(res["naive"][0].view(torch.int16), res["descending"][0].view(torch.int16))
+
+
+def test_config_s8k_d128_full():
+    pb, res = _run_config("s8k_d128_full", False, ("shift", "naive", "atomic"), heads="sample")
+
+
+def test_config_s8k_d128_causal():
+    _run_config("s8k_d128_causal", True, ("descending", "symmetric_shift", "atomic"), heads="sample")
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_config_s16k_d128(causal):
+    scheds = ("shift", "naive", "atomic") if not causal else ("descending", "symmetric_shift", "shift")
+    _run_config("s16k_d128", causal, scheds, heads=[0, 31])
+
+
+# ---------------------------------------------------------------- determinism
+@pytest.mark.parametrize("name,causal,scheds", [
+    ("s2k_d64_causal", True, ("descending", "symmetric_shift", "naive", "shift")),
+    ("s8k_d128_full", False, ("shift", "naive")),
+])
+def test_bitwise_determinism_20_runs(name, causal, scheds):
+    wl = workloads.WORKLOADS[name]
+    pb = Problem(wl.b, wl.h, wl.s, wl.d, wl.dtype, wl.seed, causal)
+    for sched in scheds:
+        _say(f"determinism {name} {sched}")
+        ref = [t.clone() for t in pb.run(sched)]
+        out = [torch.empty_like(t) for t in ref]
+        for it in range(19):
+            for t in out:
+                t.fill_(float("nan"))
+            pb.run(sched, out=out)
+            torch.cuda.synchronize()
+            for a, b_ in zip(ref, out):
+                assert torch.equal(a.view(torch.int16), b_.view(torch.int16)), f"{sched} run {it + 1}"
+        assert tsa.attn_bwd_query_status() == 0
+
+
+def test_atomic_run_to_run_deviation_is_reported():
+    """The non-deterministic variant may differ between runs (the pages
+    report ~2.4e-4 full / 4.9e-4 causal on their shapes); it must still meet
+    the parity bar, which the config tests check.  Here the deviation is only
+    printed."""
+    wl = workloads.WORKLOADS["s8k_d128_full"]
+    pb = Problem(wl.b, wl.h, wl.s, wl.d, wl.dtype, wl.seed, False)
+    a = pb.run("atomic")[0].float()
+    dev = 0.0
+    for _ in range(5):
+        b_ = pb.run("atomic")[0].float()
+        dev = max(dev, float((a - b_).abs().max()))
+    _say(f"atomic dQ run-to-run max deviation: {dev:.3e} (relative {dev / float(a.abs().max()):.3e})")
+
+
+# ---------------------------------------------------------------- misc
+def test_caller_workspace_and_stream_match_library_workspace():
+    pb = Problem(1, 4, 640, 128, "bf16", 77, True)
+    ref = [t.clone() for t in pb.run("descending")]
+    nbytes = tsa.attn_bwd_workspace_bytes(1, 4, 640, 128, 1, "descending")
+    ws = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    st = torch.cuda.Stream()
+    with torch.cuda.stream(st):
+        out = tsa.backward(pb.q, pb.k, pb.v, pb.o, pb.do, pb.lse, True, "descending", workspace=ws)
+    st.synchronize()
+    for a, b_ in zip(ref, out):
+        assert torch.equal(a.view(torch.int16), b_.view(torch.int16))
+    small = torch.empty(nbytes - 256, dtype=torch.uint8, device="cuda")
+    with pytest.raises(tsa.AttnError) as e:
+        tsa.backward(pb.q, pb.k, pb.v, pb.o, pb.do, pb.lse, True, "descending", workspace=small)
+    assert e.value.code == -6
+
+
+def test_default_entry_point_bf16():
+    pb = Problem(1, 2, 256, 64, "bf16", 91, False)
+    dq, dk, dv = (torch.empty_like(pb.q) for _ in range(3))
+    rc = tsa.attn_bwd_deterministic(pb.q, pb.k, pb.v, pb.o, pb.do, pb.lse, dq, dk, dv,
+                                    1, 2, 256, 64, 0, "shift")
+    assert rc == 0, tsa.last_error()
+    torch.cuda.synchronize()
+    _check_parity(pb, (dq, dk, dv), range(2), "default entry")
+
+
+def test_kernel_timing_and_wait_stats():
+    pb = Problem(1, 8, 2048, 128, "bf16", 3, False)
+    tsa.attn_bwd_set_timing(True)
+    tsa.attn_bwd_set_wait_stats(True)
+    try:
+        pb.run("naive")
+        pre, main, fin = tsa.attn_bwd_get_kernel_times()
+        wait, item, polls = tsa.attn_bwd_get_wait_stats()
+    finally:
+        tsa.attn_bwd_set_timing(False)
+        tsa.attn_bwd_set_wait_stats(False)
+    _say(f"timing pre={pre:.4f} main={main:.4f} fin={fin:.4f} ms; wait={wait} item={item} polls={polls}")
+    assert main > 0 and pre > 0 and fin == 0
+    assert item > 0 and polls > 0 and wait <= item
+
+
+def test_gradient_identities_full_size():
+    """sum_j dK_j = 0 and sum_j dV_j = sum_i dO_i hold for the exact gradient
+    (rows of P sum to one); on the bf16 outputs they hold to rounding."""
+    wl = workloads.WORKLOADS["s8k_d128_full"]
+    pb = Problem(1, 4, wl.s, wl.d, "bf16", 55, False)
+    dq, dk, dv = pb.run("shift")
+    torch.cuda.synchronize()
+    sdk = dk.float().sum(dim=2)
+    sdv = dv.float().sum(dim=2)
+    sdo = pb.do.float().sum(dim=2)
+    scale_dk = dk.float().abs().sum(dim=2).max()
+    assert float(sdk.abs().max()) <= 2e-2 * float(scale_dk)
+    assert float((sdv - sdo).abs().max()) <= 2e-2 * float(dv.float().abs().sum(dim=2).max())

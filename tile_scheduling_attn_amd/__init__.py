@@ -1,0 +1,228 @@
+"""Deterministic attention backward for MI355X (gfx950), scheduled with DASH.
+
+Thin ctypes binding over libattn_bwd.so (C ABI in include/attn_bwd.h).  The
+binding only marshals arguments: every step of the backward runs in the HIP
+kernels of the library, and importing this package fails loudly if the
+library is missing.  PyTorch is used only for device memory and streams.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libattn_bwd.so")
+
+SCHEDULES = {"naive": 0, "descending": 1, "shift": 2, "symmetric_shift": 3, "atomic": 4}
+DTYPES = {"bf16": 0, "fp32": 1}
+STATUS = {0: "ATTN_OK", -1: "ATTN_ERR_INVALID_ARG", -2: "ATTN_ERR_UNSUPPORTED",
+          -3: "ATTN_ERR_COSCHEDULE", -4: "ATTN_ERR_HIP", -5: "ATTN_ERR_TIMEOUT",
+          -6: "ATTN_ERR_WORKSPACE", -7: "ATTN_ERR_DEADLOCK"}
+
+# every function declared in include/attn_bwd.h
+EXPORTS = ("attn_bwd_deterministic", "attn_bwd_deterministic_ex", "attn_bwd_workspace_bytes",
+           "attn_bwd_query_status", "attn_bwd_last_error", "attn_bwd_tile_size",
+           "attn_bwd_set_timing", "attn_bwd_get_kernel_times", "attn_bwd_set_wait_stats",
+           "attn_bwd_get_wait_stats", "attn_sched_size", "attn_sched_get",
+           "attn_sched_min_workers", "attn_dagsim")
+
+
+class AttnError(RuntimeError):
+    def __init__(self, code: int, where: str, msg: str):
+        self.code = code
+        super().__init__(f"{where}: {STATUS.get(code, code)}: {msg}")
+
+
+def _load():
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"{LIB_PATH} is missing: build it with "
+                          "`python -m tile_scheduling_attn_amd.build`")
+    lib = ctypes.CDLL(LIB_PATH)
+    vp, i, f, d, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_double, ctypes.c_size_t
+    ip, dp = ctypes.POINTER(ctypes.c_int), ctypes.POINTER(ctypes.c_double)
+    ull = ctypes.POINTER(ctypes.c_ulonglong)
+    fp = ctypes.POINTER(ctypes.c_float)
+    lib.attn_bwd_deterministic.argtypes = [vp] * 9 + [i] * 6
+    lib.attn_bwd_deterministic.restype = i
+    lib.attn_bwd_deterministic_ex.argtypes = [vp] * 9 + [i] * 7 + [f, vp, sz, vp]
+    lib.attn_bwd_deterministic_ex.restype = i
+    lib.attn_bwd_workspace_bytes.argtypes = [i] * 6
+    lib.attn_bwd_workspace_bytes.restype = sz
+    lib.attn_bwd_query_status.argtypes = [vp]
+    lib.attn_bwd_query_status.restype = i
+    lib.attn_bwd_last_error.argtypes = []
+    lib.attn_bwd_last_error.restype = ctypes.c_char_p
+    lib.attn_bwd_tile_size.argtypes = [i]
+    lib.attn_bwd_tile_size.restype = i
+    lib.attn_bwd_set_timing.argtypes = [i]
+    lib.attn_bwd_set_timing.restype = i
+    lib.attn_bwd_get_kernel_times.argtypes = [fp, fp, fp]
+    lib.attn_bwd_get_kernel_times.restype = i
+    lib.attn_bwd_set_wait_stats.argtypes = [i]
+    lib.attn_bwd_set_wait_stats.restype = i
+    lib.attn_bwd_get_wait_stats.argtypes = [ull, ull, ull]
+    lib.attn_bwd_get_wait_stats.restype = i
+    lib.attn_sched_size.argtypes = [i, i, i, ip, ip]
+    lib.attn_sched_size.restype = i
+    lib.attn_sched_get.argtypes = [i, i, i, ip, ip, ip, ip, ip]
+    lib.attn_sched_get.restype = i
+    lib.attn_sched_min_workers.argtypes = [i, i, i]
+    lib.attn_sched_min_workers.restype = i
+    lib.attn_dagsim.argtypes = [i, i, i, i, i, i, d, d, dp, dp, dp]
+    lib.attn_dagsim.restype = i
+    return lib
+
+
+lib = _load()
+
+
+def last_error() -> str:
+    return lib.attn_bwd_last_error().decode()
+
+
+def _check(rc: int, where: str) -> int:
+    if rc < 0:
+        raise AttnError(rc, where, last_error())
+    return rc
+
+
+def _sched_id(schedule) -> int:
+    if isinstance(schedule, str):
+        return SCHEDULES[schedule]
+    return int(schedule)
+
+
+def _ptr(x) -> int:
+    if x is None:
+        return 0
+    if isinstance(x, int):
+        return x
+    return int(x.data_ptr())
+
+
+# ---------------------------------------------------------------------------
+# C ABI, same names and arguments (pointers may be ints or tensors)
+# ---------------------------------------------------------------------------
+def attn_bwd_deterministic(q, k, v, o, dO, lse, dq, dk, dv, b, h, s, d, causal, schedule) -> int:
+    return lib.attn_bwd_deterministic(*(_ptr(t) for t in (q, k, v, o, dO, lse, dq, dk, dv)),
+                                      b, h, s, d, int(causal), _sched_id(schedule))
+
+
+def attn_bwd_deterministic_ex(q, k, v, o, dO, lse, dq, dk, dv, b, h, s, d, causal, schedule,
+                              dtype, scale, workspace, workspace_bytes, stream) -> int:
+    dt = DTYPES[dtype] if isinstance(dtype, str) else int(dtype)
+    return lib.attn_bwd_deterministic_ex(*(_ptr(t) for t in (q, k, v, o, dO, lse, dq, dk, dv)),
+                                         b, h, s, d, int(causal), _sched_id(schedule), dt,
+                                         float(scale), _ptr(workspace), int(workspace_bytes),
+                                         int(stream or 0))
+
+
+def attn_bwd_workspace_bytes(b, h, s, d, causal, schedule) -> int:
+    return lib.attn_bwd_workspace_bytes(b, h, s, d, int(causal), _sched_id(schedule))
+
+
+def attn_bwd_query_status(stream=None) -> int:
+    return lib.attn_bwd_query_status(int(stream or 0))
+
+
+def attn_bwd_last_error() -> str:
+    return last_error()
+
+
+def attn_bwd_tile_size(dtype) -> int:
+    return lib.attn_bwd_tile_size(DTYPES[dtype] if isinstance(dtype, str) else int(dtype))
+
+
+def attn_bwd_set_timing(on: bool) -> int:
+    return lib.attn_bwd_set_timing(int(bool(on)))
+
+
+def attn_bwd_get_kernel_times():
+    a, b_, c = ctypes.c_float(), ctypes.c_float(), ctypes.c_float()
+    _check(lib.attn_bwd_get_kernel_times(ctypes.byref(a), ctypes.byref(b_), ctypes.byref(c)),
+           "attn_bwd_get_kernel_times")
+    return a.value, b_.value, c.value
+
+
+def attn_bwd_set_wait_stats(on: bool) -> int:
+    return lib.attn_bwd_set_wait_stats(int(bool(on)))
+
+
+def attn_bwd_get_wait_stats():
+    a, b_, c = ctypes.c_ulonglong(), ctypes.c_ulonglong(), ctypes.c_ulonglong()
+    _check(lib.attn_bwd_get_wait_stats(ctypes.byref(a), ctypes.byref(b_), ctypes.byref(c)),
+           "attn_bwd_get_wait_stats")
+    return a.value, b_.value, c.value
+
+
+def attn_sched_size(n, causal, schedule):
+    ni, nt = ctypes.c_int(), ctypes.c_int()
+    _check(lib.attn_sched_size(n, int(causal), _sched_id(schedule), ctypes.byref(ni),
+                               ctypes.byref(nt)), "attn_sched_size")
+    return ni.value, nt.value
+
+
+def attn_sched_get(n, causal, schedule):
+    """Returns dict of NumPy int32 arrays: item_begin, task_kv, task_q, rank (n x n), count."""
+    ni, nt = attn_sched_size(n, causal, schedule)
+    out = {"item_begin": np.zeros(ni + 1, np.int32), "task_kv": np.zeros(nt, np.int32),
+           "task_q": np.zeros(nt, np.int32), "rank": np.zeros((n, n), np.int32),
+           "count": np.zeros(n, np.int32)}
+    P = lambda a: a.ctypes.data_as(ctypes.POINTER(ctypes.c_int))
+    _check(lib.attn_sched_get(n, int(causal), _sched_id(schedule), P(out["item_begin"]),
+                              P(out["task_kv"]), P(out["task_q"]), P(out["rank"]),
+                              P(out["count"])), "attn_sched_get")
+    return out
+
+
+def attn_sched_min_workers(n, causal, schedule) -> int:
+    return _check(lib.attn_sched_min_workers(n, int(causal), _sched_id(schedule)),
+                  "attn_sched_min_workers")
+
+
+def attn_dagsim(n, causal, schedule, heads, workers, placement, c, r):
+    """Returns (makespan, wait_time, busy_time); raises AttnError on deadlock."""
+    m, w, b_ = ctypes.c_double(), ctypes.c_double(), ctypes.c_double()
+    _check(lib.attn_dagsim(n, int(causal), _sched_id(schedule), heads, workers, placement,
+                           float(c), float(r), ctypes.byref(m), ctypes.byref(w), ctypes.byref(b_)),
+           "attn_dagsim")
+    return m.value, w.value, b_.value
+
+
+# ---------------------------------------------------------------------------
+# Torch convenience wrapper (allocation and stream only)
+# ---------------------------------------------------------------------------
+def backward(q, k, v, o, do, lse, causal: bool, schedule="shift", scale=None, out=None,
+             workspace=None, stream=None):
+    """Run the backward on torch tensors [b, h, s, d] (bf16 or fp32, contiguous,
+    on the current HIP device) with lse [b, h, s] fp32.  Returns (dq, dk, dv),
+    allocated unless `out` gives them.  The call is asynchronous on `stream`
+    (default: torch's current stream)."""
+    import torch
+    b, h, s, d = q.shape
+    for name, t in (("q", q), ("k", k), ("v", v), ("o", o), ("do", do)):
+        if tuple(t.shape) != (b, h, s, d) or t.dtype != q.dtype or not t.is_contiguous() \
+                or not t.is_cuda:
+            raise ValueError(f"{name} must be a contiguous device tensor of shape {(b, h, s, d)} "
+                             f"and dtype {q.dtype}")
+    if tuple(lse.shape) != (b, h, s) or lse.dtype != torch.float32 or not lse.is_contiguous():
+        raise ValueError("lse must be a contiguous float32 tensor [b, h, s]")
+    dtype = {torch.bfloat16: "bf16", torch.float32: "fp32"}.get(q.dtype)
+    if dtype is None:
+        raise ValueError("q must be bfloat16 or float32")
+    if out is None:
+        out = (torch.empty_like(q), torch.empty_like(q), torch.empty_like(q))
+    dq, dk, dv = out
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    if stream is None:
+        stream = torch.cuda.current_stream().cuda_stream
+    ws_ptr, ws_bytes = (0, 0) if workspace is None else (workspace.data_ptr(), workspace.numel() *
+                                                         workspace.element_size())
+    rc = attn_bwd_deterministic_ex(q, k, v, o, do, lse, dq, dk, dv, b, h, s, d, causal, schedule,
+                                   dtype, scale, ws_ptr, ws_bytes, stream)
+    _check(rc, "attn_bwd_deterministic_ex")
+    return dq, dk, dv

@@ -1,0 +1,50 @@
+"""Build libattn_bwd.so (HIP kernels for gfx950 + host schedule/simulator +
+C ABI) in-tree with hipcc.  `python -m tile_scheduling_attn_amd.build`."""
+from __future__ import annotations
+
+import os
+import subprocess
+import sys
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(HERE)
+CSRC = os.path.join(HERE, "csrc")
+INCLUDE = os.path.join(ROOT, "include")
+LIB = os.path.join(HERE, "libattn_bwd.so")
+
+SOURCES = ["api.cpp", "schedule.cpp", "bwd_kernels.hip"]
+# Packed fp32 VALU forms are switched off for every HIP source.
+HIP_FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",
+             "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+             "-munsafe-fp-atomics", "-Wall", "-Wno-unused-function"]
+
+
+def build(verbose: bool = False, extra_flags=None) -> str:
+    """Compile every source and link the shared library; always rebuilds."""
+    objdir = os.path.join(HERE, "_build")
+    os.makedirs(objdir, exist_ok=True)
+    objs = []
+    for src in SOURCES:
+        obj = os.path.join(objdir, src + ".o")
+        cmd = ["hipcc", *HIP_FLAGS, *(extra_flags or []), "-I", INCLUDE, "-I", CSRC,
+               "-c", os.path.join(CSRC, src), "-o", obj]
+        if verbose:
+            print(" ".join(cmd), flush=True)
+        r = subprocess.run(cmd, capture_output=True, text=True)
+        err = "\n".join(l for l in r.stderr.splitlines() if "packed-fp32-ops" not in l)
+        if r.returncode != 0:
+            raise RuntimeError(f"hipcc failed on {src}:\n{err}")
+        if verbose and err.strip():
+            print(err, file=sys.stderr)
+        objs.append(obj)
+    tmp = LIB + f".tmp{os.getpid()}"
+    cmd = ["hipcc", "--offload-arch=gfx950", "-shared", "-fPIC", "-o", tmp, *objs]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError("link failed:\n" + r.stderr)
+    os.replace(tmp, LIB)
+    return LIB
+
+
+if __name__ == "__main__":
+    print(build(verbose="-v" in sys.argv))

@@ -1,0 +1,364 @@
+// C ABI of libattn_bwd.so: argument checks, workspace, cached device
+// schedule tables and the launch of the backward kernels.  The functions
+// are declared, with their contracts, in include/attn_bwd.h.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdint>
+#include <cstring>
+#include <map>
+#include <mutex>
+#include <string>
+#include <tuple>
+#include <vector>
+
+#include "attn_bwd.h"
+#include "internal.h"
+
+namespace attn {
+
+static thread_local std::string g_last_error;
+
+int fail(int code, const char* msg) {
+    g_last_error = msg ? msg : "";
+    return code;
+}
+
+static int fail_hip(hipError_t e, const char* what) {
+    g_last_error = std::string(what) + ": " + hipGetErrorString(e);
+    return ATTN_ERR_HIP;
+}
+
+constexpr size_t kAlign = 256;
+constexpr int kPadRows = 128;     // s is padded to a multiple of this
+constexpr int kMinTile = 64;      // smallest tile: bounds the flag count
+constexpr int kCounterWords = 64; // ticket + wait statistics
+
+static size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+struct WsLayout {
+    size_t s_pad, acc, delta, flags, counters, total;
+    int nflags;
+};
+
+static bool ws_layout(long long H, long long s, int d, WsLayout& w) {
+    if (H < 0 || s < 0 || (d != 64 && d != 128)) return false;
+    w.s_pad = (size_t)((s + kPadRows - 1) / kPadRows) * kPadRows;
+    const size_t nmax = w.s_pad / kMinTile;
+    w.nflags = (int)(H * nmax);
+    w.acc = 0;
+    w.delta = align_up(w.acc + (size_t)H * w.s_pad * d * sizeof(float));
+    w.flags = align_up(w.delta + (size_t)H * w.s_pad * sizeof(float));
+    w.counters = align_up(w.flags + (size_t)w.nflags * sizeof(unsigned));
+    w.total = align_up(w.counters + kCounterWords * sizeof(unsigned));
+    return true;
+}
+
+struct DevSchedule {
+    int* buf = nullptr;  // item_begin | task_kv | task_q | rank | count
+    int items = 0, tasks = 0, n = 0, min_workers = 1;
+};
+
+struct DevState {
+    bool init = false;
+    int num_cus = 0;
+    void* ws = nullptr;
+    size_t ws_bytes = 0;
+    unsigned* status = nullptr;
+    std::map<std::tuple<int, int, int>, DevSchedule> schedules;
+    // kernel timing: 4 events per recorded call (before preprocess, before
+    // main, after main, after finalize)
+    std::vector<hipEvent_t> ev_pool;
+    std::vector<char> ev_finalize;   // per recorded call: finalize launched
+    size_t ev_used = 0;
+    void* last_counters = nullptr;
+    bool stats_valid = false;
+};
+
+constexpr size_t kMaxTimedCalls = 4096;
+
+static std::mutex g_mutex;
+static std::map<int, DevState> g_dev;
+static bool g_timing = false;
+static bool g_wait_stats = false;
+static int g_last_dev = -1;
+
+static int dev_init(int dev, DevState& ds) {
+    if (ds.init) return ATTN_OK;
+    hipDeviceProp_t prop;
+    hipError_t e = hipGetDeviceProperties(&prop, dev);
+    if (e != hipSuccess) return fail_hip(e, "hipGetDeviceProperties");
+    ds.num_cus = prop.multiProcessorCount;
+    e = hipMalloc(&ds.status, sizeof(unsigned));
+    if (e != hipSuccess) return fail_hip(e, "hipMalloc(status)");
+    e = hipMemset(ds.status, 0, sizeof(unsigned));
+    if (e != hipSuccess) return fail_hip(e, "hipMemset(status)");
+    ds.init = true;
+    return ATTN_OK;
+}
+
+static int get_schedule(DevState& ds, int n, bool causal, int schedule, DevSchedule** out) {
+    auto key = std::make_tuple(n, (int)causal, schedule);
+    auto it = ds.schedules.find(key);
+    if (it != ds.schedules.end()) {
+        *out = &it->second;
+        return ATTN_OK;
+    }
+    Schedule sc;
+    int rc = build_schedule(n, causal, schedule, sc);
+    if (rc == ATTN_ERR_UNSUPPORTED)
+        return fail(rc, "symmetric shift under the causal mask needs an even number of tiles");
+    if (rc != ATTN_OK) return fail(rc, "invalid schedule");
+    std::vector<int> host;
+    host.insert(host.end(), sc.item_begin.begin(), sc.item_begin.end());
+    host.insert(host.end(), sc.task_kv.begin(), sc.task_kv.end());
+    host.insert(host.end(), sc.task_q.begin(), sc.task_q.end());
+    host.insert(host.end(), sc.rank.begin(), sc.rank.end());
+    host.insert(host.end(), sc.count.begin(), sc.count.end());
+    DevSchedule d;
+    hipError_t e = hipMalloc(&d.buf, host.size() * sizeof(int));
+    if (e != hipSuccess) return fail_hip(e, "hipMalloc(schedule)");
+    e = hipMemcpy(d.buf, host.data(), host.size() * sizeof(int), hipMemcpyHostToDevice);
+    if (e != hipSuccess) {
+        hipFree(d.buf);
+        return fail_hip(e, "hipMemcpy(schedule)");
+    }
+    d.items = sc.num_items();
+    d.tasks = (int)sc.task_kv.size();
+    d.n = n;
+    d.min_workers = min_workers(sc);
+    auto res = ds.schedules.emplace(key, d);
+    *out = &res.first->second;
+    return ATTN_OK;
+}
+
+static int tile_for(int dtype) { return dtype == ATTN_FP32 ? 64 : 128; }
+
+static int backward(const void* q, const void* k, const void* v, const void* o, const void* dO,
+                    const float* lse, void* dq, void* dk, void* dv, int b, int h, int s, int d,
+                    int causal, int schedule, int dtype, float scale, void* workspace,
+                    size_t workspace_bytes, void* stream) {
+    g_last_error.clear();
+    if (b < 0 || h < 0 || s < 0) return fail(ATTN_ERR_INVALID_ARG, "b, h and s must be >= 0");
+    if (causal != 0 && causal != 1) return fail(ATTN_ERR_INVALID_ARG, "causal must be 0 or 1");
+    if (schedule < ATTN_SCHED_NAIVE || schedule > ATTN_SCHED_ATOMIC)
+        return fail(ATTN_ERR_INVALID_ARG, "unknown schedule");
+    if (dtype != ATTN_BF16 && dtype != ATTN_FP32) return fail(ATTN_ERR_INVALID_ARG, "unknown dtype");
+    if (!std::isfinite(scale)) return fail(ATTN_ERR_INVALID_ARG, "scale must be finite");
+    if (d != 64 && d != 128) return fail(ATTN_ERR_UNSUPPORTED, "head dimension must be 64 or 128");
+    const long long H = (long long)b * h;
+    if (H == 0 || s == 0) return ATTN_OK;
+    if (H * (long long)s * d >= (1LL << 40)) return fail(ATTN_ERR_INVALID_ARG, "problem too large");
+    if (!q || !k || !v || !o || !dO || !lse || !dq || !dk || !dv)
+        return fail(ATTN_ERR_INVALID_ARG, "null tensor pointer");
+    const uintptr_t mis = (uintptr_t)q | (uintptr_t)k | (uintptr_t)v | (uintptr_t)o | (uintptr_t)dO |
+                          (uintptr_t)dq | (uintptr_t)dk | (uintptr_t)dv;
+    if (mis & 15) return fail(ATTN_ERR_INVALID_ARG, "tensor pointers must be 16-byte aligned");
+    if (workspace && ((uintptr_t)workspace & (kAlign - 1)))
+        return fail(ATTN_ERR_INVALID_ARG, "workspace must be 256-byte aligned");
+
+    const int tile = tile_for(dtype);
+    const int n = (s + tile - 1) / tile;
+    WsLayout wl;
+    ws_layout(H, s, d, wl);
+
+    std::lock_guard<std::mutex> lock(g_mutex);
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return fail_hip(e, "hipGetDevice");
+    DevState& ds = g_dev[dev];
+    int rc = dev_init(dev, ds);
+    if (rc != ATTN_OK) return rc;
+    DevSchedule* sch = nullptr;
+    rc = get_schedule(ds, n, causal != 0, schedule, &sch);
+    if (rc != ATTN_OK) return rc;
+
+    char* ws = static_cast<char*>(workspace);
+    if (ws) {
+        if (workspace_bytes < wl.total) return fail(ATTN_ERR_WORKSPACE, "workspace smaller than attn_bwd_workspace_bytes()");
+    } else {
+        if (ds.ws_bytes < wl.total) {
+            if (ds.ws) {
+                e = hipDeviceSynchronize();
+                if (e != hipSuccess) return fail_hip(e, "hipDeviceSynchronize");
+                hipFree(ds.ws);
+                ds.ws = nullptr;
+                ds.ws_bytes = 0;
+            }
+            e = hipMalloc(&ds.ws, wl.total);
+            if (e != hipSuccess) return fail_hip(e, "hipMalloc(workspace)");
+            ds.ws_bytes = wl.total;
+        }
+        ws = static_cast<char*>(ds.ws);
+    }
+
+    BwdArgs a{};
+    a.q = q; a.k = k; a.v = v; a.o = o; a.dO = dO; a.lse = lse;
+    a.dq = dq; a.dk = dk; a.dv = dv;
+    a.H = (int)H; a.s = s; a.d = d; a.n = n; a.tile = tile;
+    a.causal = causal != 0;
+    a.schedule = schedule;
+    a.dtype = dtype;
+    a.scale = scale;
+    a.stream = stream;
+    a.s_pad = wl.s_pad;
+    a.dq_acc = reinterpret_cast<float*>(ws + wl.acc);
+    a.delta = reinterpret_cast<float*>(ws + wl.delta);
+    a.flags = reinterpret_cast<unsigned*>(ws + wl.flags);
+    a.counters = reinterpret_cast<unsigned*>(ws + wl.counters);
+
+    void** ev = nullptr;
+    if (g_timing && ds.ev_used < kMaxTimedCalls) {
+        while (ds.ev_pool.size() < 4 * (ds.ev_used + 1)) {
+            hipEvent_t x;
+            e = hipEventCreate(&x);
+            if (e != hipSuccess) return fail_hip(e, "hipEventCreate");
+            ds.ev_pool.push_back(x);
+        }
+        ev = reinterpret_cast<void**>(&ds.ev_pool[4 * ds.ev_used]);
+    }
+
+    BwdLaunch L{};
+    L.stream = stream;
+    L.num_cus = ds.num_cus;
+    L.min_workers = sch->min_workers;
+    L.ev = ev;
+    L.status = ds.status;
+    L.stats = g_wait_stats ? reinterpret_cast<unsigned long long*>(a.counters + 2) : nullptr;
+    L.item_begin = sch->buf;
+    L.task_kv = L.item_begin + sch->items + 1;
+    L.task_q = L.task_kv + sch->tasks;
+    L.rank = L.task_q + sch->tasks;
+    L.count = L.rank + (size_t)n * n;
+    L.items_per_head = sch->items;
+    // flags and counters are contiguous: one clear covers both
+    L.nclear32 = (int)((wl.total - wl.flags) / sizeof(unsigned));
+
+    rc = launch_backward(a, L);
+    if (rc != ATTN_OK) return rc;
+    if (ev) {
+        if (ds.ev_finalize.size() <= ds.ev_used) ds.ev_finalize.resize(ds.ev_used + 1);
+        ds.ev_finalize[ds.ev_used] = schedule == ATTN_SCHED_ATOMIC;
+        ds.ev_used++;
+    }
+    ds.last_counters = a.counters;
+    ds.stats_valid = g_wait_stats;
+    g_last_dev = dev;
+    return ATTN_OK;
+}
+
+}  // namespace attn
+
+using namespace attn;
+
+extern "C" int attn_bwd_deterministic(const void* q, const void* k, const void* v, const void* o,
+                                      const void* dO, const float* lse, void* dq, void* dk, void* dv,
+                                      int b, int h, int s, int d, int causal, int schedule) {
+    const float scale = (d > 0) ? 1.0f / std::sqrt((float)d) : 1.0f;
+    return backward(q, k, v, o, dO, lse, dq, dk, dv, b, h, s, d, causal, schedule, ATTN_BF16, scale,
+                    nullptr, 0, nullptr);
+}
+
+extern "C" int attn_bwd_deterministic_ex(const void* q, const void* k, const void* v, const void* o,
+                                         const void* dO, const float* lse, void* dq, void* dk, void* dv,
+                                         int b, int h, int s, int d, int causal, int schedule, int dtype,
+                                         float scale, void* workspace, size_t workspace_bytes, void* stream) {
+    return backward(q, k, v, o, dO, lse, dq, dk, dv, b, h, s, d, causal, schedule, dtype, scale, workspace,
+                    workspace_bytes, stream);
+}
+
+extern "C" size_t attn_bwd_workspace_bytes(int b, int h, int s, int d, int causal, int schedule) {
+    (void)causal;
+    (void)schedule;
+    if (b < 0 || h < 0 || s < 0) return 0;
+    WsLayout wl;
+    if (!ws_layout((long long)b * h, s, d, wl)) return 0;
+    return wl.total;
+}
+
+extern "C" int attn_bwd_query_status(void* stream) {
+    g_last_error.clear();
+    hipError_t e = hipStreamSynchronize((hipStream_t)stream);
+    if (e != hipSuccess) return fail_hip(e, "hipStreamSynchronize");
+    std::lock_guard<std::mutex> lock(g_mutex);
+    int dev = 0;
+    e = hipGetDevice(&dev);
+    if (e != hipSuccess) return fail_hip(e, "hipGetDevice");
+    auto it = g_dev.find(dev);
+    if (it == g_dev.end() || !it->second.init) return ATTN_OK;
+    unsigned st = 0;
+    e = hipMemcpy(&st, it->second.status, sizeof(unsigned), hipMemcpyDeviceToHost);
+    if (e != hipSuccess) return fail_hip(e, "hipMemcpy(status)");
+    if (st) {
+        e = hipMemset(it->second.status, 0, sizeof(unsigned));
+        if (e != hipSuccess) return fail_hip(e, "hipMemset(status)");
+        return fail(ATTN_ERR_TIMEOUT, "a dQ flag wait expired; the results of that call are invalid");
+    }
+    return ATTN_OK;
+}
+
+extern "C" const char* attn_bwd_last_error(void) { return g_last_error.c_str(); }
+
+extern "C" int attn_bwd_tile_size(int dtype) {
+    if (dtype != ATTN_BF16 && dtype != ATTN_FP32) return fail(ATTN_ERR_INVALID_ARG, "unknown dtype");
+    return tile_for(dtype);
+}
+
+extern "C" int attn_bwd_set_timing(int on) {
+    std::lock_guard<std::mutex> lock(g_mutex);
+    g_timing = on != 0;
+    if (g_timing)
+        for (auto& kv : g_dev) kv.second.ev_used = 0;
+    return ATTN_OK;
+}
+
+extern "C" int attn_bwd_get_kernel_times(float* ms_pre, float* ms_main, float* ms_fin) {
+    std::lock_guard<std::mutex> lock(g_mutex);
+    if (ms_pre) *ms_pre = 0.f;
+    if (ms_main) *ms_main = 0.f;
+    if (ms_fin) *ms_fin = 0.f;
+    auto it = g_dev.find(g_last_dev);
+    if (it == g_dev.end() || it->second.ev_used == 0) return fail(ATTN_ERR_INVALID_ARG, "no timed call recorded");
+    DevState& ds = it->second;
+    const size_t calls = ds.ev_used;
+    hipError_t e = hipEventSynchronize(ds.ev_pool[4 * calls - 1]);
+    if (e != hipSuccess) return fail_hip(e, "hipEventSynchronize");
+    double sum[3] = {0, 0, 0};
+    for (size_t c = 0; c < calls; ++c) {
+        hipEvent_t* ev = &ds.ev_pool[4 * c];
+        for (int k = 0; k < 3; ++k) {
+            if (k == 2 && !ds.ev_finalize[c]) continue;
+            float t = 0.f;
+            e = hipEventElapsedTime(&t, ev[k], ev[k + 1]);
+            if (e != hipSuccess) return fail_hip(e, "hipEventElapsedTime");
+            sum[k] += t;
+        }
+    }
+    if (ms_pre) *ms_pre = (float)(sum[0] / calls);
+    if (ms_main) *ms_main = (float)(sum[1] / calls);
+    if (ms_fin) *ms_fin = (float)(sum[2] / calls);
+    return ATTN_OK;
+}
+
+extern "C" int attn_bwd_set_wait_stats(int on) {
+    std::lock_guard<std::mutex> lock(g_mutex);
+    g_wait_stats = on != 0;
+    return ATTN_OK;
+}
+
+extern "C" int attn_bwd_get_wait_stats(unsigned long long* wait_cycles, unsigned long long* item_cycles,
+                                       unsigned long long* polls) {
+    std::lock_guard<std::mutex> lock(g_mutex);
+    auto it = g_dev.find(g_last_dev);
+    if (it == g_dev.end() || !it->second.stats_valid || !it->second.last_counters)
+        return fail(ATTN_ERR_INVALID_ARG, "no call with wait statistics recorded");
+    hipError_t e = hipDeviceSynchronize();
+    if (e != hipSuccess) return fail_hip(e, "hipDeviceSynchronize");
+    unsigned long long v[3] = {0, 0, 0};
+    e = hipMemcpy(v, static_cast<unsigned*>(it->second.last_counters) + 2, sizeof(v), hipMemcpyDeviceToHost);
+    if (e != hipSuccess) return fail_hip(e, "hipMemcpy(stats)");
+    if (wait_cycles) *wait_cycles = v[0];
+    if (item_cycles) *item_cycles = v[1];
+    if (polls) *polls = v[2];
+    return ATTN_OK;
+}

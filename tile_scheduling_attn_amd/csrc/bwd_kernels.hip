@@ -1,0 +1,617 @@
+// HIP kernels of the deterministic attention backward for gfx950 (CDNA4).
+//
+// Method: DASH ("DASH: Deterministic Attention Scheduling for
+// High-throughput Reproducible LLM Training").  Fig. 1 of the paper (as
+// captioned on the pith.science review page) shows the tiled backward: the
+// owner of a KV tile accumulates dK/dV locally while partial dQ tiles are
+// reduced globally; the Problem section of the summary page says the
+// deterministic mode serialises those dQ additions in a fixed order.
+// The per-tile arithmetic is the softmax-attention gradient (no formulas are
+// printed on the pages; this is the standard definition):
+//   S = Q_j K_i^T,  P = exp(scale*S - lse_j),  dP = dO_j V_i^T,
+//   dS = P o (dP - D_j),  dV_i += P^T dO_j,  dK_i += dS^T Q_j,
+//   dQ_j += dS K_i  (scale applied to dK and dQ at the end).
+//
+// Mapping onto gfx950.  A work group of 4 wave64s owns one KV tile of T rows
+// (T = 128 for bf16, 64 for fp32).  Wave w keeps K and V rows
+// [w*T/4, (w+1)*T/4) of the tile in registers as MFMA B operands, its dK/dV
+// accumulators in registers for the whole tile, and a K^T slice of D/4
+// columns for the dQ contraction.  Q tiles stream through LDS in 64-row
+// sub-steps, both row-major (A operands of S and dP) and transposed (B
+// operands of dV and dK, whose contraction runs over query rows).  All five
+// contractions use v_mfma_f32_16x16x32_bf16 (fp32 inputs: eight
+// v_mfma_f32_16x16x4_f32 over the same 32-wide k slice).  The 16x16 output
+// layout (lane l holds column l%16, rows 4*(l/16)..+3) is reused directly as
+// the A operand of the next contraction by permuting the contraction index
+// consistently in both operands, so P and dS never leave registers for dV
+// and dK.  dS goes through LDS once for dQ.
+//
+// dQ reduction (the R phase of the pages' DAG).  Deterministic mode: the
+// work group waits until the tile's flag equals its rank in the schedule's
+// fixed order (agent-scope acquire), adds its partial into the fp32
+// accumulator (rank 0 stores, the last contributor writes the output dQ in
+// the output type), and publishes rank+1 (agent-scope release).  No float
+// atomics.  Atomic mode: unordered fp32 atomic adds, then a finalize kernel.
+//
+// Persistent grid: every work group takes work items from a ticket counter
+// in increasing order; items are numbered head-major, so a head's items are
+// all resident before any of them waits (see attn_sched_min_workers).
+#include <hip/hip_runtime.h>
+
+#include "attn_bwd.h"
+#include "internal.h"
+
+namespace attn {
+
+typedef __bf16 bf16;
+typedef bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x8 __attribute__((ext_vector_type(8)));
+
+constexpr float kLog2e = 1.4426950408889634f;
+// A flag wait gives up after this many polls (each poll sleeps ~64 cycles
+// plus a memory round trip, so well under a second in all), sets the
+// call's abort word and the device status word, and continues; once the
+// abort word is set every later wait of the call is skipped, so a broken
+// schedule ends the kernel quickly instead of hanging the device.
+constexpr unsigned kSpinLimit = 1u << 20;
+
+template <typename T> struct Elem;
+
+template <> struct Elem<bf16> {
+    using vec8 = bf16x8;  // MFMA operand: 8 consecutive k values of one row
+    using vec4 = bf16x4;
+    static constexpr int kPad = 8;  // LDS row padding in elements (16 bytes)
+    __device__ static inline f32x4 mma(f32x4 c, vec8 a, vec8 b) {
+        return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+    }
+    __device__ static inline bf16 from_f(float x) { return (bf16)x; }
+    __device__ static inline float to_f(bf16 x) { return (float)x; }
+};
+
+template <> struct Elem<float> {
+    using vec8 = f32x8;
+    using vec4 = f32x4;
+    static constexpr int kPad = 4;
+    // the same 32-wide k slice as the bf16 instruction, as 8 steps of k=4:
+    // step e takes element e of every lane, so lane group l/16 supplies k
+    // slot l/16 of step e for both operands alike.
+    __device__ static inline f32x4 mma(f32x4 c, vec8 a, vec8 b) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) c = __builtin_amdgcn_mfma_f32_16x16x4f32(a[e], b[e], c, 0, 0, 0);
+        return c;
+    }
+    __device__ static inline float from_f(float x) { return x; }
+    __device__ static inline float to_f(float x) { return x; }
+};
+
+struct KParams {
+    const void *q, *k, *v, *dO;
+    const float* lse;
+    const float* delta;
+    void *dq, *dk, *dv;
+    float* dq_acc;
+    unsigned* flags;
+    unsigned* ticket;   // counters[0]: next work item
+    unsigned* abort;    // counters[1]: a wait of this call expired
+    unsigned* status;   // device status word, reported by attn_bwd_query_status
+    unsigned long long* stats;  // null unless wait statistics are on
+    const int* item_begin;
+    const int* task_kv;
+    const int* task_q;
+    const int* rank;
+    const int* count;
+    int H, s, n, items_per_head, s_pad;
+    long long total_items;
+    float scale, scale_log2;
+};
+
+template <typename T, int D, int TILE>
+struct Layout {
+    // query rows per sub-step (fp32 at d=128 halves it to stay within LDS)
+    static constexpr int BQ = (sizeof(T) == 4 && D == 128) ? 32 : 64;
+    static constexpr int LDQ = D + Elem<T>::kPad;   // sQ, sdO row stride
+    static constexpr int LDT = BQ + Elem<T>::kPad;  // sQt, sdOt row stride
+    static constexpr int LDS = TILE + Elem<T>::kPad;  // sdS and sKt row stride
+    static constexpr size_t bytes =
+        sizeof(T) * (2 * (size_t)BQ * LDQ + 2 * (size_t)D * LDT + (size_t)TILE * LDS + (size_t)D * LDS) +
+        2 * BQ * sizeof(float);
+    static_assert(bytes <= 160 * 1024 - 64, "LDS budget of a gfx950 work group exceeded");
+    static_assert(TILE % BQ == 0 && BQ % 32 == 0, "sub-step shape");
+};
+
+template <typename V>
+__device__ inline V zero_vec() {
+    V z;
+#pragma unroll
+    for (int e = 0; e < (int)(sizeof(V) / sizeof(z[0])); ++e) z[e] = 0;
+    return z;
+}
+
+template <typename T, int D, int TILE, bool CAUSAL, bool DET>
+__global__ __launch_bounds__(256, 1) void bwd_main_kernel(KParams p) {
+    using E = Elem<T>;
+    using V8 = typename E::vec8;
+    using V4 = typename E::vec4;
+    using L = Layout<T, D, TILE>;
+    constexpr int BQ = L::BQ, NSUB = TILE / BQ;
+    constexpr int RW = TILE / 4, NT = RW / 16;   // KV rows per wave, 16-row tiles
+    constexpr int DW = D / 4, NDT = DW / 16;     // dQ columns per wave
+    constexpr int KSD = D / 32, KSQ = BQ / 32, KSKV = TILE / 32;
+    constexpr int MT = BQ / 16, DT = D / 16, MTT = TILE / 16;
+    constexpr int LDQ = L::LDQ, LDT = L::LDT, LDSS = L::LDS;
+
+    extern __shared__ __align__(16) unsigned char smem[];
+    T* sQ = reinterpret_cast<T*>(smem);
+    T* sdO = sQ + BQ * LDQ;
+    T* sQt = sdO + BQ * LDQ;
+    T* sdOt = sQt + D * LDT;
+    T* sdS = sdOt + D * LDT;
+    T* sKt = sdS + TILE * LDSS;  // K^T of the current KV tile: [d][key]
+    float* slse = reinterpret_cast<float*>(sKt + D * LDSS);
+    float* sdelta = slse + BQ;
+    __shared__ long long s_item;
+
+    const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, g = lane >> 4, c16 = lane & 15;
+    const T* gQ = static_cast<const T*>(p.q);
+    const T* gK = static_cast<const T*>(p.k);
+    const T* gV = static_cast<const T*>(p.v);
+    const T* gdO = static_cast<const T*>(p.dO);
+    T* gdQ = static_cast<T*>(p.dq);
+    T* gdK = static_cast<T*>(p.dk);
+    T* gdV = static_cast<T*>(p.dv);
+    const int s = p.s, n = p.n;
+
+    unsigned long long wait_cycles = 0, polls = 0, item_cycles = 0;
+
+    for (;;) {
+        if (tid == 0) s_item = (long long)atomicAdd(p.ticket, 1u);
+        __syncthreads();
+        const long long item = s_item;
+        __syncthreads();
+        if (item >= p.total_items) break;
+        const unsigned long long t_item0 = p.stats ? __builtin_readcyclecounter() : 0;
+        const int head = (int)(item / p.items_per_head);
+        const int pat = (int)(item % p.items_per_head);
+        const size_t hoff = (size_t)head * s * D;
+        const int t_end = p.item_begin[pat + 1];
+
+        int cur_kv = -1;
+        f32x4 dK[NT][DT], dV[NT][DT];
+        V8 Kr[NT][KSD], Vr[NT][KSD];
+
+        auto store_dkdv = [&](int kvt) {
+#pragma unroll
+            for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+                for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        const int row = kvt * TILE + w * RW + nt * 16 + 4 * g + i;
+                        if (row < s) {
+                            const size_t off = hoff + (size_t)row * D + dt * 16 + c16;
+                            gdV[off] = E::from_f(dV[nt][dt][i]);
+                            gdK[off] = E::from_f(p.scale * dK[nt][dt][i]);
+                        }
+                    }
+        };
+
+        for (int t = p.item_begin[pat]; t < t_end; ++t) {
+            const int kv = p.task_kv[t], qt = p.task_q[t];
+            if (kv != cur_kv) {
+                if (cur_kv >= 0) store_dkdv(cur_kv);
+                cur_kv = kv;
+#pragma unroll
+                for (int nt = 0; nt < NT; ++nt) {
+                    const int row = kv * TILE + w * RW + nt * 16 + c16;
+#pragma unroll
+                    for (int ks = 0; ks < KSD; ++ks) {
+                        if (row < s) {
+                            const size_t off = hoff + (size_t)row * D + ks * 32 + 8 * g;
+                            Kr[nt][ks] = *reinterpret_cast<const V8*>(gK + off);
+                            Vr[nt][ks] = *reinterpret_cast<const V8*>(gV + off);
+                        } else {
+                            Kr[nt][ks] = zero_vec<V8>();
+                            Vr[nt][ks] = zero_vec<V8>();
+                        }
+                    }
+#pragma unroll
+                    for (int dt = 0; dt < DT; ++dt) {
+                        dK[nt][dt] = zero_vec<f32x4>();
+                        dV[nt][dt] = zero_vec<f32x4>();
+                    }
+                }
+                // K^T of the tile in LDS for the dQ contraction (A operand: d rows,
+                // key columns), once every wave is done with the previous tile's.
+                __syncthreads();
+#pragma unroll
+                for (int c = tid; c < TILE * (D / 8); c += 256) {
+                    const int row = c / (D / 8), col = (c % (D / 8)) * 8;
+                    const int grow = kv * TILE + row;
+                    const V8 vk = grow < s ? *reinterpret_cast<const V8*>(gK + hoff + (size_t)grow * D + col)
+                                           : zero_vec<V8>();
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) sKt[(col + e) * LDSS + row] = vk[e];
+                }
+            }
+
+            const bool diag = CAUSAL && kv == qt;
+            const bool ragged = (kv + 1) * TILE > s || (qt + 1) * TILE > s;
+
+#pragma unroll 1
+            for (int sub = 0; sub < NSUB; ++sub) {
+                const int q0 = qt * TILE + sub * BQ;
+                // ---- stage Q and dO rows [q0, q0+BQ) in LDS, row-major and transposed
+                constexpr int CPR = D / 8;  // 8-element chunks per row
+#pragma unroll
+                for (int c = tid; c < BQ * CPR; c += 256) {
+                    const int row = c / CPR, col = (c % CPR) * 8;
+                    V8 vq, vo;
+                    if (q0 + row < s) {
+                        const size_t off = hoff + (size_t)(q0 + row) * D + col;
+                        vq = *reinterpret_cast<const V8*>(gQ + off);
+                        vo = *reinterpret_cast<const V8*>(gdO + off);
+                    } else {
+                        vq = zero_vec<V8>();
+                        vo = zero_vec<V8>();
+                    }
+                    *reinterpret_cast<V8*>(sQ + row * LDQ + col) = vq;
+                    *reinterpret_cast<V8*>(sdO + row * LDQ + col) = vo;
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) {
+                        sQt[(col + e) * LDT + row] = vq[e];
+                        sdOt[(col + e) * LDT + row] = vo[e];
+                    }
+                }
+                if (tid < BQ) {
+                    const int row = q0 + tid;
+                    slse[tid] = row < s ? p.lse[(size_t)head * s + row] * kLog2e : 0.f;
+                    sdelta[tid] = p.delta[(size_t)head * p.s_pad + row];
+                }
+                __syncthreads();
+
+                // ---- S = Q K^T and dP = dO V^T (rows: queries, cols: this wave's keys)
+                f32x4 S[MT][NT], dP[MT][NT];
+#pragma unroll
+                for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+                    for (int nt = 0; nt < NT; ++nt) {
+                        S[mt][nt] = zero_vec<f32x4>();
+                        dP[mt][nt] = zero_vec<f32x4>();
+                    }
+#pragma unroll
+                for (int ks = 0; ks < KSD; ++ks)
+#pragma unroll
+                    for (int mt = 0; mt < MT; ++mt) {
+                        const V8 aq = *reinterpret_cast<const V8*>(sQ + (mt * 16 + c16) * LDQ + ks * 32 + 8 * g);
+                        const V8 ao = *reinterpret_cast<const V8*>(sdO + (mt * 16 + c16) * LDQ + ks * 32 + 8 * g);
+#pragma unroll
+                        for (int nt = 0; nt < NT; ++nt) {
+                            S[mt][nt] = E::mma(S[mt][nt], aq, Kr[nt][ks]);
+                            dP[mt][nt] = E::mma(dP[mt][nt], ao, Vr[nt][ks]);
+                        }
+                    }
+
+                // ---- P = exp(scale*S - lse), dS = P (dP - D); S/dP overwritten in place
+#pragma unroll
+                for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        const int ql = mt * 16 + 4 * g + i;
+                        const float l2 = slse[ql], dl = sdelta[ql];
+#pragma unroll
+                        for (int nt = 0; nt < NT; ++nt) {
+                            float pv = __builtin_amdgcn_exp2f(S[mt][nt][i] * p.scale_log2 - l2);
+                            if (diag || ragged) {
+                                const int qg = q0 + ql;
+                                const int kg = kv * TILE + w * RW + nt * 16 + c16;
+                                const bool ok = qg < s && kg < s && (!CAUSAL || kg <= qg);
+                                pv = ok ? pv : 0.f;
+                            }
+                            S[mt][nt][i] = pv;
+                            dP[mt][nt][i] = pv * (dP[mt][nt][i] - dl);
+                        }
+                    }
+
+                // ---- dV += P^T dO, dK += dS^T Q (contraction over this sub-step's rows)
+#pragma unroll
+                for (int ks = 0; ks < KSQ; ++ks) {
+                    V8 aP[NT], aS[NT];
+#pragma unroll
+                    for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) {
+                            aP[nt][e] = E::from_f(S[2 * ks][nt][e]);
+                            aP[nt][4 + e] = E::from_f(S[2 * ks + 1][nt][e]);
+                            aS[nt][e] = E::from_f(dP[2 * ks][nt][e]);
+                            aS[nt][4 + e] = E::from_f(dP[2 * ks + 1][nt][e]);
+                        }
+#pragma unroll
+                    for (int dt = 0; dt < DT; ++dt) {
+                        const T* bq = sQt + (dt * 16 + c16) * LDT + ks * 32 + 4 * g;
+                        const T* bo = sdOt + (dt * 16 + c16) * LDT + ks * 32 + 4 * g;
+                        const V8 vq = __builtin_shufflevector(*reinterpret_cast<const V4*>(bq),
+                                                              *reinterpret_cast<const V4*>(bq + 16),
+                                                              0, 1, 2, 3, 4, 5, 6, 7);
+                        const V8 vo = __builtin_shufflevector(*reinterpret_cast<const V4*>(bo),
+                                                              *reinterpret_cast<const V4*>(bo + 16),
+                                                              0, 1, 2, 3, 4, 5, 6, 7);
+#pragma unroll
+                        for (int nt = 0; nt < NT; ++nt) {
+                            dV[nt][dt] = E::mma(dV[nt][dt], aP[nt], vo);
+                            dK[nt][dt] = E::mma(dK[nt][dt], aS[nt], vq);
+                        }
+                    }
+                }
+
+                // ---- dS to LDS as [query][key] for the dQ contraction
+#pragma unroll
+                for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+                    for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+                        for (int i = 0; i < 4; ++i)
+                            sdS[(sub * BQ + mt * 16 + 4 * g + i) * LDSS + w * RW + nt * 16 + c16] =
+                                E::from_f(dP[mt][nt][i]);
+                __syncthreads();
+            }
+
+            // ---- dQ^T[d][q] = K^T[d][key] dS^T[key][q] over the whole tile, for
+            // this wave's d columns (lane: 4 consecutive d of one query row)
+            f32x4 dQt[NDT][MTT];
+#pragma unroll
+            for (int dtw = 0; dtw < NDT; ++dtw)
+#pragma unroll
+                for (int mt = 0; mt < MTT; ++mt) dQt[dtw][mt] = zero_vec<f32x4>();
+#pragma unroll
+            for (int ks = 0; ks < KSKV; ++ks) {
+                V8 a[NDT];
+#pragma unroll
+                for (int dtw = 0; dtw < NDT; ++dtw)
+                    a[dtw] = *reinterpret_cast<const V8*>(sKt + (w * DW + dtw * 16 + c16) * LDSS + ks * 32 + 8 * g);
+#pragma unroll
+                for (int mt = 0; mt < MTT; ++mt) {
+                    const V8 b = *reinterpret_cast<const V8*>(sdS + (mt * 16 + c16) * LDSS + ks * 32 + 8 * g);
+#pragma unroll
+                    for (int dtw = 0; dtw < NDT; ++dtw) dQt[dtw][mt] = E::mma(dQt[dtw][mt], a[dtw], b);
+                }
+            }
+
+            // ---- R phase: add the partial dQ of (kv, qt) into the accumulator
+            float* acc = p.dq_acc + (size_t)head * p.s_pad * D;
+            if (DET) {
+                const int rank = p.rank[kv * n + qt];
+                const int cnt = p.count[qt];
+                unsigned* flag = p.flags + (size_t)head * n + qt;
+                if (rank > 0) {
+                    if (tid == 0) {
+                        const unsigned long long t0 = p.stats ? __builtin_readcyclecounter() : 0;
+                        unsigned spins = 0;
+                        while (__hip_atomic_load(flag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) !=
+                               (unsigned)rank) {
+                            if ((spins & 1023u) == 0 &&
+                                __hip_atomic_load(p.abort, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT))
+                                break;
+                            __builtin_amdgcn_s_sleep(1);
+                            if (++spins >= kSpinLimit) {
+                                atomicOr(p.abort, 1u);
+                                atomicOr(p.status, 1u);
+                                break;
+                            }
+                        }
+                        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+                        if (p.stats) {
+                            wait_cycles += __builtin_readcyclecounter() - t0;
+                            polls += spins + 1;
+                        }
+                    }
+                    __syncthreads();
+                }
+                const bool last = rank == cnt - 1;
+#pragma unroll
+                for (int dtw = 0; dtw < NDT; ++dtw)
+#pragma unroll
+                    for (int mt = 0; mt < MTT; ++mt) {
+                            const int row = qt * TILE + mt * 16 + c16;
+                            const int col = w * DW + dtw * 16 + 4 * g;
+                            f32x4* ptr = reinterpret_cast<f32x4*>(acc + (size_t)row * D + col);
+                            f32x4 val = dQt[dtw][mt];
+                            if (rank > 0) val = *ptr + val;
+                            if (last) {
+                                if (row < s) {
+                                    V4 o;
+#pragma unroll
+                                    for (int e = 0; e < 4; ++e) o[e] = E::from_f(p.scale * val[e]);
+                                    *reinterpret_cast<V4*>(gdQ + hoff + (size_t)row * D + col) = o;
+                                }
+                            } else {
+                                *ptr = val;
+                            }
+                        }
+                if (!last) {
+                    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+                    __syncthreads();
+                    if (tid == 0)
+                        __hip_atomic_store(flag, (unsigned)(rank + 1), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                }
+            } else {
+#pragma unroll
+                for (int dtw = 0; dtw < NDT; ++dtw)
+#pragma unroll
+                    for (int mt = 0; mt < MTT; ++mt) {
+                            const int row = qt * TILE + mt * 16 + c16;
+                            const int col = w * DW + dtw * 16 + 4 * g;
+                            float* ptr = acc + (size_t)row * D + col;
+#pragma unroll
+                            for (int e = 0; e < 4; ++e) unsafeAtomicAdd(ptr + e, dQt[dtw][mt][e]);
+                        }
+            }
+        }
+        if (cur_kv >= 0) store_dkdv(cur_kv);
+        if (p.stats) item_cycles += __builtin_readcyclecounter() - t_item0;
+    }
+    if (p.stats && tid == 0) {
+        atomicAdd(p.stats + 0, wait_cycles);
+        atomicAdd(p.stats + 1, item_cycles);
+        atomicAdd(p.stats + 2, polls);
+    }
+}
+
+// D[head][row] = <dO_row, O_row> in fp32 (zero for padded rows); clears the
+// flags and counters of the call and, for the atomic variant, the dQ
+// accumulator.  16 lanes per row.
+template <typename T, int D>
+__global__ __launch_bounds__(256) void bwd_preprocess_kernel(const T* __restrict__ o, const T* __restrict__ dO,
+                                                              float* __restrict__ delta, int H, int s, int s_pad,
+                                                              unsigned* __restrict__ clear32, int nclear32,
+                                                              float* __restrict__ zero_acc, size_t nzero4) {
+    constexpr int PER = D / 16;
+    const size_t rows = (size_t)H * s_pad;
+    const size_t gtid = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+    const size_t row = gtid / 16;
+    const int part = (int)(gtid % 16);
+    if (row < rows) {
+        const int hh = (int)(row / s_pad), r = (int)(row % s_pad);
+        float acc = 0.f;
+        if (r < s) {
+            const size_t off = ((size_t)hh * s + r) * D + part * PER;
+#pragma unroll
+            for (int e = 0; e < PER; ++e) acc += Elem<T>::to_f(o[off + e]) * Elem<T>::to_f(dO[off + e]);
+        }
+#pragma unroll
+        for (int m = 8; m >= 1; m >>= 1) acc += __shfl_xor(acc, m, 16);
+        if (part == 0) delta[row] = acc;
+    }
+    const size_t nthreads = (size_t)gridDim.x * blockDim.x;
+    for (size_t i = gtid; i < (size_t)nclear32; i += nthreads) clear32[i] = 0u;
+    if (zero_acc) {
+        f32x4* z = reinterpret_cast<f32x4*>(zero_acc);
+        for (size_t i = gtid; i < nzero4; i += nthreads) z[i] = zero_vec<f32x4>();
+    }
+}
+
+// Atomic variant only: dQ = scale * accumulator, converted to the output type.
+template <typename T, int D>
+__global__ __launch_bounds__(256) void bwd_finalize_kernel(const float* __restrict__ acc, T* __restrict__ dq,
+                                                            int H, int s, int s_pad, float scale) {
+    const size_t total4 = (size_t)H * s * D / 4;
+    const size_t nthreads = (size_t)gridDim.x * blockDim.x;
+    for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < total4; i += nthreads) {
+        const size_t e0 = i * 4;
+        const size_t hh = e0 / ((size_t)s * D), rem = e0 % ((size_t)s * D);
+        const f32x4 a = *reinterpret_cast<const f32x4*>(acc + hh * (size_t)s_pad * D + rem);
+        typename Elem<T>::vec4 out;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) out[e] = Elem<T>::from_f(scale * a[e]);
+        *reinterpret_cast<typename Elem<T>::vec4*>(dq + e0) = out;
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Launch
+// ---------------------------------------------------------------------------
+template <typename T, int D, int TILE, bool CAUSAL, bool DET>
+static int launch_main_t(const KParams& kp, const BwdLaunch& L) {
+    auto kern = bwd_main_kernel<T, D, TILE, CAUSAL, DET>;
+    const size_t smem = Layout<T, D, TILE>::bytes;
+    static bool attr_set = false;  // per instantiation; attribute is per device-function
+    if (!attr_set) {
+        if (hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem) != hipSuccess)
+            return fail(ATTN_ERR_HIP, "hipFuncSetAttribute failed for the main kernel");
+        attr_set = true;
+    }
+    int per_cu = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, (const void*)kern, 256, smem) != hipSuccess ||
+        per_cu < 1)
+        return fail(ATTN_ERR_HIP, "occupancy query failed for the main kernel");
+    const long long resident = (long long)per_cu * L.num_cus;
+    if (L.min_workers > resident)
+        return fail(ATTN_ERR_COSCHEDULE,
+                    "schedule needs more simultaneously resident work groups than the device holds");
+    const long long grid = std::min<long long>(resident, kp.total_items);
+    if (grid <= 0) return ATTN_OK;
+    hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(256), smem, (hipStream_t)L.stream, kp);
+    if (hipGetLastError() != hipSuccess) return fail(ATTN_ERR_HIP, "main kernel launch failed");
+    return ATTN_OK;
+}
+
+template <typename T, int D, int TILE>
+static int launch_main_d(const KParams& kp, const BwdLaunch& L, bool causal, bool det) {
+    if (causal)
+        return det ? launch_main_t<T, D, TILE, true, true>(kp, L) : launch_main_t<T, D, TILE, true, false>(kp, L);
+    return det ? launch_main_t<T, D, TILE, false, true>(kp, L) : launch_main_t<T, D, TILE, false, false>(kp, L);
+}
+
+template <typename T, int TILE>
+static int launch_all(const BwdArgs& a, const BwdLaunch& L, KParams& kp) {
+    const T* o = static_cast<const T*>(a.o);
+    const T* dO = static_cast<const T*>(a.dO);
+    const bool det = a.schedule != ATTN_SCHED_ATOMIC;
+    hipStream_t st = (hipStream_t)L.stream;
+
+    // preprocess
+    if (L.ev && hipEventRecord((hipEvent_t)L.ev[0], st) != hipSuccess) return fail(ATTN_ERR_HIP, "hipEventRecord failed");
+    {
+        const size_t rows = (size_t)a.H * a.s_pad;
+        const size_t threads = rows * 16;
+        const unsigned blocks = (unsigned)((threads + 255) / 256);
+        const size_t nzero4 = det ? 0 : (size_t)a.H * a.s_pad * a.d / 4;
+        if (a.d == 64)
+            hipLaunchKernelGGL((bwd_preprocess_kernel<T, 64>), dim3(blocks), dim3(256), 0, st, o, dO, a.delta, a.H,
+                               a.s, (int)a.s_pad, a.flags, L.nclear32, det ? nullptr : a.dq_acc, nzero4);
+        else
+            hipLaunchKernelGGL((bwd_preprocess_kernel<T, 128>), dim3(blocks), dim3(256), 0, st, o, dO, a.delta, a.H,
+                               a.s, (int)a.s_pad, a.flags, L.nclear32, det ? nullptr : a.dq_acc, nzero4);
+        if (hipGetLastError() != hipSuccess) return fail(ATTN_ERR_HIP, "preprocess kernel launch failed");
+    }
+    if (L.ev && hipEventRecord((hipEvent_t)L.ev[1], st) != hipSuccess) return fail(ATTN_ERR_HIP, "hipEventRecord failed");
+    int rc = (a.d == 64) ? launch_main_d<T, 64, TILE>(kp, L, a.causal, det)
+                         : launch_main_d<T, 128, TILE>(kp, L, a.causal, det);
+    if (rc != ATTN_OK) return rc;
+    if (L.ev && hipEventRecord((hipEvent_t)L.ev[2], st) != hipSuccess) return fail(ATTN_ERR_HIP, "hipEventRecord failed");
+    if (!det) {
+        const size_t total4 = (size_t)a.H * a.s * a.d / 4;
+        const unsigned blocks = (unsigned)std::min<size_t>((total4 + 255) / 256, 65536);
+        if (a.d == 64)
+            hipLaunchKernelGGL((bwd_finalize_kernel<T, 64>), dim3(blocks), dim3(256), 0, st, a.dq_acc,
+                               static_cast<T*>(a.dq), a.H, a.s, (int)a.s_pad, a.scale);
+        else
+            hipLaunchKernelGGL((bwd_finalize_kernel<T, 128>), dim3(blocks), dim3(256), 0, st, a.dq_acc,
+                               static_cast<T*>(a.dq), a.H, a.s, (int)a.s_pad, a.scale);
+        if (hipGetLastError() != hipSuccess) return fail(ATTN_ERR_HIP, "finalize kernel launch failed");
+    }
+    if (L.ev && hipEventRecord((hipEvent_t)L.ev[3], st) != hipSuccess) return fail(ATTN_ERR_HIP, "hipEventRecord failed");
+    return ATTN_OK;
+}
+
+int launch_backward(const BwdArgs& a, const BwdLaunch& L) {
+    KParams kp{};
+    kp.q = a.q; kp.k = a.k; kp.v = a.v; kp.dO = a.dO;
+    kp.lse = a.lse;
+    kp.delta = a.delta;
+    kp.dq = a.dq; kp.dk = a.dk; kp.dv = a.dv;
+    kp.dq_acc = a.dq_acc;
+    kp.flags = a.flags;
+    kp.ticket = a.counters;
+    kp.abort = a.counters + 1;
+    kp.status = L.status;
+    kp.stats = L.stats;
+    kp.item_begin = L.item_begin;
+    kp.task_kv = L.task_kv;
+    kp.task_q = L.task_q;
+    kp.rank = L.rank;
+    kp.count = L.count;
+    kp.H = a.H;
+    kp.s = a.s;
+    kp.n = a.n;
+    kp.items_per_head = L.items_per_head;
+    kp.s_pad = (int)a.s_pad;
+    kp.total_items = (long long)a.H * L.items_per_head;
+    kp.scale = a.scale;
+    kp.scale_log2 = a.scale * kLog2e;
+    if (a.dtype == ATTN_BF16) return launch_all<bf16, 128>(a, L, kp);
+    return launch_all<float, 64>(a, L, kp);
+}
+
+}  // namespace attn

@@ -1,0 +1,63 @@
+// Internal declarations shared by the host sources of libattn_bwd.so.
+#pragma once
+
+#include <cstddef>
+#include <vector>
+
+namespace attn {
+
+// One head's schedule pattern (see attn_sched_get in attn_bwd.h).
+struct Schedule {
+    int n = 0;
+    bool causal = false;
+    int schedule = 0;
+    std::vector<int> item_begin;  // num_items + 1
+    std::vector<int> task_kv, task_q;
+    std::vector<int> rank;        // n*n, -1 = masked (or ATOMIC)
+    std::vector<int> count;       // n
+    int num_items() const { return (int)item_begin.size() - 1; }
+};
+
+int build_schedule(int n, bool causal, int schedule, Schedule& out);
+int min_workers(const Schedule& sc);
+int simulate(const Schedule& sc, int heads, int workers, int placement, double c, double r,
+             double* makespan, double* wait_time, double* busy_time);
+
+// Records `msg` as the calling thread's last error and returns `code`.
+int fail(int code, const char* msg);
+
+// Parameters of one backward launch (device pointers).
+struct BwdArgs {
+    const void *q, *k, *v, *o, *dO;
+    const float* lse;
+    void *dq, *dk, *dv;
+    int H, s, d, n, tile;
+    bool causal;
+    int schedule;
+    int dtype;
+    float scale;
+    void* stream;
+    // workspace carve-out
+    float* dq_acc;
+    float* delta;
+    unsigned* flags;
+    unsigned* counters;   // [0] ticket, [1..] wait statistics
+    size_t s_pad;
+};
+
+// Launch-time context prepared by the API layer (device pointers).
+struct BwdLaunch {
+    void* stream;                 // hipStream_t
+    int num_cus;
+    int min_workers;              // resident work groups the schedule needs
+    void** ev;                    // 4 hipEvent_t to record, or null
+    unsigned* status;             // device status word (bit 0: wait expired)
+    unsigned long long* stats;    // wait statistics or null
+    const int *item_begin, *task_kv, *task_q, *rank, *count;
+    int items_per_head;
+    int nclear32;                 // flags + counters words to clear
+};
+
+int launch_backward(const BwdArgs& a, const BwdLaunch& L);
+
+}  // namespace attn
