@@ -37,6 +37,10 @@ class AttnError(RuntimeError):
 
 
 def _load():
+    # PyTorch ships its own HIP runtime (same soname as the system one).  Load
+    # it first so that the library binds to the runtime that owns the
+    # caller's tensors and streams instead of bringing up a second one.
+    import torch  # noqa: F401
     if not os.path.exists(LIB_PATH):
         raise ImportError(f"{LIB_PATH} is missing: build it with "
                           "`python -m tile_scheduling_attn_amd.build`")

@@ -57,10 +57,13 @@ constexpr float kLog2e = 1.4426950408889634f;
 // schedule ends the kernel quickly instead of hanging the device.
 constexpr unsigned kSpinLimit = 1u << 20;
 
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+
 template <typename T> struct Elem;
 
 template <> struct Elem<bf16> {
-    using vec8 = bf16x8;  // MFMA operand: 8 consecutive k values of one row
+    using vec8 = bf16x8;  // MFMA operand: 8 k values of one row or column
     using vec4 = bf16x4;
     static constexpr int kPad = 8;  // LDS row padding in elements (16 bytes)
     __device__ static inline f32x4 mma(f32x4 c, vec8 a, vec8 b) {
@@ -68,6 +71,20 @@ template <> struct Elem<bf16> {
     }
     __device__ static inline bf16 from_f(float x) { return (bf16)x; }
     __device__ static inline float to_f(bf16 x) { return (float)x; }
+    // Operand whose contraction index runs DOWN the columns of a row-major
+    // LDS tile: lane (16g + i) receives column `col + i` at rows
+    // rowA(g)..rowA(g)+3 (elements 0..3) and rowB(g)..rowB(g)+3 (4..7).
+    // ds_read_b64_tr_b16 transposes within each 16-lane group: result lane
+    // i, element e comes from element i%4 of the 4-vector that lane
+    // i/4 + 4e of the group read, so lane j of the group reads row
+    // rowX + j/4, columns col + 4*(j%4) .. +3.
+    __device__ static inline vec8 frag_col(const bf16* base, int ld, int rowA, int rowB, int col, int c16) {
+        const int off = (c16 >> 2) * ld + col + 4 * (c16 & 3);
+        const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(base + rowA * ld + off));
+        const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(base + rowB * ld + off));
+        const s16x4 both[2] = {lo, hi};
+        return *reinterpret_cast<const vec8*>(both);
+    }
 };
 
 template <> struct Elem<float> {
@@ -84,6 +101,16 @@ template <> struct Elem<float> {
     }
     __device__ static inline float from_f(float x) { return x; }
     __device__ static inline float to_f(float x) { return x; }
+    // same contract as the bf16 version, with plain scalar LDS reads
+    __device__ static inline vec8 frag_col(const float* base, int ld, int rowA, int rowB, int col, int c16) {
+        vec8 r;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            r[e] = base[(rowA + e) * ld + col + c16];
+            r[4 + e] = base[(rowB + e) * ld + col + c16];
+        }
+        return r;
+    }
 };
 
 struct KParams {
@@ -107,16 +134,18 @@ struct KParams {
     float scale, scale_log2;
 };
 
+// LDS of one work group, all tiles row-major with padded rows:
+//   sQ, sdO [BQ][D]    query rows of the current sub-step
+//   sK      [TILE][D]  keys of the current KV tile (A operand of dQ^T)
+//   sdS     [TILE][TILE] dS of the current (KV, Q) tile as [query][key]
+//   slse, sdelta [BQ]
 template <typename T, int D, int TILE>
 struct Layout {
-    // query rows per sub-step (fp32 at d=128 halves it to stay within LDS)
-    static constexpr int BQ = (sizeof(T) == 4 && D == 128) ? 32 : 64;
-    static constexpr int LDQ = D + Elem<T>::kPad;   // sQ, sdO row stride
-    static constexpr int LDT = BQ + Elem<T>::kPad;  // sQt, sdOt row stride
-    static constexpr int LDS = TILE + Elem<T>::kPad;  // sdS and sKt row stride
+    static constexpr int BQ = 64;  // query rows per sub-step
+    static constexpr int LDQ = D + Elem<T>::kPad;
+    static constexpr int LDSS = TILE + Elem<T>::kPad;
     static constexpr size_t bytes =
-        sizeof(T) * (2 * (size_t)BQ * LDQ + 2 * (size_t)D * LDT + (size_t)TILE * LDS + (size_t)D * LDS) +
-        2 * BQ * sizeof(float);
+        sizeof(T) * (2 * (size_t)BQ * LDQ + (size_t)TILE * LDQ + (size_t)TILE * LDSS) + 2 * BQ * sizeof(float);
     static_assert(bytes <= 160 * 1024 - 64, "LDS budget of a gfx950 work group exceeded");
     static_assert(TILE % BQ == 0 && BQ % 32 == 0, "sub-step shape");
 };
@@ -127,6 +156,31 @@ __device__ inline V zero_vec() {
 #pragma unroll
     for (int e = 0; e < (int)(sizeof(V) / sizeof(z[0])); ++e) z[e] = 0;
     return z;
+}
+
+// Copy rows [row0, row0 + ROWS) of a [s][D] tensor into a row-major LDS tile
+// (rows >= s read as zero).  All global loads are issued before the first
+// LDS store so their latencies overlap.
+template <typename T, int D, int ROWS, int LD>
+__device__ inline void stage_rows(T* lds, const T* g, int row0, int s, int tid) {
+    using V8 = typename Elem<T>::vec8;
+    constexpr int CPR = D / 8;
+    constexpr int IT = ROWS * CPR / 256;
+    static_assert(ROWS * CPR % 256 == 0, "staging shape");
+    V8 v[IT];
+#pragma unroll
+    for (int it = 0; it < IT; ++it) {
+        const int c = tid + it * 256;
+        const int row = c / CPR, col = (c % CPR) * 8;
+        const int gr = min(row0 + row, s - 1);
+        v[it] = *reinterpret_cast<const V8*>(g + (size_t)gr * D + col);
+    }
+#pragma unroll
+    for (int it = 0; it < IT; ++it) {
+        const int c = tid + it * 256;
+        const int row = c / CPR, col = (c % CPR) * 8;
+        *reinterpret_cast<V8*>(lds + row * LD + col) = (row0 + row < s) ? v[it] : zero_vec<V8>();
+    }
 }
 
 template <typename T, int D, int TILE, bool CAUSAL, bool DET>
@@ -140,16 +194,14 @@ __global__ __launch_bounds__(256, 1) void bwd_main_kernel(KParams p) {
     constexpr int DW = D / 4, NDT = DW / 16;     // dQ columns per wave
     constexpr int KSD = D / 32, KSQ = BQ / 32, KSKV = TILE / 32;
     constexpr int MT = BQ / 16, DT = D / 16, MTT = TILE / 16;
-    constexpr int LDQ = L::LDQ, LDT = L::LDT, LDSS = L::LDS;
+    constexpr int LDQ = L::LDQ, LDSS = L::LDSS;
 
     extern __shared__ __align__(16) unsigned char smem[];
     T* sQ = reinterpret_cast<T*>(smem);
     T* sdO = sQ + BQ * LDQ;
-    T* sQt = sdO + BQ * LDQ;
-    T* sdOt = sQt + D * LDT;
-    T* sdS = sdOt + D * LDT;
-    T* sKt = sdS + TILE * LDSS;  // K^T of the current KV tile: [d][key]
-    float* slse = reinterpret_cast<float*>(sKt + D * LDSS);
+    T* sK = sdO + BQ * LDQ;
+    T* sdS = sK + TILE * LDQ;
+    float* slse = reinterpret_cast<float*>(sdS + TILE * LDSS);
     float* sdelta = slse + BQ;
     __shared__ long long s_item;
 
@@ -202,38 +254,32 @@ __global__ __launch_bounds__(256, 1) void bwd_main_kernel(KParams p) {
             if (kv != cur_kv) {
                 if (cur_kv >= 0) store_dkdv(cur_kv);
                 cur_kv = kv;
+                // this wave's K and V rows as B operands of S and dP
 #pragma unroll
                 for (int nt = 0; nt < NT; ++nt) {
                     const int row = kv * TILE + w * RW + nt * 16 + c16;
+                    const size_t roff = hoff + (size_t)min(row, s - 1) * D;
 #pragma unroll
                     for (int ks = 0; ks < KSD; ++ks) {
-                        if (row < s) {
-                            const size_t off = hoff + (size_t)row * D + ks * 32 + 8 * g;
-                            Kr[nt][ks] = *reinterpret_cast<const V8*>(gK + off);
-                            Vr[nt][ks] = *reinterpret_cast<const V8*>(gV + off);
-                        } else {
+                        Kr[nt][ks] = *reinterpret_cast<const V8*>(gK + roff + ks * 32 + 8 * g);
+                        Vr[nt][ks] = *reinterpret_cast<const V8*>(gV + roff + ks * 32 + 8 * g);
+                    }
+#pragma unroll
+                    for (int ks = 0; ks < KSD; ++ks)
+                        if (row >= s) {
                             Kr[nt][ks] = zero_vec<V8>();
                             Vr[nt][ks] = zero_vec<V8>();
                         }
-                    }
 #pragma unroll
                     for (int dt = 0; dt < DT; ++dt) {
                         dK[nt][dt] = zero_vec<f32x4>();
                         dV[nt][dt] = zero_vec<f32x4>();
                     }
                 }
-                // K^T of the tile in LDS for the dQ contraction (A operand: d rows,
-                // key columns), once every wave is done with the previous tile's.
+                // the whole K tile in LDS for the dQ contraction, once every
+                // wave is done with the previous tile's
                 __syncthreads();
-#pragma unroll
-                for (int c = tid; c < TILE * (D / 8); c += 256) {
-                    const int row = c / (D / 8), col = (c % (D / 8)) * 8;
-                    const int grow = kv * TILE + row;
-                    const V8 vk = grow < s ? *reinterpret_cast<const V8*>(gK + hoff + (size_t)grow * D + col)
-                                           : zero_vec<V8>();
-#pragma unroll
-                    for (int e = 0; e < 8; ++e) sKt[(col + e) * LDSS + row] = vk[e];
-                }
+                stage_rows<T, D, TILE, LDQ>(sK, gK + hoff, kv * TILE, s, tid);
             }
 
             const bool diag = CAUSAL && kv == qt;
@@ -242,28 +288,9 @@ __global__ __launch_bounds__(256, 1) void bwd_main_kernel(KParams p) {
 #pragma unroll 1
             for (int sub = 0; sub < NSUB; ++sub) {
                 const int q0 = qt * TILE + sub * BQ;
-                // ---- stage Q and dO rows [q0, q0+BQ) in LDS, row-major and transposed
-                constexpr int CPR = D / 8;  // 8-element chunks per row
-#pragma unroll
-                for (int c = tid; c < BQ * CPR; c += 256) {
-                    const int row = c / CPR, col = (c % CPR) * 8;
-                    V8 vq, vo;
-                    if (q0 + row < s) {
-                        const size_t off = hoff + (size_t)(q0 + row) * D + col;
-                        vq = *reinterpret_cast<const V8*>(gQ + off);
-                        vo = *reinterpret_cast<const V8*>(gdO + off);
-                    } else {
-                        vq = zero_vec<V8>();
-                        vo = zero_vec<V8>();
-                    }
-                    *reinterpret_cast<V8*>(sQ + row * LDQ + col) = vq;
-                    *reinterpret_cast<V8*>(sdO + row * LDQ + col) = vo;
-#pragma unroll
-                    for (int e = 0; e < 8; ++e) {
-                        sQt[(col + e) * LDT + row] = vq[e];
-                        sdOt[(col + e) * LDT + row] = vo[e];
-                    }
-                }
+                // ---- stage Q and dO rows [q0, q0+BQ) in LDS
+                stage_rows<T, D, BQ, LDQ>(sQ, gQ + hoff, q0, s, tid);
+                stage_rows<T, D, BQ, LDQ>(sdO, gdO + hoff, q0, s, tid);
                 if (tid < BQ) {
                     const int row = q0 + tid;
                     slse[tid] = row < s ? p.lse[(size_t)head * s + row] * kLog2e : 0.f;
@@ -314,7 +341,10 @@ __global__ __launch_bounds__(256, 1) void bwd_main_kernel(KParams p) {
                         }
                     }
 
-                // ---- dV += P^T dO, dK += dS^T Q (contraction over this sub-step's rows)
+                // ---- dV += P^T dO, dK += dS^T Q over this sub-step's rows.  The
+                // contraction index (query row) is permuted alike in both operands:
+                // slot (g, e) is row 16*(2ks + e/4) + 4g + e%4, which is where the
+                // 16x16 output layout of S left P and dS.
 #pragma unroll
                 for (int ks = 0; ks < KSQ; ++ks) {
                     V8 aP[NT], aS[NT];
@@ -327,16 +357,11 @@ __global__ __launch_bounds__(256, 1) void bwd_main_kernel(KParams p) {
                             aS[nt][e] = E::from_f(dP[2 * ks][nt][e]);
                             aS[nt][4 + e] = E::from_f(dP[2 * ks + 1][nt][e]);
                         }
+                    const int rA = ks * 32 + 4 * g, rB = ks * 32 + 16 + 4 * g;
 #pragma unroll
                     for (int dt = 0; dt < DT; ++dt) {
-                        const T* bq = sQt + (dt * 16 + c16) * LDT + ks * 32 + 4 * g;
-                        const T* bo = sdOt + (dt * 16 + c16) * LDT + ks * 32 + 4 * g;
-                        const V8 vq = __builtin_shufflevector(*reinterpret_cast<const V4*>(bq),
-                                                              *reinterpret_cast<const V4*>(bq + 16),
-                                                              0, 1, 2, 3, 4, 5, 6, 7);
-                        const V8 vo = __builtin_shufflevector(*reinterpret_cast<const V4*>(bo),
-                                                              *reinterpret_cast<const V4*>(bo + 16),
-                                                              0, 1, 2, 3, 4, 5, 6, 7);
+                        const V8 vq = E::frag_col(sQ, LDQ, rA, rB, dt * 16, c16);
+                        const V8 vo = E::frag_col(sdO, LDQ, rA, rB, dt * 16, c16);
 #pragma unroll
                         for (int nt = 0; nt < NT; ++nt) {
                             dV[nt][dt] = E::mma(dV[nt][dt], aP[nt], vo);
@@ -369,7 +394,7 @@ __global__ __launch_bounds__(256, 1) void bwd_main_kernel(KParams p) {
                 V8 a[NDT];
 #pragma unroll
                 for (int dtw = 0; dtw < NDT; ++dtw)
-                    a[dtw] = *reinterpret_cast<const V8*>(sKt + (w * DW + dtw * 16 + c16) * LDSS + ks * 32 + 8 * g);
+                    a[dtw] = E::frag_col(sK, LDQ, ks * 32 + 8 * g, ks * 32 + 8 * g + 4, w * DW + dtw * 16, c16);
 #pragma unroll
                 for (int mt = 0; mt < MTT; ++mt) {
                     const V8 b = *reinterpret_cast<const V8*>(sdS + (mt * 16 + c16) * LDSS + ks * 32 + 8 * g);
