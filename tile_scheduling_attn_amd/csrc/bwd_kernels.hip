@@ -28,10 +28,19 @@
 //
 // dQ reduction (the R phase of the pages' DAG).  Deterministic mode: the
 // work group waits until the tile's flag equals its rank in the schedule's
-// fixed order (agent-scope acquire), adds its partial into the fp32
-// accumulator (rank 0 stores, the last contributor writes the output dQ in
-// the output type), and publishes rank+1 (agent-scope release).  No float
-// atomics.  Atomic mode: unordered fp32 atomic adds, then a finalize kernel.
+// fixed order, adds its partial into the fp32 accumulator (rank 0 stores,
+// the last contributor writes the output dQ in the output type), and
+// publishes rank+1.  No float atomics.  Work groups of one head run on all
+// eight XCDs, whose L2 caches are not coherent with each other, so every
+// access to the accumulator and the flags is an agent-scope coherent access
+// (the sc1 cache policy, which is how the gfx942-family memory model
+// implements relaxed agent-scope atomics): such loads never return a stale
+// L2 line and such stores are acknowledged only once visible device-wide.
+// Release is therefore "sc1 stores; s_waitcnt vmcnt(0); barrier; sc1 flag
+// store", acquire is "sc1 flag poll; barrier; sc1 loads", and no L2
+// write-back or invalidate is needed (a buffer_wbl2 per release costs far
+// more than the data it protects).  Atomic mode: unordered fp32 atomic adds,
+// then a finalize kernel.
 //
 // Persistent grid: every work group takes work items from a ticket counter
 // in increasing order; items are numbered head-major, so a head's items are
@@ -149,6 +158,21 @@ struct Layout {
     static_assert(bytes <= 160 * 1024 - 64, "LDS budget of a gfx950 work group exceeded");
     static_assert(TILE % BQ == 0 && BQ % 32 == 0, "sub-step shape");
 };
+
+// Agent-scope coherent (sc1) 16-byte accesses through a raw buffer resource
+// (dword 3 = 0x00020000 is the raw-buffer format word of the gfx9 family;
+// out-of-range offsets read 0 and drop writes).
+constexpr int kCpolSc1 = 16;
+__device__ inline __amdgpu_buffer_rsrc_t make_rsrc(void* base, unsigned bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(base, 0, (int)bytes, 0x00020000);
+}
+__device__ inline f32x4 load_sc1(__amdgpu_buffer_rsrc_t r, unsigned off) {
+    return __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, kCpolSc1));
+}
+__device__ inline void store_sc1(__amdgpu_buffer_rsrc_t r, unsigned off, f32x4 v) {
+    typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), r, (int)off, 0, kCpolSc1);
+}
 
 template <typename V>
 __device__ inline V zero_vec() {
@@ -406,6 +430,7 @@ __global__ __launch_bounds__(256, 1) void bwd_main_kernel(KParams p) {
             // ---- R phase: add the partial dQ of (kv, qt) into the accumulator
             float* acc = p.dq_acc + (size_t)head * p.s_pad * D;
             if (DET) {
+                const __amdgpu_buffer_rsrc_t racc = make_rsrc(acc, (unsigned)(p.s_pad * D * sizeof(float)));
                 const int rank = p.rank[kv * n + qt];
                 const int cnt = p.count[qt];
                 unsigned* flag = p.flags + (size_t)head * n + qt;
@@ -425,7 +450,6 @@ __global__ __launch_bounds__(256, 1) void bwd_main_kernel(KParams p) {
                                 break;
                             }
                         }
-                        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
                         if (p.stats) {
                             wait_cycles += __builtin_readcyclecounter() - t0;
                             polls += spins + 1;
@@ -434,28 +458,47 @@ __global__ __launch_bounds__(256, 1) void bwd_main_kernel(KParams p) {
                     __syncthreads();
                 }
                 const bool last = rank == cnt - 1;
+                const int col0 = w * DW + 4 * g;
+                // every load of the accumulator is issued before the first add
+                // so their latencies overlap (rank 0 stores without reading)
+                if (rank > 0) {
+                    f32x4 prev[NDT][MTT];
 #pragma unroll
-                for (int dtw = 0; dtw < NDT; ++dtw)
+                    for (int dtw = 0; dtw < NDT; ++dtw)
 #pragma unroll
-                    for (int mt = 0; mt < MTT; ++mt) {
+                        for (int mt = 0; mt < MTT; ++mt)
+                            prev[dtw][mt] = load_sc1(
+                                racc, (unsigned)(((qt * TILE + mt * 16 + c16) * D + col0 + dtw * 16) * 4));
+#pragma unroll
+                    for (int dtw = 0; dtw < NDT; ++dtw)
+#pragma unroll
+                        for (int mt = 0; mt < MTT; ++mt) dQt[dtw][mt] = prev[dtw][mt] + dQt[dtw][mt];
+                }
+                if (last) {
+                    // the last contributor writes dQ = scale * sum in the output type
+#pragma unroll
+                    for (int dtw = 0; dtw < NDT; ++dtw)
+#pragma unroll
+                        for (int mt = 0; mt < MTT; ++mt) {
                             const int row = qt * TILE + mt * 16 + c16;
-                            const int col = w * DW + dtw * 16 + 4 * g;
-                            f32x4* ptr = reinterpret_cast<f32x4*>(acc + (size_t)row * D + col);
-                            f32x4 val = dQt[dtw][mt];
-                            if (rank > 0) val = *ptr + val;
-                            if (last) {
-                                if (row < s) {
-                                    V4 o;
+                            V4 o;
 #pragma unroll
-                                    for (int e = 0; e < 4; ++e) o[e] = E::from_f(p.scale * val[e]);
-                                    *reinterpret_cast<V4*>(gdQ + hoff + (size_t)row * D + col) = o;
-                                }
-                            } else {
-                                *ptr = val;
-                            }
+                            for (int e = 0; e < 4; ++e) o[e] = E::from_f(p.scale * dQt[dtw][mt][e]);
+                            if (row < s)
+                                *reinterpret_cast<V4*>(gdQ + hoff + (size_t)row * D + col0 + dtw * 16) = o;
                         }
+                } else {
+#pragma unroll
+                    for (int dtw = 0; dtw < NDT; ++dtw)
+#pragma unroll
+                        for (int mt = 0; mt < MTT; ++mt)
+                            store_sc1(racc, (unsigned)(((qt * TILE + mt * 16 + c16) * D + col0 + dtw * 16) * 4),
+                                      dQt[dtw][mt]);
+                }
                 if (!last) {
-                    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+                    // every wave's accumulator stores acknowledged (device-wide
+                    // visible) before the flag moves on
+                    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
                     __syncthreads();
                     if (tid == 0)
                         __hip_atomic_store(flag, (unsigned)(rank + 1), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
