@@ -254,8 +254,19 @@ __global__ __launch_bounds__(256, 1) void bwd_main_kernel(KParams p) {
         const int t_end = p.item_begin[pat + 1];
 
         int cur_kv = -1;
+        // release of the last accumulator update, not yet published: every
+        // wave waits for its sc1 stores to be acknowledged (device-wide
+        // visible), then after a barrier one thread moves the flag on
+        unsigned* pend_flag = nullptr;
+        unsigned pend_val = 0;
+        auto publish = [&]() {
+            asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+            __syncthreads();
+            if (tid == 0) __hip_atomic_store(pend_flag, pend_val, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            pend_flag = nullptr;
+        };
         f32x4 dK[NT][DT], dV[NT][DT];
-        V8 Kr[NT][KSD], Vr[NT][KSD];
+        V8 Vr[NT][KSD];
 
         auto store_dkdv = [&](int kvt) {
 #pragma unroll
@@ -278,22 +289,17 @@ __global__ __launch_bounds__(256, 1) void bwd_main_kernel(KParams p) {
             if (kv != cur_kv) {
                 if (cur_kv >= 0) store_dkdv(cur_kv);
                 cur_kv = kv;
-                // this wave's K and V rows as B operands of S and dP
+                // this wave's V rows as B operands of dP (its K rows are read
+                // from the LDS copy of the tile when S is formed)
 #pragma unroll
                 for (int nt = 0; nt < NT; ++nt) {
                     const int row = kv * TILE + w * RW + nt * 16 + c16;
                     const size_t roff = hoff + (size_t)min(row, s - 1) * D;
 #pragma unroll
-                    for (int ks = 0; ks < KSD; ++ks) {
-                        Kr[nt][ks] = *reinterpret_cast<const V8*>(gK + roff + ks * 32 + 8 * g);
-                        Vr[nt][ks] = *reinterpret_cast<const V8*>(gV + roff + ks * 32 + 8 * g);
-                    }
+                    for (int ks = 0; ks < KSD; ++ks) Vr[nt][ks] = *reinterpret_cast<const V8*>(gV + roff + ks * 32 + 8 * g);
 #pragma unroll
                     for (int ks = 0; ks < KSD; ++ks)
-                        if (row >= s) {
-                            Kr[nt][ks] = zero_vec<V8>();
-                            Vr[nt][ks] = zero_vec<V8>();
-                        }
+                        if (row >= s) Vr[nt][ks] = zero_vec<V8>();
 #pragma unroll
                     for (int dt = 0; dt < DT; ++dt) {
                         dK[nt][dt] = zero_vec<f32x4>();
@@ -320,7 +326,8 @@ __global__ __launch_bounds__(256, 1) void bwd_main_kernel(KParams p) {
                     slse[tid] = row < s ? p.lse[(size_t)head * s + row] * kLog2e : 0.f;
                     sdelta[tid] = p.delta[(size_t)head * p.s_pad + row];
                 }
-                __syncthreads();
+                if (pend_flag) publish();  // this barrier also ends the staging
+                else __syncthreads();
 
                 // ---- S = Q K^T and dP = dO V^T (rows: queries, cols: this wave's keys)
                 f32x4 S[MT][NT], dP[MT][NT];
@@ -332,17 +339,22 @@ __global__ __launch_bounds__(256, 1) void bwd_main_kernel(KParams p) {
                         dP[mt][nt] = zero_vec<f32x4>();
                     }
 #pragma unroll
-                for (int ks = 0; ks < KSD; ++ks)
+                for (int ks = 0; ks < KSD; ++ks) {
+                    V8 bk[NT];
+#pragma unroll
+                    for (int nt = 0; nt < NT; ++nt)
+                        bk[nt] = *reinterpret_cast<const V8*>(sK + (w * RW + nt * 16 + c16) * LDQ + ks * 32 + 8 * g);
 #pragma unroll
                     for (int mt = 0; mt < MT; ++mt) {
                         const V8 aq = *reinterpret_cast<const V8*>(sQ + (mt * 16 + c16) * LDQ + ks * 32 + 8 * g);
                         const V8 ao = *reinterpret_cast<const V8*>(sdO + (mt * 16 + c16) * LDQ + ks * 32 + 8 * g);
 #pragma unroll
                         for (int nt = 0; nt < NT; ++nt) {
-                            S[mt][nt] = E::mma(S[mt][nt], aq, Kr[nt][ks]);
+                            S[mt][nt] = E::mma(S[mt][nt], aq, bk[nt]);
                             dP[mt][nt] = E::mma(dP[mt][nt], ao, Vr[nt][ks]);
                         }
                     }
+                }
 
                 // ---- P = exp(scale*S - lse), dS = P (dP - D); S/dP overwritten in place
 #pragma unroll
@@ -406,33 +418,19 @@ __global__ __launch_bounds__(256, 1) void bwd_main_kernel(KParams p) {
                 __syncthreads();
             }
 
-            // ---- dQ^T[d][q] = K^T[d][key] dS^T[key][q] over the whole tile, for
-            // this wave's d columns (lane: 4 consecutive d of one query row)
-            f32x4 dQt[NDT][MTT];
-#pragma unroll
-            for (int dtw = 0; dtw < NDT; ++dtw)
-#pragma unroll
-                for (int mt = 0; mt < MTT; ++mt) dQt[dtw][mt] = zero_vec<f32x4>();
-#pragma unroll
-            for (int ks = 0; ks < KSKV; ++ks) {
-                V8 a[NDT];
-#pragma unroll
-                for (int dtw = 0; dtw < NDT; ++dtw)
-                    a[dtw] = E::frag_col(sK, LDQ, ks * 32 + 8 * g, ks * 32 + 8 * g + 4, w * DW + dtw * 16, c16);
-#pragma unroll
-                for (int mt = 0; mt < MTT; ++mt) {
-                    const V8 b = *reinterpret_cast<const V8*>(sdS + (mt * 16 + c16) * LDSS + ks * 32 + 8 * g);
-#pragma unroll
-                    for (int dtw = 0; dtw < NDT; ++dtw) dQt[dtw][mt] = E::mma(dQt[dtw][mt], a[dtw], b);
-                }
-            }
-
-            // ---- R phase: add the partial dQ of (kv, qt) into the accumulator
+            // ---- R phase, first half: wait for this tile's turn and start the
+            // accumulator loads now, so that their latency overlaps the dQ
+            // contraction below.  The previous task's release was published
+            // at this task's first barrier, so the work group holds no
+            // unpublished release while it waits.
             float* acc = p.dq_acc + (size_t)head * p.s_pad * D;
+            const __amdgpu_buffer_rsrc_t racc = make_rsrc(acc, (unsigned)(p.s_pad * D * sizeof(float)));
+            const int col0 = w * DW + 4 * g;
+            int rank = 0, cnt = 1;
+            f32x4 prev[NDT][MTT];
             if (DET) {
-                const __amdgpu_buffer_rsrc_t racc = make_rsrc(acc, (unsigned)(p.s_pad * D * sizeof(float)));
-                const int rank = p.rank[kv * n + qt];
-                const int cnt = p.count[qt];
+                rank = p.rank[kv * n + qt];
+                cnt = p.count[qt];
                 unsigned* flag = p.flags + (size_t)head * n + qt;
                 if (rank > 0) {
                     if (tid == 0) {
@@ -456,66 +454,90 @@ __global__ __launch_bounds__(256, 1) void bwd_main_kernel(KParams p) {
                         }
                     }
                     __syncthreads();
-                }
-                const bool last = rank == cnt - 1;
-                const int col0 = w * DW + 4 * g;
-                // every load of the accumulator is issued before the first add
-                // so their latencies overlap (rank 0 stores without reading)
-                if (rank > 0) {
-                    f32x4 prev[NDT][MTT];
 #pragma unroll
                     for (int dtw = 0; dtw < NDT; ++dtw)
 #pragma unroll
                         for (int mt = 0; mt < MTT; ++mt)
                             prev[dtw][mt] = load_sc1(
                                 racc, (unsigned)(((qt * TILE + mt * 16 + c16) * D + col0 + dtw * 16) * 4));
-#pragma unroll
-                    for (int dtw = 0; dtw < NDT; ++dtw)
-#pragma unroll
-                        for (int mt = 0; mt < MTT; ++mt) dQt[dtw][mt] = prev[dtw][mt] + dQt[dtw][mt];
                 }
-                if (last) {
-                    // the last contributor writes dQ = scale * sum in the output type
+            }
+
+            // ---- dQ^T[d][q] = K^T[d][key] dS^T[key][q] over the tile, for this
+            // wave's d columns (lane: 4 consecutive d of one query row), in two
+            // halves of query rows; each half is added into the accumulator
+            // as soon as it is done (R phase, second half).
+            constexpr int MTH = MTT / 2;
+#pragma unroll
+            for (int half = 0; half < 2; ++half) {
+                f32x4 dQt[NDT][MTH];
+#pragma unroll
+                for (int dtw = 0; dtw < NDT; ++dtw)
+#pragma unroll
+                    for (int j = 0; j < MTH; ++j) dQt[dtw][j] = zero_vec<f32x4>();
+#pragma unroll
+                for (int ks = 0; ks < KSKV; ++ks) {
+                    V8 a[NDT];
 #pragma unroll
                     for (int dtw = 0; dtw < NDT; ++dtw)
+                        a[dtw] = E::frag_col(sK, LDQ, ks * 32 + 8 * g, ks * 32 + 8 * g + 4, w * DW + dtw * 16, c16);
 #pragma unroll
-                        for (int mt = 0; mt < MTT; ++mt) {
-                            const int row = qt * TILE + mt * 16 + c16;
-                            V4 o;
+                    for (int j = 0; j < MTH; ++j) {
+                        const int mt = half * MTH + j;
+                        const V8 b = *reinterpret_cast<const V8*>(sdS + (mt * 16 + c16) * LDSS + ks * 32 + 8 * g);
 #pragma unroll
-                            for (int e = 0; e < 4; ++e) o[e] = E::from_f(p.scale * dQt[dtw][mt][e]);
-                            if (row < s)
-                                *reinterpret_cast<V4*>(gdQ + hoff + (size_t)row * D + col0 + dtw * 16) = o;
-                        }
+                        for (int dtw = 0; dtw < NDT; ++dtw) dQt[dtw][j] = E::mma(dQt[dtw][j], a[dtw], b);
+                    }
+                }
+                if (DET) {
+                    if (rank > 0) {
+#pragma unroll
+                        for (int dtw = 0; dtw < NDT; ++dtw)
+#pragma unroll
+                            for (int j = 0; j < MTH; ++j) dQt[dtw][j] = prev[dtw][half * MTH + j] + dQt[dtw][j];
+                    }
+                    if (rank == cnt - 1) {
+                        // the last contributor writes dQ = scale * sum in the output type
+#pragma unroll
+                        for (int dtw = 0; dtw < NDT; ++dtw)
+#pragma unroll
+                            for (int j = 0; j < MTH; ++j) {
+                                const int row = qt * TILE + (half * MTH + j) * 16 + c16;
+                                V4 o;
+#pragma unroll
+                                for (int e = 0; e < 4; ++e) o[e] = E::from_f(p.scale * dQt[dtw][j][e]);
+                                if (row < s)
+                                    *reinterpret_cast<V4*>(gdQ + hoff + (size_t)row * D + col0 + dtw * 16) = o;
+                            }
+                    } else {
+#pragma unroll
+                        for (int dtw = 0; dtw < NDT; ++dtw)
+#pragma unroll
+                            for (int j = 0; j < MTH; ++j)
+                                store_sc1(racc,
+                                          (unsigned)(((qt * TILE + (half * MTH + j) * 16 + c16) * D + col0 +
+                                                      dtw * 16) * 4),
+                                          dQt[dtw][j]);
+                    }
                 } else {
 #pragma unroll
                     for (int dtw = 0; dtw < NDT; ++dtw)
 #pragma unroll
-                        for (int mt = 0; mt < MTT; ++mt)
-                            store_sc1(racc, (unsigned)(((qt * TILE + mt * 16 + c16) * D + col0 + dtw * 16) * 4),
-                                      dQt[dtw][mt]);
-                }
-                if (!last) {
-                    // every wave's accumulator stores acknowledged (device-wide
-                    // visible) before the flag moves on
-                    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-                    __syncthreads();
-                    if (tid == 0)
-                        __hip_atomic_store(flag, (unsigned)(rank + 1), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-                }
-            } else {
+                        for (int j = 0; j < MTH; ++j) {
+                            float* ptr = acc + (size_t)(qt * TILE + (half * MTH + j) * 16 + c16) * D + col0 + dtw * 16;
 #pragma unroll
-                for (int dtw = 0; dtw < NDT; ++dtw)
-#pragma unroll
-                    for (int mt = 0; mt < MTT; ++mt) {
-                            const int row = qt * TILE + mt * 16 + c16;
-                            const int col = w * DW + dtw * 16 + 4 * g;
-                            float* ptr = acc + (size_t)row * D + col;
-#pragma unroll
-                            for (int e = 0; e < 4; ++e) unsafeAtomicAdd(ptr + e, dQt[dtw][mt][e]);
+                            for (int e = 0; e < 4; ++e) unsafeAtomicAdd(ptr + e, dQt[dtw][j][e]);
                         }
+                }
+            }
+            if (DET && rank != cnt - 1) {
+                // published after the next barrier that follows a full
+                // s_waitcnt (next task's staging, or the end of the item)
+                pend_flag = p.flags + (size_t)head * n + qt;
+                pend_val = (unsigned)(rank + 1);
             }
         }
+        if (pend_flag) publish();
         if (cur_kv >= 0) store_dkdv(cur_kv);
         if (p.stats) item_cycles += __builtin_readcyclecounter() - t_item0;
     }
