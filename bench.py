@@ -111,6 +111,9 @@ def main():
     ap.add_argument("--compare", default="naive,atomic",
                     help="comma list of schedules also timed for context ('' for none)")
     ap.add_argument("--cpu-heads", type=int, default=4, help="heads in the CPU oracle sample (0: skip)")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="only run a plain device copy of MIB MiB five times (scales the HBM "
+                         "traffic counters of a profiler run) and exit")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -121,6 +124,16 @@ def main():
         sys.exit(2)
 
     import torch
+    if args.copy_calibration:
+        n = args.copy_calibration * (1 << 20) // 4
+        src = torch.ones(n, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_calibration_bytes_read": n * 4, "copy_calibration_bytes_written": n * 4,
+                          "launches": 5}))
+        return
     import tile_scheduling_attn_amd as tsa
     import workloads
     from tests.support import Problem

@@ -80,20 +80,6 @@ template <> struct Elem<bf16> {
     }
     __device__ static inline bf16 from_f(float x) { return (bf16)x; }
     __device__ static inline float to_f(bf16 x) { return (float)x; }
-    // Operand whose contraction index runs DOWN the columns of a row-major
-    // LDS tile: lane (16g + i) receives column `col + i` at rows
-    // rowA(g)..rowA(g)+3 (elements 0..3) and rowB(g)..rowB(g)+3 (4..7).
-    // ds_read_b64_tr_b16 transposes within each 16-lane group: result lane
-    // i, element e comes from element i%4 of the 4-vector that lane
-    // i/4 + 4e of the group read, so lane j of the group reads row
-    // rowX + j/4, columns col + 4*(j%4) .. +3.
-    __device__ static inline vec8 frag_col(const bf16* base, int ld, int rowA, int rowB, int col, int c16) {
-        const int off = (c16 >> 2) * ld + col + 4 * (c16 & 3);
-        const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(base + rowA * ld + off));
-        const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(base + rowB * ld + off));
-        const s16x4 both[2] = {lo, hi};
-        return *reinterpret_cast<const vec8*>(both);
-    }
 };
 
 template <> struct Elem<float> {
@@ -110,16 +96,6 @@ template <> struct Elem<float> {
     }
     __device__ static inline float from_f(float x) { return x; }
     __device__ static inline float to_f(float x) { return x; }
-    // same contract as the bf16 version, with plain scalar LDS reads
-    __device__ static inline vec8 frag_col(const float* base, int ld, int rowA, int rowB, int col, int c16) {
-        vec8 r;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            r[e] = base[(rowA + e) * ld + col + c16];
-            r[4 + e] = base[(rowB + e) * ld + col + c16];
-        }
-        return r;
-    }
 };
 
 struct KParams {
@@ -141,22 +117,6 @@ struct KParams {
     int H, s, n, items_per_head, s_pad;
     long long total_items;
     float scale, scale_log2;
-};
-
-// LDS of one work group, all tiles row-major with padded rows:
-//   sQ, sdO [BQ][D]    query rows of the current sub-step
-//   sK      [TILE][D]  keys of the current KV tile (A operand of dQ^T)
-//   sdS     [TILE][TILE] dS of the current (KV, Q) tile as [query][key]
-//   slse, sdelta [BQ]
-template <typename T, int D, int TILE>
-struct Layout {
-    static constexpr int BQ = 64;  // query rows per sub-step
-    static constexpr int LDQ = D + Elem<T>::kPad;
-    static constexpr int LDSS = TILE + Elem<T>::kPad;
-    static constexpr size_t bytes =
-        sizeof(T) * (2 * (size_t)BQ * LDQ + (size_t)TILE * LDQ + (size_t)TILE * LDSS) + 2 * BQ * sizeof(float);
-    static_assert(bytes <= 160 * 1024 - 64, "LDS budget of a gfx950 work group exceeded");
-    static_assert(TILE % BQ == 0 && BQ % 32 == 0, "sub-step shape");
 };
 
 // Agent-scope coherent (sc1) 16-byte accesses through a raw buffer resource
@@ -182,30 +142,115 @@ __device__ inline V zero_vec() {
     return z;
 }
 
-// Copy rows [row0, row0 + ROWS) of a [s][D] tensor into a row-major LDS tile
-// (rows >= s read as zero).  All global loads are issued before the first
-// LDS store so their latencies overlap.
-template <typename T, int D, int ROWS, int LD>
-__device__ inline void stage_rows(T* lds, const T* g, int row0, int s, int tid) {
-    using V8 = typename Elem<T>::vec8;
-    constexpr int CPR = D / 8;
-    constexpr int IT = ROWS * CPR / 256;
-    static_assert(ROWS * CPR % 256 == 0, "staging shape");
-    V8 v[IT];
+// Row-major LDS tile of rows of D elements with 16 bytes of padding per row
+// (row stride RS = row bytes + 16, so the 16 rows read by one 16-lane
+// operand fetch start 4 banks apart).  It is filled straight from global
+// memory by global_load_lds_dwordx4: each wave-wide load fills 1 KiB of LDS,
+// lane l writing bytes [16l, 16l+16); a lane whose slot falls in a row's
+// padding is switched off.
+template <typename T, int D>
+struct Pad {
+    static constexpr int RB = D * (int)sizeof(T);  // data bytes per row
+    static constexpr int RS = RB + 16;            // row stride in bytes
+    __device__ static inline int off(int row, int col) { return row * RS + col * (int)sizeof(T); }
+};
+
+// Issue the loads of rows [row0, row0 + ROWS) of a [s][D] tensor into a
+// padded LDS tile, 1 KiB blocks dealt round-robin over the 4 waves.  Rows
+// past the end repeat row s-1 (finite values that the masks of ragged tiles
+// remove).  Completion: s_waitcnt vmcnt(0), then a barrier.
+template <typename T, int D, int ROWS>
+__device__ inline void load_tile_async(unsigned char* tile, const T* g, int row0, int s, int w, int lane) {
+    using P = Pad<T, D>;
+    constexpr int TOTAL = ROWS * P::RS;
+    constexpr int BLOCKS = (TOTAL + 1023) / 1024;
 #pragma unroll
-    for (int it = 0; it < IT; ++it) {
-        const int c = tid + it * 256;
-        const int row = c / CPR, col = (c % CPR) * 8;
-        const int gr = min(row0 + row, s - 1);
-        v[it] = *reinterpret_cast<const V8*>(g + (size_t)gr * D + col);
-    }
-#pragma unroll
-    for (int it = 0; it < IT; ++it) {
-        const int c = tid + it * 256;
-        const int row = c / CPR, col = (c % CPR) * 8;
-        *reinterpret_cast<V8*>(lds + row * LD + col) = (row0 + row < s) ? v[it] : zero_vec<V8>();
+    for (int it = 0; it < (BLOCKS + 3) / 4; ++it) {
+        const int blk = w + 4 * it;
+        if (blk < BLOCKS) {
+            const int byte = blk * 1024 + lane * 16;
+            const int row = byte / P::RS, inrow = byte % P::RS;
+            if (byte < TOTAL && inrow < P::RB) {
+                const int gr = min(row0 + row, s - 1);
+                const char* src = reinterpret_cast<const char*>(g + (size_t)gr * D) + inrow;
+                __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)(src),
+                                                 (__attribute__((address_space(3))) void*)(tile + blk * 1024), 16, 0,
+                                                 0);
+            }
+        }
     }
 }
+
+// 64 consecutive fp32 values (rows [row0, row0+n) of a per-row vector, row
+// index clamped to rmax) into LDS, by one wave.
+__device__ inline void load_vec_async(float* dst, const float* src, int row0, int n, int rmax, int lane) {
+    if (lane < n)
+        __builtin_amdgcn_global_load_lds(
+            (const __attribute__((address_space(1))) void*)(src + min(row0 + lane, rmax)),
+            (__attribute__((address_space(3))) void*)dst, 4, 0, 0);
+}
+
+// MFMA operand whose contraction index runs ALONG a row of a padded tile:
+// lane (16g + i) gets row `row`, elements col .. col+7 (col = 8-aligned).
+template <typename T, int D>
+__device__ inline typename Elem<T>::vec8 frag_row(const unsigned char* tile, int row, int col) {
+    using S = Pad<T, D>;
+    using V8 = typename Elem<T>::vec8;
+    if constexpr (sizeof(T) == 2) {
+        return *reinterpret_cast<const V8*>(tile + S::off(row, col));
+    } else {
+        const f32x4 a = *reinterpret_cast<const f32x4*>(tile + S::off(row, col));
+        const f32x4 b = *reinterpret_cast<const f32x4*>(tile + S::off(row, col + 4));
+        return __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7);
+    }
+}
+
+// MFMA operand whose contraction index runs DOWN the columns of a padded
+// tile: lane (16g + i) receives column col + i at rows rowA..rowA+3
+// (elements 0..3) and rowB..rowB+3 (elements 4..7), rowA/rowB chosen per
+// lane group.  For bf16, ds_read_b64_tr_b16 transposes within each 16-lane
+// group: result lane i, element e is element i%4 of the 4-vector read by
+// lane i/4 + 4e of the group, so lane j of the group reads row rowX + j/4,
+// columns col + 4*(j%4) .. +3.  fp32 uses plain scalar reads.
+template <typename T, int D>
+__device__ inline typename Elem<T>::vec8 frag_col(const unsigned char* tile, int rowA, int rowB, int col, int c16) {
+    using S = Pad<T, D>;
+    typename Elem<T>::vec8 r;
+    if constexpr (sizeof(T) == 2) {
+        const int rr = c16 >> 2, cc = col + 4 * (c16 & 3);
+        const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(tile + S::off(rowA + rr, cc)));
+        const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(tile + S::off(rowB + rr, cc)));
+        const s16x4 both[2] = {lo, hi};
+        r = *reinterpret_cast<const typename Elem<T>::vec8*>(both);
+    } else {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            r[e] = *reinterpret_cast<const float*>(tile + S::off(rowA + e, col + c16));
+            r[4 + e] = *reinterpret_cast<const float*>(tile + S::off(rowB + e, col + c16));
+        }
+    }
+    return r;
+}
+
+// LDS of one work group:
+//   sQ[2], sdO[2]  padded [BQ][D]   query rows of a sub-step (double buffer)
+//   sK             padded [TILE][D] keys of the current KV tile
+//   sdS            [TILE][TILE] (+pad) dS of the current task as [query][key]
+//   slse[2], sdelta[2] [BQ]
+template <typename T, int D, int TILE>
+struct Layout {
+    // query rows per sub-step (fp32 at d=128 halves it to stay within LDS)
+    static constexpr int BQ = (sizeof(T) == 4 && D == 128) ? 32 : 64;
+    static constexpr int QB = BQ * Pad<T, D>::RS;    // bytes of one Q (or dO) buffer
+    static constexpr int KB = TILE * Pad<T, D>::RS;  // bytes of sK
+    static constexpr int LDSS = TILE + Elem<T>::kPad;
+    static constexpr int SB = TILE * LDSS * (int)sizeof(T);
+    static constexpr int OFF_Q = 0, OFF_DO = 2 * QB, OFF_K = 4 * QB, OFF_S = OFF_K + KB;
+    static constexpr int OFF_LSE = OFF_S + SB, OFF_DEL = OFF_LSE + 2 * BQ * 4;
+    static constexpr size_t bytes = OFF_DEL + 2 * BQ * 4;
+    static_assert(bytes <= 160 * 1024 - 64, "LDS budget of a gfx950 work group exceeded");
+    static_assert(TILE % BQ == 0 && BQ % 32 == 0, "sub-step shape");
+};
 
 template <typename T, int D, int TILE, bool CAUSAL, bool DET>
 __global__ __launch_bounds__(256, 1) void bwd_main_kernel(KParams p) {
@@ -218,15 +263,11 @@ __global__ __launch_bounds__(256, 1) void bwd_main_kernel(KParams p) {
     constexpr int DW = D / 4, NDT = DW / 16;     // dQ columns per wave
     constexpr int KSD = D / 32, KSQ = BQ / 32, KSKV = TILE / 32;
     constexpr int MT = BQ / 16, DT = D / 16, MTT = TILE / 16;
-    constexpr int LDQ = L::LDQ, LDSS = L::LDSS;
+    constexpr int LDSS = L::LDSS;
 
     extern __shared__ __align__(16) unsigned char smem[];
-    T* sQ = reinterpret_cast<T*>(smem);
-    T* sdO = sQ + BQ * LDQ;
-    T* sK = sdO + BQ * LDQ;
-    T* sdS = sK + TILE * LDQ;
-    float* slse = reinterpret_cast<float*>(sdS + TILE * LDSS);
-    float* sdelta = slse + BQ;
+    unsigned char* sK = smem + L::OFF_K;
+    T* sdS = reinterpret_cast<T*>(smem + L::OFF_S);
     __shared__ long long s_item;
 
     const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, g = lane >> 4, c16 = lane & 15;
@@ -264,6 +305,18 @@ __global__ __launch_bounds__(256, 1) void bwd_main_kernel(KParams p) {
             __syncthreads();
             if (tid == 0) __hip_atomic_store(pend_flag, pend_val, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
             pend_flag = nullptr;
+        };
+        // Q/dO double buffer: `buf` is the buffer the next sub-step reads;
+        // `staged` says whether its rows were already requested
+        int buf = 0;
+        bool staged = false;
+        auto issue_q = [&](int b, int q0) {
+            load_tile_async<T, D, BQ>(smem + L::OFF_Q + b * L::QB, gQ + hoff, q0, s, w, lane);
+            load_tile_async<T, D, BQ>(smem + L::OFF_DO + b * L::QB, gdO + hoff, q0, s, w, lane);
+            float* dl = reinterpret_cast<float*>(smem + L::OFF_LSE) + b * BQ;
+            float* dd = reinterpret_cast<float*>(smem + L::OFF_DEL) + b * BQ;
+            if (w == 0) load_vec_async(dl, p.lse + (size_t)head * s, q0, BQ, s - 1, lane);
+            if (w == 1) load_vec_async(dd, p.delta + (size_t)head * p.s_pad, q0, BQ, p.s_pad - 1, lane);
         };
         f32x4 dK[NT][DT], dV[NT][DT];
         V8 Vr[NT][KSD];
@@ -306,28 +359,51 @@ __global__ __launch_bounds__(256, 1) void bwd_main_kernel(KParams p) {
                         dV[nt][dt] = zero_vec<f32x4>();
                     }
                 }
-                // the whole K tile in LDS for the dQ contraction, once every
-                // wave is done with the previous tile's
+                // the whole K tile in LDS (B operand of S, A operand of dQ^T),
+                // once every wave is done with the previous tile's
                 __syncthreads();
-                stage_rows<T, D, TILE, LDQ>(sK, gK + hoff, kv * TILE, s, tid);
+                load_tile_async<T, D, TILE>(sK, gK + hoff, kv * TILE, s, w, lane);
             }
 
             const bool diag = CAUSAL && kv == qt;
             const bool ragged = (kv + 1) * TILE > s || (qt + 1) * TILE > s;
 
+            const int rank = DET ? p.rank[kv * n + qt] : 0;
+            const int cnt = DET ? p.count[qt] : 1;
+            unsigned* flag = p.flags + (size_t)head * n + qt;
+            unsigned early = 0;  // tid 0: the flag as read before the last sub-step
+
 #pragma unroll 1
             for (int sub = 0; sub < NSUB; ++sub) {
                 const int q0 = qt * TILE + sub * BQ;
-                // ---- stage Q and dO rows [q0, q0+BQ) in LDS
-                stage_rows<T, D, BQ, LDQ>(sQ, gQ + hoff, q0, s, tid);
-                stage_rows<T, D, BQ, LDQ>(sdO, gdO + hoff, q0, s, tid);
-                if (tid < BQ) {
-                    const int row = q0 + tid;
-                    slse[tid] = row < s ? p.lse[(size_t)head * s + row] * kLog2e : 0.f;
-                    sdelta[tid] = p.delta[(size_t)head * p.s_pad + row];
+                // ---- the Q/dO rows [q0, q0+BQ) are in buffer `buf` (prefetched
+                // during the previous sub-step, or loaded now at an item start)
+                if (!staged) issue_q(buf, q0);
+                // landed for every wave, and the previous release published
+                asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+                __syncthreads();
+                if (pend_flag) {
+                    if (tid == 0) __hip_atomic_store(pend_flag, pend_val, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                    pend_flag = nullptr;
                 }
-                if (pend_flag) publish();  // this barrier also ends the staging
-                else __syncthreads();
+                // read this task's flag early: its latency hides behind the
+                // last sub-step (and a wait usually finds it already set)
+                if (DET && sub == NSUB - 1 && rank > 0 && tid == 0)
+                    early = __hip_atomic_load(flag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                // prefetch the next sub-step's rows into the other buffer
+                staged = false;
+                if (sub + 1 < NSUB) {
+                    issue_q(buf ^ 1, q0 + BQ);
+                    staged = true;
+                } else if (t + 1 < t_end) {
+                    issue_q(buf ^ 1, p.task_q[t + 1] * TILE);
+                    staged = true;
+                }
+                const unsigned char* sQ = smem + L::OFF_Q + buf * L::QB;
+                const unsigned char* sdO = smem + L::OFF_DO + buf * L::QB;
+                const float* slse = reinterpret_cast<const float*>(smem + L::OFF_LSE) + buf * BQ;
+                const float* sdelta = reinterpret_cast<const float*>(smem + L::OFF_DEL) + buf * BQ;
+                buf ^= 1;
 
                 // ---- S = Q K^T and dP = dO V^T (rows: queries, cols: this wave's keys)
                 f32x4 S[MT][NT], dP[MT][NT];
@@ -342,12 +418,11 @@ __global__ __launch_bounds__(256, 1) void bwd_main_kernel(KParams p) {
                 for (int ks = 0; ks < KSD; ++ks) {
                     V8 bk[NT];
 #pragma unroll
-                    for (int nt = 0; nt < NT; ++nt)
-                        bk[nt] = *reinterpret_cast<const V8*>(sK + (w * RW + nt * 16 + c16) * LDQ + ks * 32 + 8 * g);
+                    for (int nt = 0; nt < NT; ++nt) bk[nt] = frag_row<T, D>(sK, w * RW + nt * 16 + c16, ks * 32 + 8 * g);
 #pragma unroll
                     for (int mt = 0; mt < MT; ++mt) {
-                        const V8 aq = *reinterpret_cast<const V8*>(sQ + (mt * 16 + c16) * LDQ + ks * 32 + 8 * g);
-                        const V8 ao = *reinterpret_cast<const V8*>(sdO + (mt * 16 + c16) * LDQ + ks * 32 + 8 * g);
+                        const V8 aq = frag_row<T, D>(sQ, mt * 16 + c16, ks * 32 + 8 * g);
+                        const V8 ao = frag_row<T, D>(sdO, mt * 16 + c16, ks * 32 + 8 * g);
 #pragma unroll
                         for (int nt = 0; nt < NT; ++nt) {
                             S[mt][nt] = E::mma(S[mt][nt], aq, bk[nt]);
@@ -362,7 +437,7 @@ __global__ __launch_bounds__(256, 1) void bwd_main_kernel(KParams p) {
 #pragma unroll
                     for (int i = 0; i < 4; ++i) {
                         const int ql = mt * 16 + 4 * g + i;
-                        const float l2 = slse[ql], dl = sdelta[ql];
+                        const float l2 = slse[ql] * kLog2e, dl = sdelta[ql];
 #pragma unroll
                         for (int nt = 0; nt < NT; ++nt) {
                             float pv = __builtin_amdgcn_exp2f(S[mt][nt][i] * p.scale_log2 - l2);
@@ -396,8 +471,8 @@ __global__ __launch_bounds__(256, 1) void bwd_main_kernel(KParams p) {
                     const int rA = ks * 32 + 4 * g, rB = ks * 32 + 16 + 4 * g;
 #pragma unroll
                     for (int dt = 0; dt < DT; ++dt) {
-                        const V8 vq = E::frag_col(sQ, LDQ, rA, rB, dt * 16, c16);
-                        const V8 vo = E::frag_col(sdO, LDQ, rA, rB, dt * 16, c16);
+                        const V8 vq = frag_col<T, D>(sQ, rA, rB, dt * 16, c16);
+                        const V8 vo = frag_col<T, D>(sdO, rA, rB, dt * 16, c16);
 #pragma unroll
                         for (int nt = 0; nt < NT; ++nt) {
                             dV[nt][dt] = E::mma(dV[nt][dt], aP[nt], vo);
@@ -426,18 +501,14 @@ __global__ __launch_bounds__(256, 1) void bwd_main_kernel(KParams p) {
             float* acc = p.dq_acc + (size_t)head * p.s_pad * D;
             const __amdgpu_buffer_rsrc_t racc = make_rsrc(acc, (unsigned)(p.s_pad * D * sizeof(float)));
             const int col0 = w * DW + 4 * g;
-            int rank = 0, cnt = 1;
             f32x4 prev[NDT][MTT];
             if (DET) {
-                rank = p.rank[kv * n + qt];
-                cnt = p.count[qt];
-                unsigned* flag = p.flags + (size_t)head * n + qt;
                 if (rank > 0) {
                     if (tid == 0) {
                         const unsigned long long t0 = p.stats ? __builtin_readcyclecounter() : 0;
                         unsigned spins = 0;
-                        while (__hip_atomic_load(flag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) !=
-                               (unsigned)rank) {
+                        unsigned seen = early;
+                        while (seen != (unsigned)rank) {
                             if ((spins & 1023u) == 0 &&
                                 __hip_atomic_load(p.abort, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT))
                                 break;
@@ -447,6 +518,7 @@ __global__ __launch_bounds__(256, 1) void bwd_main_kernel(KParams p) {
                                 atomicOr(p.status, 1u);
                                 break;
                             }
+                            seen = __hip_atomic_load(flag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
                         }
                         if (p.stats) {
                             wait_cycles += __builtin_readcyclecounter() - t0;
@@ -480,7 +552,7 @@ __global__ __launch_bounds__(256, 1) void bwd_main_kernel(KParams p) {
                     V8 a[NDT];
 #pragma unroll
                     for (int dtw = 0; dtw < NDT; ++dtw)
-                        a[dtw] = E::frag_col(sK, LDQ, ks * 32 + 8 * g, ks * 32 + 8 * g + 4, w * DW + dtw * 16, c16);
+                        a[dtw] = frag_col<T, D>(sK, ks * 32 + 8 * g, ks * 32 + 8 * g + 4, w * DW + dtw * 16, c16);
 #pragma unroll
                     for (int j = 0; j < MTH; ++j) {
                         const int mt = half * MTH + j;
