@@ -109,7 +109,7 @@ def main():
     ap.add_argument("--causal", type=int, default=None, help="override the workload's mask")
     ap.add_argument("--schedule", default=None, help="default: shift (full) / descending (causal)")
     ap.add_argument("--compare", default="naive,atomic",
-                    help="comma list of schedules also timed for context ('' for none)")
+                    help="comma list of schedules also timed for context ('none' for none)")
     ap.add_argument("--cpu-heads", type=int, default=4, help="heads in the CPU oracle sample (0: skip)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of MIB MiB five times (scales the HBM "
@@ -154,7 +154,7 @@ def main():
         f"(main kernel {res['ms_main']:.3f} ms, {main_tflops:.1f} TFLOPS)")
 
     extra = {}
-    for other in [x for x in args.compare.split(",") if x and x != schedule]:
+    for other in [x for x in args.compare.split(",") if x and x not in (schedule, "none")]:
         if other == "symmetric_shift" and causal and (wl.s // 128) % 2:
             continue
         r2 = time_calls(tsa, pb, other, max(5, args.steps // 2), 2, torch)
