@@ -155,39 +155,38 @@ struct Pad {
     __device__ static inline int off(int row, int col) { return row * RS + col * (int)sizeof(T); }
 };
 
-// Issue the loads of rows [row0, row0 + ROWS) of a [s][D] tensor into a
-// padded LDS tile, 1 KiB blocks dealt round-robin over the 4 waves.  Rows
-// past the end repeat row s-1 (finite values that the masks of ragged tiles
-// remove).  Completion: s_waitcnt vmcnt(0), then a barrier.
-template <typename T, int D, int ROWS>
-__device__ inline void load_tile_async(unsigned char* tile, const T* g, int row0, int s, int w, int lane) {
+typedef __attribute__((address_space(3))) unsigned char lds_u8;
+constexpr unsigned kOutOfRange = 0x80000000u;  // a buffer offset past any tensor
+
+// Issue the loads of rows [row0, row0 + ROWS) of one head's [s][D] tensor
+// into a padded LDS tile, 1 KiB blocks dealt round-robin over the NW waves.
+// `rsrc` covers exactly that head's s rows, so rows past the end read as
+// zero; slots that fall in a row's padding or past the tile are pointed out
+// of range (and write zeros), so the destination region must extend to a
+// whole number of 1 KiB blocks.  Completion: s_waitcnt vmcnt(0), then a
+// barrier.
+template <typename T, int D, int ROWS, int NW>
+__device__ inline void load_tile_async(lds_u8* tile, __amdgpu_buffer_rsrc_t rsrc, int row0, int w, int lane) {
     using P = Pad<T, D>;
     constexpr int TOTAL = ROWS * P::RS;
     constexpr int BLOCKS = (TOTAL + 1023) / 1024;
 #pragma unroll
-    for (int it = 0; it < (BLOCKS + 3) / 4; ++it) {
-        const int blk = w + 4 * it;
+    for (int it = 0; it < (BLOCKS + NW - 1) / NW; ++it) {
+        const int blk = w + NW * it;
         if (blk < BLOCKS) {
             const int byte = blk * 1024 + lane * 16;
             const int row = byte / P::RS, inrow = byte % P::RS;
-            if (byte < TOTAL && inrow < P::RB) {
-                const int gr = min(row0 + row, s - 1);
-                const char* src = reinterpret_cast<const char*>(g + (size_t)gr * D) + inrow;
-                __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)(src),
-                                                 (__attribute__((address_space(3))) void*)(tile + blk * 1024), 16, 0,
-                                                 0);
-            }
+            const unsigned voff = (byte < TOTAL && inrow < P::RB) ? (unsigned)((row0 + row) * P::RB + inrow)
+                                                                 : kOutOfRange;
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, tile + blk * 1024, 16, (int)voff, 0, 0, 0);
         }
     }
 }
 
-// 64 consecutive fp32 values (rows [row0, row0+n) of a per-row vector, row
-// index clamped to rmax) into LDS, by one wave.
-__device__ inline void load_vec_async(float* dst, const float* src, int row0, int n, int rmax, int lane) {
-    if (lane < n)
-        __builtin_amdgcn_global_load_lds(
-            (const __attribute__((address_space(1))) void*)(src + min(row0 + lane, rmax)),
-            (__attribute__((address_space(3))) void*)dst, 4, 0, 0);
+// n consecutive fp32 values of a per-row vector (rows [row0, row0 + n),
+// n <= 64) into LDS, by one wave; rows past the resource read as zero.
+__device__ inline void load_vec_async(lds_u8* dst, __amdgpu_buffer_rsrc_t rsrc, int row0, int n, int lane) {
+    if (lane < n) __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, dst, 4, (row0 + lane) * 4, 0, 0, 0);
 }
 
 // MFMA operand whose contraction index runs ALONG a row of a padded tile:
@@ -241,8 +240,10 @@ template <typename T, int D, int TILE>
 struct Layout {
     // query rows per sub-step (fp32 at d=128 halves it to stay within LDS)
     static constexpr int BQ = (sizeof(T) == 4 && D == 128) ? 32 : 64;
-    static constexpr int QB = BQ * Pad<T, D>::RS;    // bytes of one Q (or dO) buffer
-    static constexpr int KB = TILE * Pad<T, D>::RS;  // bytes of sK
+    // Q/dO buffers and sK are whole numbers of 1 KiB blocks: the last block
+    // of a tile load writes (zeros) up to its end
+    static constexpr int QB = (BQ * Pad<T, D>::RS + 1023) / 1024 * 1024;    // one Q (or dO) buffer
+    static constexpr int KB = (TILE * Pad<T, D>::RS + 1023) / 1024 * 1024;  // sK
     static constexpr int LDSS = TILE + Elem<T>::kPad;
     static constexpr int SB = TILE * LDSS * (int)sizeof(T);
     static constexpr int OFF_Q = 0, OFF_DO = 2 * QB, OFF_K = 4 * QB, OFF_S = OFF_K + KB;
@@ -266,6 +267,7 @@ __global__ __launch_bounds__(256, 1) void bwd_main_kernel(KParams p) {
     constexpr int LDSS = L::LDSS;
 
     extern __shared__ __align__(16) unsigned char smem[];
+    lds_u8* const lsm = (lds_u8*)smem;  // LDS address space: no per-use conversion
     unsigned char* sK = smem + L::OFF_K;
     T* sdS = reinterpret_cast<T*>(smem + L::OFF_S);
     __shared__ long long s_item;
@@ -310,13 +312,18 @@ __global__ __launch_bounds__(256, 1) void bwd_main_kernel(KParams p) {
         // `staged` says whether its rows were already requested
         int buf = 0;
         bool staged = false;
+        // buffer resources over this head's rows (rows past s read as zero)
+        const unsigned head_bytes = (unsigned)((size_t)s * D * sizeof(T));
+        const __amdgpu_buffer_rsrc_t rq = make_rsrc((void*)(gQ + hoff), head_bytes);
+        const __amdgpu_buffer_rsrc_t rdo = make_rsrc((void*)(gdO + hoff), head_bytes);
+        const __amdgpu_buffer_rsrc_t rk = make_rsrc((void*)(gK + hoff), head_bytes);
+        const __amdgpu_buffer_rsrc_t rlse = make_rsrc((void*)(p.lse + (size_t)head * s), (unsigned)(s * 4));
+        const __amdgpu_buffer_rsrc_t rdel = make_rsrc((void*)(p.delta + (size_t)head * p.s_pad), (unsigned)(p.s_pad * 4));
         auto issue_q = [&](int b, int q0) {
-            load_tile_async<T, D, BQ>(smem + L::OFF_Q + b * L::QB, gQ + hoff, q0, s, w, lane);
-            load_tile_async<T, D, BQ>(smem + L::OFF_DO + b * L::QB, gdO + hoff, q0, s, w, lane);
-            float* dl = reinterpret_cast<float*>(smem + L::OFF_LSE) + b * BQ;
-            float* dd = reinterpret_cast<float*>(smem + L::OFF_DEL) + b * BQ;
-            if (w == 0) load_vec_async(dl, p.lse + (size_t)head * s, q0, BQ, s - 1, lane);
-            if (w == 1) load_vec_async(dd, p.delta + (size_t)head * p.s_pad, q0, BQ, p.s_pad - 1, lane);
+            load_tile_async<T, D, BQ, 4>(lsm + L::OFF_Q + b * L::QB, rq, q0, w, lane);
+            load_tile_async<T, D, BQ, 4>(lsm + L::OFF_DO + b * L::QB, rdo, q0, w, lane);
+            if (w == 0) load_vec_async(lsm + L::OFF_LSE + b * BQ * 4, rlse, q0, BQ, lane);
+            if (w == 1) load_vec_async(lsm + L::OFF_DEL + b * BQ * 4, rdel, q0, BQ, lane);
         };
         f32x4 dK[NT][DT], dV[NT][DT];
         V8 Vr[NT][KSD];
@@ -362,7 +369,7 @@ __global__ __launch_bounds__(256, 1) void bwd_main_kernel(KParams p) {
                 // the whole K tile in LDS (B operand of S, A operand of dQ^T),
                 // once every wave is done with the previous tile's
                 __syncthreads();
-                load_tile_async<T, D, TILE>(sK, gK + hoff, kv * TILE, s, w, lane);
+                load_tile_async<T, D, TILE, 4>(lsm + L::OFF_K, rk, kv * TILE, w, lane);
             }
 
             const bool diag = CAUSAL && kv == qt;
