@@ -253,15 +253,28 @@ struct Layout {
     static_assert(TILE % BQ == 0 && BQ % 32 == 0, "sub-step shape");
 };
 
+// Wave count of a work group: 8 (two per SIMD) for bf16 at d = 128, so that
+// each wave's share of the KV tile (16 rows: dK/dV accumulators, V operands,
+// S/dP of a sub-step, a 16-column dQ slice) fits in 256 registers and two
+// waves per SIMD can overlap each other's LDS, VALU and MFMA work; 4 for the
+// smaller shapes (the dQ slice of a wave is D/NW >= 16 columns).
+template <typename T, int D>
+struct Waves {
+    static constexpr int NW = (sizeof(T) == 2 && D == 128) ? 8 : 4;
+    static constexpr int NTHREADS = 64 * NW;
+};
+
 template <typename T, int D, int TILE, bool CAUSAL, bool DET>
-__global__ __launch_bounds__(256, 1) void bwd_main_kernel(KParams p) {
+__global__ __launch_bounds__((Waves<T, D>::NTHREADS), 1) void bwd_main_kernel(KParams p) {
     using E = Elem<T>;
     using V8 = typename E::vec8;
     using V4 = typename E::vec4;
     using L = Layout<T, D, TILE>;
+    constexpr int NW = Waves<T, D>::NW;
     constexpr int BQ = L::BQ, NSUB = TILE / BQ;
-    constexpr int RW = TILE / 4, NT = RW / 16;   // KV rows per wave, 16-row tiles
-    constexpr int DW = D / 4, NDT = DW / 16;     // dQ columns per wave
+    constexpr int RW = TILE / NW, NT = RW / 16;  // KV rows per wave, 16-row tiles
+    constexpr int DW = D / NW, NDT = DW / 16;    // dQ columns per wave
+    static_assert(RW % 16 == 0 && DW % 16 == 0, "wave shares must be whole 16-wide MFMA tiles");
     constexpr int KSD = D / 32, KSQ = BQ / 32, KSKV = TILE / 32;
     constexpr int MT = BQ / 16, DT = D / 16, MTT = TILE / 16;
     constexpr int LDSS = L::LDSS;
@@ -320,8 +333,8 @@ __global__ __launch_bounds__(256, 1) void bwd_main_kernel(KParams p) {
         const __amdgpu_buffer_rsrc_t rlse = make_rsrc((void*)(p.lse + (size_t)head * s), (unsigned)(s * 4));
         const __amdgpu_buffer_rsrc_t rdel = make_rsrc((void*)(p.delta + (size_t)head * p.s_pad), (unsigned)(p.s_pad * 4));
         auto issue_q = [&](int b, int q0) {
-            load_tile_async<T, D, BQ, 4>(lsm + L::OFF_Q + b * L::QB, rq, q0, w, lane);
-            load_tile_async<T, D, BQ, 4>(lsm + L::OFF_DO + b * L::QB, rdo, q0, w, lane);
+            load_tile_async<T, D, BQ, NW>(lsm + L::OFF_Q + b * L::QB, rq, q0, w, lane);
+            load_tile_async<T, D, BQ, NW>(lsm + L::OFF_DO + b * L::QB, rdo, q0, w, lane);
             if (w == 0) load_vec_async(lsm + L::OFF_LSE + b * BQ * 4, rlse, q0, BQ, lane);
             if (w == 1) load_vec_async(lsm + L::OFF_DEL + b * BQ * 4, rdel, q0, BQ, lane);
         };
@@ -369,7 +382,7 @@ __global__ __launch_bounds__(256, 1) void bwd_main_kernel(KParams p) {
                 // the whole K tile in LDS (B operand of S, A operand of dQ^T),
                 // once every wave is done with the previous tile's
                 __syncthreads();
-                load_tile_async<T, D, TILE, 4>(lsm + L::OFF_K, rk, kv * TILE, w, lane);
+                load_tile_async<T, D, TILE, NW>(lsm + L::OFF_K, rk, kv * TILE, w, lane);
             }
 
             const bool diag = CAUSAL && kv == qt;
@@ -691,7 +704,8 @@ static int launch_main_t(const KParams& kp, const BwdLaunch& L) {
         attr_set = true;
     }
     int per_cu = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, (const void*)kern, 256, smem) != hipSuccess ||
+    constexpr int nthreads = Waves<T, D>::NTHREADS;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, (const void*)kern, nthreads, smem) != hipSuccess ||
         per_cu < 1)
         return fail(ATTN_ERR_HIP, "occupancy query failed for the main kernel");
     const long long resident = (long long)per_cu * L.num_cus;
@@ -700,7 +714,7 @@ static int launch_main_t(const KParams& kp, const BwdLaunch& L) {
                     "schedule needs more simultaneously resident work groups than the device holds");
     const long long grid = std::min<long long>(resident, kp.total_items);
     if (grid <= 0) return ATTN_OK;
-    hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(256), smem, (hipStream_t)L.stream, kp);
+    hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(nthreads), smem, (hipStream_t)L.stream, kp);
     if (hipGetLastError() != hipSuccess) return fail(ATTN_ERR_HIP, "main kernel launch failed");
     return ATTN_OK;
 }
