@@ -227,3 +227,22 @@ def test_gradient_identities_full_size():
     scale_dk = dk.float().abs().sum(dim=2).max()
     assert float(sdk.abs().max()) <= 2e-2 * float(scale_dk)
     assert float((sdv - sdo).abs().max()) <= 2e-2 * float(dv.float().abs().sum(dim=2).max())
+
+
+def test_items_longer_than_one_record_block():
+    """An item with more tasks than the kernel keeps in LDS at once (257 Q
+    tiles of 64 rows, fp32, ragged tail): the records are reloaded mid-item.
+    Shift at this size needs 257 resident work groups; the launcher either
+    runs it or refuses with ATTN_ERR_COSCHEDULE, never hangs."""
+    s = 257 * 64 - 40
+    pb = Problem(1, 1, s, 64, "fp32", 4242, False)
+    _say(f"long item fp32 s={s} naive")
+    g = pb.run("naive")
+    torch.cuda.synchronize()
+    _check_parity(pb, g, [0], f"long item s={s} naive")
+    try:
+        g2 = pb.run("shift")
+        torch.cuda.synchronize()
+        _check_parity(pb, g2, [0], f"long item s={s} shift")
+    except tsa.AttnError as e:
+        assert e.code == -3, e

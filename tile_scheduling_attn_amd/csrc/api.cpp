@@ -55,7 +55,9 @@ static bool ws_layout(long long H, long long s, int d, WsLayout& w) {
 }
 
 struct DevSchedule {
-    int* buf = nullptr;  // item_begin | task_kv | task_q | rank | count
+    // item_begin (items+1 ints, padded to a multiple of 4) | one 16-byte
+    // record per task: {kv tile, q tile, rank, contributors of the q tile}
+    int* buf = nullptr;
     int items = 0, tasks = 0, n = 0, min_workers = 1;
 };
 
@@ -109,12 +111,15 @@ static int get_schedule(DevState& ds, int n, bool causal, int schedule, DevSched
     if (rc == ATTN_ERR_UNSUPPORTED)
         return fail(rc, "symmetric shift under the causal mask needs an even number of tiles");
     if (rc != ATTN_OK) return fail(rc, "invalid schedule");
-    std::vector<int> host;
-    host.insert(host.end(), sc.item_begin.begin(), sc.item_begin.end());
-    host.insert(host.end(), sc.task_kv.begin(), sc.task_kv.end());
-    host.insert(host.end(), sc.task_q.begin(), sc.task_q.end());
-    host.insert(host.end(), sc.rank.begin(), sc.rank.end());
-    host.insert(host.end(), sc.count.begin(), sc.count.end());
+    std::vector<int> host(sc.item_begin.begin(), sc.item_begin.end());
+    host.resize((host.size() + 3) / 4 * 4, 0);
+    for (size_t t = 0; t < sc.task_kv.size(); ++t) {
+        const int kv = sc.task_kv[t], q = sc.task_q[t];
+        host.push_back(kv);
+        host.push_back(q);
+        host.push_back(sc.rank[(size_t)kv * n + q]);
+        host.push_back(sc.count[q]);
+    }
     DevSchedule d;
     hipError_t e = hipMalloc(&d.buf, host.size() * sizeof(int));
     if (e != hipSuccess) return fail_hip(e, "hipMalloc(schedule)");
@@ -226,10 +231,7 @@ static int backward(const void* q, const void* k, const void* v, const void* o, 
     L.status = ds.status;
     L.stats = g_wait_stats ? reinterpret_cast<unsigned long long*>(a.counters + 2) : nullptr;
     L.item_begin = sch->buf;
-    L.task_kv = L.item_begin + sch->items + 1;
-    L.task_q = L.task_kv + sch->tasks;
-    L.rank = L.task_q + sch->tasks;
-    L.count = L.rank + (size_t)n * n;
+    L.tasks = L.item_begin + (sch->items + 1 + 3) / 4 * 4;
     L.items_per_head = sch->items;
     // flags and counters are contiguous: one clear covers both
     L.nclear32 = (int)((wl.total - wl.flags) / sizeof(unsigned));

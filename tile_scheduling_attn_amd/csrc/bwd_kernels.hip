@@ -57,6 +57,7 @@ typedef bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x8 __attribute__((ext_vector_type(8)));
+typedef int i32x4 __attribute__((ext_vector_type(4)));
 
 constexpr float kLog2e = 1.4426950408889634f;
 // A flag wait gives up after this many polls (each poll sleeps ~64 cycles
@@ -110,10 +111,7 @@ struct KParams {
     unsigned* status;   // device status word, reported by attn_bwd_query_status
     unsigned long long* stats;  // null unless wait statistics are on
     const int* item_begin;
-    const int* task_kv;
-    const int* task_q;
-    const int* rank;
-    const int* count;
+    const i32x4* tasks;  // {kv tile, q tile, rank, contributors} per task
     int H, s, n, items_per_head, s_pad;
     long long total_items;
     float scale, scale_log2;
@@ -248,7 +246,9 @@ struct Layout {
     static constexpr int SB = TILE * LDSS * (int)sizeof(T);
     static constexpr int OFF_Q = 0, OFF_DO = 2 * QB, OFF_K = 4 * QB, OFF_S = OFF_K + KB;
     static constexpr int OFF_LSE = OFF_S + SB, OFF_DEL = OFF_LSE + 2 * BQ * 4;
-    static constexpr size_t bytes = OFF_DEL + 2 * BQ * 4;
+    static constexpr int MAXT = 256;  // task records of an item held in LDS at a time
+    static constexpr int OFF_TASK = OFF_DEL + 2 * BQ * 4;
+    static constexpr size_t bytes = OFF_TASK + MAXT * 16;
     static_assert(bytes <= 160 * 1024 - 64, "LDS budget of a gfx950 work group exceeded");
     static_assert(TILE % BQ == 0 && BQ % 32 == 0, "sub-step shape");
 };
@@ -307,7 +307,19 @@ __global__ __launch_bounds__((Waves<T, D>::NTHREADS), 1) void bwd_main_kernel(KP
         const int head = (int)(item / p.items_per_head);
         const int pat = (int)(item % p.items_per_head);
         const size_t hoff = (size_t)head * s * D;
-        const int t_end = p.item_begin[pat + 1];
+        const int t_beg = p.item_begin[pat], t_end = p.item_begin[pat + 1];
+        // the item's task records, MAXT at a time, in LDS: one broadcast LDS
+        // read per task instead of dependent scalar loads
+        i32x4* stask = reinterpret_cast<i32x4*>(smem + L::OFF_TASK);
+        auto load_tasks = [&](int t0) {
+            __syncthreads();  // readers of the previous records are done
+            for (int i = tid; i < L::MAXT && t0 + i < t_end; i += Waves<T, D>::NTHREADS) stask[i] = p.tasks[t0 + i];
+            __syncthreads();
+        };
+        auto task_q_of = [&](int t) {  // q tile of task t (t in the current or next record block)
+            return (t - t_beg) % L::MAXT != 0 ? __builtin_amdgcn_readfirstlane(stask[(t - t_beg) % L::MAXT][1])
+                                               : p.tasks[t][1];
+        };
 
         int cur_kv = -1;
         // release of the last accumulator update, not yet published: every
@@ -357,8 +369,10 @@ __global__ __launch_bounds__((Waves<T, D>::NTHREADS), 1) void bwd_main_kernel(KP
                     }
         };
 
-        for (int t = p.item_begin[pat]; t < t_end; ++t) {
-            const int kv = p.task_kv[t], qt = p.task_q[t];
+        for (int t = t_beg; t < t_end; ++t) {
+            if ((t - t_beg) % L::MAXT == 0) load_tasks(t);
+            const i32x4 rec = stask[(t - t_beg) % L::MAXT];
+            const int kv = __builtin_amdgcn_readfirstlane(rec[0]), qt = __builtin_amdgcn_readfirstlane(rec[1]);
             if (kv != cur_kv) {
                 if (cur_kv >= 0) store_dkdv(cur_kv);
                 cur_kv = kv;
@@ -388,8 +402,8 @@ __global__ __launch_bounds__((Waves<T, D>::NTHREADS), 1) void bwd_main_kernel(KP
             const bool diag = CAUSAL && kv == qt;
             const bool ragged = (kv + 1) * TILE > s || (qt + 1) * TILE > s;
 
-            const int rank = DET ? p.rank[kv * n + qt] : 0;
-            const int cnt = DET ? p.count[qt] : 1;
+            const int rank = DET ? __builtin_amdgcn_readfirstlane(rec[2]) : 0;
+            const int cnt = DET ? __builtin_amdgcn_readfirstlane(rec[3]) : 1;
             unsigned* flag = p.flags + (size_t)head * n + qt;
             unsigned early = 0;  // tid 0: the flag as read before the last sub-step
 
@@ -416,7 +430,7 @@ __global__ __launch_bounds__((Waves<T, D>::NTHREADS), 1) void bwd_main_kernel(KP
                     issue_q(buf ^ 1, q0 + BQ);
                     staged = true;
                 } else if (t + 1 < t_end) {
-                    issue_q(buf ^ 1, p.task_q[t + 1] * TILE);
+                    issue_q(buf ^ 1, task_q_of(t + 1) * TILE);
                     staged = true;
                 }
                 const unsigned char* sQ = smem + L::OFF_Q + buf * L::QB;
@@ -781,10 +795,7 @@ int launch_backward(const BwdArgs& a, const BwdLaunch& L) {
     kp.status = L.status;
     kp.stats = L.stats;
     kp.item_begin = L.item_begin;
-    kp.task_kv = L.task_kv;
-    kp.task_q = L.task_q;
-    kp.rank = L.rank;
-    kp.count = L.count;
+    kp.tasks = reinterpret_cast<const i32x4*>(L.tasks);
     kp.H = a.H;
     kp.s = a.s;
     kp.n = a.n;
