@@ -594,7 +594,12 @@ __global__ __launch_bounds__((Waves<T, D>::NTHREADS), 1) void bwd_main_kernel(KP
                         const int mt = half * MTH + j;
                         const V8 b = *reinterpret_cast<const V8*>(sdS + (mt * 16 + c16) * LDSS + ks * 32 + 8 * g);
 #pragma unroll
-                        for (int dtw = 0; dtw < NDT; ++dtw) dQt[dtw][j] = E::mma(dQt[dtw][j], a[dtw], b);
+                        for (int dtw = 0; dtw < NDT; ++dtw)
+                            // deterministic: dQ^T tiles (lane: 4 consecutive d of one
+                            // query row, 16-byte accumulator accesses); atomic: dQ
+                            // tiles (16 lanes: 16 consecutive d of one query row, so
+                            // each atomic instruction covers 64 contiguous bytes per row)
+                            dQt[dtw][j] = DET ? E::mma(dQt[dtw][j], a[dtw], b) : E::mma(dQt[dtw][j], b, a[dtw]);
                     }
                 }
                 if (DET) {
@@ -631,11 +636,12 @@ __global__ __launch_bounds__((Waves<T, D>::NTHREADS), 1) void bwd_main_kernel(KP
 #pragma unroll
                     for (int dtw = 0; dtw < NDT; ++dtw)
 #pragma unroll
-                        for (int j = 0; j < MTH; ++j) {
-                            float* ptr = acc + (size_t)(qt * TILE + (half * MTH + j) * 16 + c16) * D + col0 + dtw * 16;
+                        for (int j = 0; j < MTH; ++j)
 #pragma unroll
-                            for (int e = 0; e < 4; ++e) unsafeAtomicAdd(ptr + e, dQt[dtw][j][e]);
-                        }
+                            for (int i = 0; i < 4; ++i)
+                                unsafeAtomicAdd(acc + (size_t)(qt * TILE + (half * MTH + j) * 16 + 4 * g + i) * D +
+                                                    w * DW + dtw * 16 + c16,
+                                                dQt[dtw][j][i]);
                 }
             }
             if (DET && rank != cnt - 1) {
