@@ -526,7 +526,10 @@ __global__ __launch_bounds__((Waves<T, D>::NTHREADS), 1) void bwd_main_kernel(KP
                         for (int i = 0; i < 4; ++i)
                             sdS[(sub * BQ + mt * 16 + 4 * g + i) * LDSS + w * RW + nt * 16 + c16] =
                                 E::from_f(dP[mt][nt][i]);
-                __syncthreads();
+                // No barrier here: the next sub-step's first barrier orders
+                // these reads of the Q/dO buffer before its refill, and the
+                // dS rows are read only after the barrier that ends the task's
+                // last sub-step (below).
             }
 
             // ---- R phase, first half: wait for this tile's turn and start the
@@ -538,37 +541,40 @@ __global__ __launch_bounds__((Waves<T, D>::NTHREADS), 1) void bwd_main_kernel(KP
             const __amdgpu_buffer_rsrc_t racc = make_rsrc(acc, (unsigned)(p.s_pad * D * sizeof(float)));
             const int col0 = w * DW + 4 * g;
             f32x4 prev[NDT][MTT];
-            if (DET) {
-                if (rank > 0) {
-                    if (tid == 0) {
-                        const unsigned long long t0 = p.stats ? __builtin_readcyclecounter() : 0;
-                        unsigned spins = 0;
-                        unsigned seen = early;
-                        while (seen != (unsigned)rank) {
-                            if ((spins & 1023u) == 0 &&
-                                __hip_atomic_load(p.abort, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT))
-                                break;
-                            __builtin_amdgcn_s_sleep(1);
-                            if (++spins >= kSpinLimit) {
-                                atomicOr(p.abort, 1u);
-                                atomicOr(p.status, 1u);
-                                break;
-                            }
-                            seen = __hip_atomic_load(flag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            // One barrier ends the last sub-step (all of dS is in LDS) and, for
+            // rank > 0, the wait for this tile's turn: thread 0 waits for the
+            // flag before arriving.
+            if (DET && rank > 0) {
+                if (tid == 0) {
+                    const unsigned long long t0 = p.stats ? __builtin_readcyclecounter() : 0;
+                    unsigned spins = 0;
+                    unsigned seen = early;
+                    while (seen != (unsigned)rank) {
+                        if ((spins & 1023u) == 0 &&
+                            __hip_atomic_load(p.abort, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT))
+                            break;
+                        __builtin_amdgcn_s_sleep(1);
+                        if (++spins >= kSpinLimit) {
+                            atomicOr(p.abort, 1u);
+                            atomicOr(p.status, 1u);
+                            break;
                         }
-                        if (p.stats) {
-                            wait_cycles += __builtin_readcyclecounter() - t0;
-                            polls += spins + 1;
-                        }
+                        seen = __hip_atomic_load(flag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
                     }
-                    __syncthreads();
-#pragma unroll
-                    for (int dtw = 0; dtw < NDT; ++dtw)
-#pragma unroll
-                        for (int mt = 0; mt < MTT; ++mt)
-                            prev[dtw][mt] = load_sc1(
-                                racc, (unsigned)(((qt * TILE + mt * 16 + c16) * D + col0 + dtw * 16) * 4));
+                    if (p.stats) {
+                        wait_cycles += __builtin_readcyclecounter() - t0;
+                        polls += spins + 1;
+                    }
                 }
+            }
+            __syncthreads();
+            if (DET && rank > 0) {
+#pragma unroll
+                for (int dtw = 0; dtw < NDT; ++dtw)
+#pragma unroll
+                    for (int mt = 0; mt < MTT; ++mt)
+                        prev[dtw][mt] =
+                            load_sc1(racc, (unsigned)(((qt * TILE + mt * 16 + c16) * D + col0 + dtw * 16) * 4));
             }
 
             // ---- dQ^T[d][q] = K^T[d][key] dS^T[key][q] over the tile, for this
