@@ -47,6 +47,8 @@
 // all resident before any of them waits (see attn_sched_min_workers).
 #include <hip/hip_runtime.h>
 
+#include <type_traits>
+
 #include "attn_bwd.h"
 #include "internal.h"
 
@@ -158,6 +160,46 @@ struct Pad {
 typedef __attribute__((address_space(3))) unsigned char lds_u8;
 constexpr unsigned kOutOfRange = 0x80000000u;  // a buffer offset past any tensor
 
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+
+// The words of a raw buffer resource over [base, base + bytes) (the same
+// descriptor as make_rsrc), for the copy instructions below.
+__device__ inline u32x4 rsrc_words(const void* base, unsigned bytes) {
+    const unsigned long long a = (unsigned long long)base;
+    return u32x4{(unsigned)a, (unsigned)(a >> 32) & 0xffffu, bytes, 0x00020000u};
+}
+
+// Global-to-LDS copies (buffer_load_dword[x4] ... lds): the element at byte
+// offset voff of the resource lands at LDS address m0 + 4 * lane (dword) or
+// m0 + 16 * lane (dwordx4).  They are written as inline assembly so that the
+// compiler does not know an LDS copy is in flight: otherwise it makes every
+// transposing LDS read (which it cannot tell apart from the copy's
+// destination) wait for all outstanding vector-memory operations, which
+// would stall each sub-step until the prefetch of the next one had landed.
+// Readers of a copied tile are ordered after it by an explicit
+// s_waitcnt vmcnt(0) and a barrier.  A write of m0 needs one wait state
+// before the copy reads it.
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+__device__ inline void copy16_to_lds(u32x4 rsrc, unsigned voff, unsigned lds) {
+    asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds"
+                 :
+                 : "v"(voff), "s"(rsrc), "s"(__builtin_amdgcn_readfirstlane(lds))
+                 : "memory", "m0");
+}
+__device__ inline void copy4_to_lds(u32x4 rsrc, unsigned voff, unsigned lds) {
+    asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tbuffer_load_dword %0, %1, 0 offen lds"
+                 :
+                 : "v"(voff), "s"(rsrc), "s"(__builtin_amdgcn_readfirstlane(lds))
+                 : "memory", "m0");
+}
+#pragma clang diagnostic pop
+
+// LDS byte address of a pointer into the work group's LDS.
+__device__ inline unsigned lds_addr(const void* p) {
+    return (unsigned)(size_t)(const lds_u8*)p;
+}
+
 // Issue the loads of rows [row0, row0 + ROWS) of one head's [s][D] tensor
 // into a padded LDS tile, 1 KiB blocks dealt round-robin over the NW waves.
 // `rsrc` covers exactly that head's s rows, so rows past the end read as
@@ -166,7 +208,7 @@ constexpr unsigned kOutOfRange = 0x80000000u;  // a buffer offset past any tenso
 // whole number of 1 KiB blocks.  Completion: s_waitcnt vmcnt(0), then a
 // barrier.
 template <typename T, int D, int ROWS, int NW>
-__device__ inline void load_tile_async(lds_u8* tile, __amdgpu_buffer_rsrc_t rsrc, int row0, int w, int lane) {
+__device__ inline void load_tile_async(unsigned tile, u32x4 rsrc, int row0, int w, int lane) {
     using P = Pad<T, D>;
     constexpr int TOTAL = ROWS * P::RS;
     constexpr int BLOCKS = (TOTAL + 1023) / 1024;
@@ -178,15 +220,30 @@ __device__ inline void load_tile_async(lds_u8* tile, __amdgpu_buffer_rsrc_t rsrc
             const int row = byte / P::RS, inrow = byte % P::RS;
             const unsigned voff = (byte < TOTAL && inrow < P::RB) ? (unsigned)((row0 + row) * P::RB + inrow)
                                                                  : kOutOfRange;
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, tile + blk * 1024, 16, (int)voff, 0, 0, 0);
+            copy16_to_lds(rsrc, voff, tile + blk * 1024);
         }
     }
 }
 
+// Block `it` of this wave in load_tile_async, without a branch: a block
+// index past the tile is sent to `sink` (1 KiB of LDS that nobody reads)
+// with every lane out of range.
+template <typename T, int D, int ROWS, int NW>
+__device__ inline void load_tile_block(unsigned tile, unsigned sink, u32x4 rsrc, int row0, int w, int lane, int it) {
+    using P = Pad<T, D>;
+    constexpr int TOTAL = ROWS * P::RS;
+    constexpr int BLOCKS = (TOTAL + 1023) / 1024;
+    const int blk = w + NW * it;
+    const int byte = blk * 1024 + lane * 16;
+    const int row = byte / P::RS, inrow = byte % P::RS;
+    const unsigned voff = (byte < TOTAL && inrow < P::RB) ? (unsigned)((row0 + row) * P::RB + inrow) : kOutOfRange;
+    copy16_to_lds(rsrc, voff, blk < BLOCKS ? tile + blk * 1024 : sink);
+}
+
 // n consecutive fp32 values of a per-row vector (rows [row0, row0 + n),
 // n <= 64) into LDS, by one wave; rows past the resource read as zero.
-__device__ inline void load_vec_async(lds_u8* dst, __amdgpu_buffer_rsrc_t rsrc, int row0, int n, int lane) {
-    if (lane < n) __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, dst, 4, (row0 + lane) * 4, 0, 0, 0);
+__device__ inline void load_vec_async(unsigned dst, u32x4 rsrc, int row0, int n, int lane) {
+    if (lane < n) copy4_to_lds(rsrc, (unsigned)((row0 + lane) * 4), dst);
 }
 
 // MFMA operand whose contraction index runs ALONG a row of a padded tile:
@@ -231,11 +288,32 @@ __device__ inline typename Elem<T>::vec8 frag_col(const unsigned char* tile, int
     return r;
 }
 
+// Compile-time loop: f(std::integral_constant<int, I>) for I in [B, E).
+template <int B, int E, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+    if constexpr (B < E) {
+        f(std::integral_constant<int, B>{});
+        static_for<B + 1, E>(f);
+    }
+}
+
+// The bf16 column operand of frag_col, as two ds_read_b64_tr_b16 at
+// compile-time byte offsets OLO and OHI from a per-lane pointer (row
+// rowX + lane/4, column col + 4*(lane%4) of the 16-lane group).
+template <int OLO, int OHI>
+__device__ inline bf16x8 tr_frag(const lds_u8* p) {
+    const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p + OLO));
+    const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p + OHI));
+    return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+}
+
 // LDS of one work group:
 //   sQ[2], sdO[2]  padded [BQ][D]   query rows of a sub-step (double buffer)
-//   sK             padded [TILE][D] keys of the current KV tile
+//   sK             padded [TILE][D] keys of the current KV tile (dQ operand)
 //   sdS            [TILE][TILE] (+pad) dS of the current task as [query][key]
 //   slse[2], sdelta[2] [BQ]
+//   the current item's task records, MAXT at a time (plus the next one)
+//   a 1 KiB sink for copy slots with nothing to copy
 template <typename T, int D, int TILE>
 struct Layout {
     // query rows per sub-step (fp32 at d=128 halves it to stay within LDS)
@@ -250,29 +328,28 @@ struct Layout {
     static constexpr int OFF_LSE = OFF_S + SB, OFF_DEL = OFF_LSE + 2 * BQ * 4;
     static constexpr int MAXT = 256;  // task records of an item held in LDS at a time
     static constexpr int OFF_TASK = OFF_DEL + 2 * BQ * 4;
-    static constexpr size_t bytes = OFF_TASK + MAXT * 16;
+    // 1 KiB that copy slots with nothing to copy write (nobody reads it)
+    static constexpr int OFF_SINK = OFF_TASK + (MAXT + 1) * 16;
+    static constexpr size_t bytes = OFF_SINK + 1024;
     static_assert(bytes <= 160 * 1024 - 64, "LDS budget of a gfx950 work group exceeded");
     static_assert(TILE % BQ == 0 && BQ % 32 == 0, "sub-step shape");
 };
 
-// Wave count of a work group: 8 (two per SIMD) for bf16 at d = 128, so that
-// each wave's share of the KV tile (16 rows: dK/dV accumulators, V operands,
-// S/dP of a sub-step, a 16-column dQ slice) fits in 256 registers and two
-// waves per SIMD can overlap each other's LDS, VALU and MFMA work; 4 for the
-// smaller shapes (the dQ slice of a wave is D/NW >= 16 columns).
-template <typename T, int D>
-struct Waves {
-    static constexpr int NW = (sizeof(T) == 2 && D == 128) ? 8 : 4;
-    static constexpr int NTHREADS = 64 * NW;
-};
+// Four waves per work group and one work group per CU (the LDS above allows
+// no second), so each wave has a SIMD to itself and the SIMD's whole register
+// file (512 per lane, VGPRs and AGPRs).  A wave owns TILE/4 KV rows: 32 for
+// bf16, so every Q/dO operand fetched from LDS feeds two MFMAs, and the
+// registers left over hold several operand fetches in flight.
+constexpr int kWaves = 4, kThreads = 64 * kWaves;
 
 template <typename T, int D, int TILE, bool CAUSAL, bool DET>
-__global__ __launch_bounds__((Waves<T, D>::NTHREADS), 1) void bwd_main_kernel(KParams p) {
+__global__ __launch_bounds__(kThreads, 1) __attribute__((amdgpu_waves_per_eu(1, 1)))
+void bwd_main_kernel(KParams p) {
     using E = Elem<T>;
     using V8 = typename E::vec8;
     using V4 = typename E::vec4;
     using L = Layout<T, D, TILE>;
-    constexpr int NW = Waves<T, D>::NW;
+    constexpr int NW = kWaves;
     constexpr int BQ = L::BQ, NSUB = TILE / BQ;
     constexpr int RW = TILE / NW, NT = RW / 16;  // KV rows per wave, 16-row tiles
     constexpr int DW = D / NW, NDT = DW / 16;    // dQ columns per wave
@@ -283,21 +360,81 @@ __global__ __launch_bounds__((Waves<T, D>::NTHREADS), 1) void bwd_main_kernel(KP
 
     extern __shared__ __align__(16) unsigned char smem[];
     lds_u8* const lsm = (lds_u8*)smem;  // LDS address space: no per-use conversion
+    const unsigned lds_base = lds_addr(smem);
     unsigned char* sK = smem + L::OFF_K;
     T* sdS = reinterpret_cast<T*>(smem + L::OFF_S);
     __shared__ long long s_item;
 
-    const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, g = lane >> 4, c16 = lane & 15;
-    const T* gQ = static_cast<const T*>(p.q);
+    const int tid = threadIdx.x, lane = tid & 63, g = lane >> 4, c16 = lane & 15;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave index, in an SGPR
     const T* gK = static_cast<const T*>(p.k);
     const T* gV = static_cast<const T*>(p.v);
-    const T* gdO = static_cast<const T*>(p.dO);
     T* gdQ = static_cast<T*>(p.dq);
     T* gdK = static_cast<T*>(p.dk);
     T* gdV = static_cast<T*>(p.dv);
     const int s = p.s, n = p.n;
 
     unsigned long long wait_cycles = 0, polls = 0, item_cycles = 0;
+
+    // dQ^T (deterministic) or dQ (atomic) of query rows [r0, r0 + BQ) of
+    // the task's tile, for this wave's DW columns, contracted over the whole
+    // KV tile: A = K^T from sK (transposed reads), B = dS rows from sdS.
+    // Deterministic: C[d][q], a lane holds 4 consecutive d of one query row
+    // (16-byte accumulator accesses).  Atomic: C[q][d], 16 lanes hold 16
+    // consecutive d of one row (64 contiguous bytes per atomic instruction).
+    // hook(std::integral_constant<int, ks>) runs at the start of each 32-key
+    // step, so that a caller can spread other instructions over the steps.
+    auto dq_rows = [&](f32x4 (&acc)[NDT][MT], int r0, auto&& hook) {
+#pragma unroll
+        for (int dtw = 0; dtw < NDT; ++dtw)
+#pragma unroll
+            for (int mt = 0; mt < MT; ++mt) acc[dtw][mt] = zero_vec<f32x4>();
+        auto step = [&](int ks, const V8 (&a)[NDT]) {
+            V8 b[MT];
+#pragma unroll
+            for (int mt = 0; mt < MT; ++mt)
+                b[mt] = *reinterpret_cast<const V8*>(sdS + (r0 + mt * 16 + c16) * LDSS + ks * 32 + 8 * g);
+#pragma unroll
+            for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+                for (int dtw = 0; dtw < NDT; ++dtw)
+                    acc[dtw][mt] = DET ? E::mma(acc[dtw][mt], a[dtw], b[mt]) : E::mma(acc[dtw][mt], b[mt], a[dtw]);
+        };
+        if constexpr (sizeof(T) == 2) {
+            // K^T operands one 32-key step ahead of the MFMAs that use them
+            using P = Pad<T, D>;
+            const lds_u8* tk = lsm + L::OFF_K + (8 * g + (c16 >> 2)) * P::RS + (w * DW + 4 * (c16 & 3)) * 2;
+            auto fetch = [&](auto ksc, V8 (&a)[NDT]) {
+                constexpr int ks = decltype(ksc)::value;
+                static_for<0, NDT>([&](auto jc) {
+                    constexpr int o = ks * 32 * P::RS + decltype(jc)::value * 32;
+                    a[decltype(jc)::value] = tr_frag<o, o + 4 * P::RS>(tk);
+                });
+            };
+            V8 cur[NDT], nxt[NDT];
+            fetch(std::integral_constant<int, 0>{}, cur);
+            static_for<0, KSKV>([&](auto ksc) {
+                constexpr int ks = decltype(ksc)::value;
+                if constexpr (ks + 1 < KSKV) fetch(std::integral_constant<int, ks + 1>{}, nxt);
+                hook(ksc);
+                step(ks, cur);
+                if constexpr (ks + 1 < KSKV) {
+#pragma unroll
+                    for (int j = 0; j < NDT; ++j) cur[j] = nxt[j];
+                }
+            });
+        } else {
+            static_for<0, KSKV>([&](auto ksc) {
+                constexpr int ks = decltype(ksc)::value;
+                V8 a[NDT];
+#pragma unroll
+                for (int dtw = 0; dtw < NDT; ++dtw)
+                    a[dtw] = frag_col<T, D>(sK, ks * 32 + 8 * g, ks * 32 + 8 * g + 4, w * DW + dtw * 16, c16);
+                hook(ksc);
+                step(ks, a);
+            });
+        }
+    };
 
     for (;;) {
         if (tid == 0) s_item = (long long)atomicAdd(p.ticket, 1u);
@@ -310,20 +447,19 @@ __global__ __launch_bounds__((Waves<T, D>::NTHREADS), 1) void bwd_main_kernel(KP
         const int pat = (int)(item % p.items_per_head);
         const size_t hoff = (size_t)head * s * D;
         const int t_beg = p.item_begin[pat], t_end = p.item_begin[pat + 1];
-        // the item's task records, MAXT at a time, in LDS: one broadcast LDS
-        // read per task instead of dependent scalar loads
+        // the item's task records, MAXT at a time plus the one after them, in
+        // LDS: one broadcast LDS read per task instead of dependent scalar
+        // loads, and the next task's Q tile (for the prefetch) always at hand
         i32x4* stask = reinterpret_cast<i32x4*>(smem + L::OFF_TASK);
         auto load_tasks = [&](int t0) {
             __syncthreads();  // readers of the previous records are done
-            for (int i = tid; i < L::MAXT && t0 + i < t_end; i += Waves<T, D>::NTHREADS) stask[i] = p.tasks[t0 + i];
+            for (int i = tid; i <= L::MAXT && t0 + i < t_end; i += kThreads) stask[i] = p.tasks[t0 + i];
             __syncthreads();
         };
-        auto task_q_of = [&](int t) {  // q tile of task t (t in the current or next record block)
-            return (t - t_beg) % L::MAXT != 0 ? __builtin_amdgcn_readfirstlane(stask[(t - t_beg) % L::MAXT][1])
-                                               : p.tasks[t][1];
+        auto next_q_of = [&](int t) {  // q tile of task t + 1 (< t_end)
+            return __builtin_amdgcn_readfirstlane(stask[(t - t_beg) % L::MAXT + 1][1]);
         };
 
-        int cur_kv = -1;
         // release of the last accumulator update, not yet published: every
         // wave waits for its sc1 stores to be acknowledged (device-wide
         // visible), then after a barrier one thread moves the flag on
@@ -341,19 +477,48 @@ __global__ __launch_bounds__((Waves<T, D>::NTHREADS), 1) void bwd_main_kernel(KP
         bool staged = false;
         // buffer resources over this head's rows (rows past s read as zero)
         const unsigned head_bytes = (unsigned)((size_t)s * D * sizeof(T));
-        const __amdgpu_buffer_rsrc_t rq = make_rsrc((void*)(gQ + hoff), head_bytes);
-        const __amdgpu_buffer_rsrc_t rdo = make_rsrc((void*)(gdO + hoff), head_bytes);
-        const __amdgpu_buffer_rsrc_t rk = make_rsrc((void*)(gK + hoff), head_bytes);
-        const __amdgpu_buffer_rsrc_t rlse = make_rsrc((void*)(p.lse + (size_t)head * s), (unsigned)(s * 4));
-        const __amdgpu_buffer_rsrc_t rdel = make_rsrc((void*)(p.delta + (size_t)head * p.s_pad), (unsigned)(p.s_pad * 4));
-        auto issue_q = [&](int b, int q0) {
-            load_tile_async<T, D, BQ, NW>(lsm + L::OFF_Q + b * L::QB, rq, q0, w, lane);
-            load_tile_async<T, D, BQ, NW>(lsm + L::OFF_DO + b * L::QB, rdo, q0, w, lane);
-            if (w == 0) load_vec_async(lsm + L::OFF_LSE + b * BQ * 4, rlse, q0, BQ, lane);
-            if (w == 1) load_vec_async(lsm + L::OFF_DEL + b * BQ * 4, rdel, q0, BQ, lane);
+        const u32x4 rq = rsrc_words(static_cast<const T*>(p.q) + hoff, head_bytes);
+        const u32x4 rdo = rsrc_words(static_cast<const T*>(p.dO) + hoff, head_bytes);
+        const u32x4 rk = rsrc_words(gK + hoff, head_bytes);
+        const u32x4 rlse = rsrc_words(p.lse + (size_t)head * s, (unsigned)(s * 4));
+        const u32x4 rdel = rsrc_words(p.delta + (size_t)head * p.s_pad, (unsigned)(p.s_pad * 4));
+        // The copies of one sub-step's rows, as NSLOT issue slots per wave: the
+        // wave's blocks of the Q tile, of the dO tile, then one slot for the
+        // lse (wave 0) or D (wave 1) values of the rows.  A sub-step spreads
+        // the slots of the next sub-step's prefetch over its first MFMA steps
+        // instead of issuing them in one burst.
+        constexpr int QITS = (L::QB / 1024 + NW - 1) / NW, NSLOT = 2 * QITS + 1;
+        const unsigned sink = lds_base + L::OFF_SINK;
+        auto issue_slot = [&](auto slotc, int b, int q0) {
+            constexpr int slot = decltype(slotc)::value;
+            if constexpr (slot < QITS) {
+                load_tile_block<T, D, BQ, NW>(lds_base + L::OFF_Q + b * L::QB, sink, rq, q0, w, lane, slot);
+            } else if constexpr (slot < 2 * QITS) {
+                load_tile_block<T, D, BQ, NW>(lds_base + L::OFF_DO + b * L::QB, sink, rdo, q0, w, lane, slot - QITS);
+            } else if constexpr (BQ == 64) {
+                const bool lw = w == 0, dw = w == 1;
+                copy4_to_lds(lw ? rlse : rdel, lw || dw ? (unsigned)((q0 + lane) * 4) : kOutOfRange,
+                             lw ? lds_base + L::OFF_LSE + b * BQ * 4 : (dw ? lds_base + L::OFF_DEL + b * BQ * 4 : sink));
+            } else {
+                if (w == 0) load_vec_async(lds_base + L::OFF_LSE + b * BQ * 4, rlse, q0, BQ, lane);
+                if (w == 1) load_vec_async(lds_base + L::OFF_DEL + b * BQ * 4, rdel, q0, BQ, lane);
+            }
+        };
+        auto issue_q = [&](int b, int q0) { static_for<0, NSLOT>([&](auto sc) { issue_slot(sc, b, q0); }); };
+        // part `part` of NPART of the slots
+        auto issue_q_part = [&](auto partc, auto npartc, int b, int q0) {
+            constexpr int part = decltype(partc)::value, npart = decltype(npartc)::value;
+            constexpr int per = (NSLOT + npart - 1) / npart;
+            constexpr int lo = part * per, hi = (part + 1) * per < NSLOT ? (part + 1) * per : NSLOT;
+            static_for<lo, hi>([&](auto sc) { issue_slot(sc, b, q0); });
         };
         f32x4 dK[NT][DT], dV[NT][DT];
-        V8 Vr[NT][KSD];
+        V8 Kr[NT][KSD], Vr[NT][KSD];
+        // initial value of S in this lane's key column: 0, or -inf for a key
+        // row past s, so that P = 0 there.  (Query rows past s need nothing:
+        // their Q, dO, lse and D read as zero, so dS = 0 on them, and no
+        // output row past s is stored.)
+        float s_init[NT];
 
         auto store_dkdv = [&](int kvt) {
 #pragma unroll
@@ -371,187 +536,215 @@ __global__ __launch_bounds__((Waves<T, D>::NTHREADS), 1) void bwd_main_kernel(KP
                     }
         };
 
-        for (int t = t_beg; t < t_end; ++t) {
-            if ((t - t_beg) % L::MAXT == 0) load_tasks(t);
-            const i32x4 rec = stask[(t - t_beg) % L::MAXT];
-            const int kv = __builtin_amdgcn_readfirstlane(rec[0]), qt = __builtin_amdgcn_readfirstlane(rec[1]);
-            if (kv != cur_kv) {
-                if (cur_kv >= 0) store_dkdv(cur_kv);
-                cur_kv = kv;
-                // this wave's V rows as B operands of dP (its K rows are read
-                // from the LDS copy of the tile when S is formed)
+        // The item's tasks, as runs of consecutive tasks on one KV tile: the
+        // run keeps the tile's K/V operands and dK/dV accumulators in
+        // registers and stores dK/dV at its end.
+        load_tasks(t_beg);
+        int t = t_beg;
+        while (t < t_end) {
+            const int kv = __builtin_amdgcn_readfirstlane(stask[(t - t_beg) % L::MAXT][0]);
+            // this wave's K and V rows: B operands of S and dP for the run
 #pragma unroll
-                for (int nt = 0; nt < NT; ++nt) {
-                    const int row = kv * TILE + w * RW + nt * 16 + c16;
-                    const size_t roff = hoff + (size_t)min(row, s - 1) * D;
-#pragma unroll
-                    for (int ks = 0; ks < KSD; ++ks) Vr[nt][ks] = *reinterpret_cast<const V8*>(gV + roff + ks * 32 + 8 * g);
-#pragma unroll
-                    for (int ks = 0; ks < KSD; ++ks)
-                        if (row >= s) Vr[nt][ks] = zero_vec<V8>();
-#pragma unroll
-                    for (int dt = 0; dt < DT; ++dt) {
-                        dK[nt][dt] = zero_vec<f32x4>();
-                        dV[nt][dt] = zero_vec<f32x4>();
-                    }
-                }
-                // the whole K tile in LDS (B operand of S, A operand of dQ^T),
-                // once every wave is done with the previous tile's
-                __syncthreads();
-                load_tile_async<T, D, TILE, NW>(lsm + L::OFF_K, rk, kv * TILE, w, lane);
-            }
-
-            const bool diag = CAUSAL && kv == qt;
-            const bool ragged = (kv + 1) * TILE > s || (qt + 1) * TILE > s;
-
-            const int rank = DET ? __builtin_amdgcn_readfirstlane(rec[2]) : 0;
-            const int cnt = DET ? __builtin_amdgcn_readfirstlane(rec[3]) : 1;
-            unsigned* flag = p.flags + (size_t)head * n + qt;
-            unsigned early = 0;  // tid 0: the flag as read before the last sub-step
-
-#pragma unroll 1
-            for (int sub = 0; sub < NSUB; ++sub) {
-                const int q0 = qt * TILE + sub * BQ;
-                // ---- the Q/dO rows [q0, q0+BQ) are in buffer `buf` (prefetched
-                // during the previous sub-step, or loaded now at an item start)
-                if (!staged) issue_q(buf, q0);
-                // landed for every wave, and the previous release published
-                asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-                __syncthreads();
-                if (pend_flag) {
-                    if (tid == 0) __hip_atomic_store(pend_flag, pend_val, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-                    pend_flag = nullptr;
-                }
-                // read this task's flag early: its latency hides behind the
-                // last sub-step (and a wait usually finds it already set)
-                if (DET && sub == NSUB - 1 && rank > 0 && tid == 0)
-                    early = __hip_atomic_load(flag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-                // prefetch the next sub-step's rows into the other buffer
-                staged = false;
-                if (sub + 1 < NSUB) {
-                    issue_q(buf ^ 1, q0 + BQ);
-                    staged = true;
-                } else if (t + 1 < t_end) {
-                    issue_q(buf ^ 1, task_q_of(t + 1) * TILE);
-                    staged = true;
-                }
-                const unsigned char* sQ = smem + L::OFF_Q + buf * L::QB;
-                const unsigned char* sdO = smem + L::OFF_DO + buf * L::QB;
-                const float* slse = reinterpret_cast<const float*>(smem + L::OFF_LSE) + buf * BQ;
-                const float* sdelta = reinterpret_cast<const float*>(smem + L::OFF_DEL) + buf * BQ;
-                buf ^= 1;
-
-                // ---- S = Q K^T and dP = dO V^T (rows: queries, cols: this wave's keys)
-                f32x4 S[MT][NT], dP[MT][NT];
-#pragma unroll
-                for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-                    for (int nt = 0; nt < NT; ++nt) {
-                        S[mt][nt] = zero_vec<f32x4>();
-                        dP[mt][nt] = zero_vec<f32x4>();
-                    }
+            for (int nt = 0; nt < NT; ++nt) {
+                const int row = kv * TILE + w * RW + nt * 16 + c16;
+                const size_t roff = hoff + (size_t)min(row, s - 1) * D;
 #pragma unroll
                 for (int ks = 0; ks < KSD; ++ks) {
-                    V8 bk[NT];
-#pragma unroll
-                    for (int nt = 0; nt < NT; ++nt) bk[nt] = frag_row<T, D>(sK, w * RW + nt * 16 + c16, ks * 32 + 8 * g);
-#pragma unroll
-                    for (int mt = 0; mt < MT; ++mt) {
-                        const V8 aq = frag_row<T, D>(sQ, mt * 16 + c16, ks * 32 + 8 * g);
-                        const V8 ao = frag_row<T, D>(sdO, mt * 16 + c16, ks * 32 + 8 * g);
-#pragma unroll
-                        for (int nt = 0; nt < NT; ++nt) {
-                            S[mt][nt] = E::mma(S[mt][nt], aq, bk[nt]);
-                            dP[mt][nt] = E::mma(dP[mt][nt], ao, Vr[nt][ks]);
-                        }
-                    }
+                    Kr[nt][ks] = *reinterpret_cast<const V8*>(gK + roff + ks * 32 + 8 * g);
+                    Vr[nt][ks] = *reinterpret_cast<const V8*>(gV + roff + ks * 32 + 8 * g);
                 }
-
-                // ---- P = exp(scale*S - lse), dS = P (dP - D); S/dP overwritten in place
 #pragma unroll
-                for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-                    for (int i = 0; i < 4; ++i) {
-                        const int ql = mt * 16 + 4 * g + i;
-                        const float l2 = slse[ql] * kLog2e, dl = sdelta[ql];
-#pragma unroll
-                        for (int nt = 0; nt < NT; ++nt) {
-                            float pv = __builtin_amdgcn_exp2f(S[mt][nt][i] * p.scale_log2 - l2);
-                            if (diag || ragged) {
-                                const int qg = q0 + ql;
-                                const int kg = kv * TILE + w * RW + nt * 16 + c16;
-                                const bool ok = qg < s && kg < s && (!CAUSAL || kg <= qg);
-                                pv = ok ? pv : 0.f;
-                            }
-                            S[mt][nt][i] = pv;
-                            dP[mt][nt][i] = pv * (dP[mt][nt][i] - dl);
-                        }
+                for (int ks = 0; ks < KSD; ++ks)
+                    if (row >= s) {
+                        Kr[nt][ks] = zero_vec<V8>();
+                        Vr[nt][ks] = zero_vec<V8>();
                     }
-
-                // ---- dV += P^T dO, dK += dS^T Q over this sub-step's rows.  The
-                // contraction index (query row) is permuted alike in both operands:
-                // slot (g, e) is row 16*(2ks + e/4) + 4g + e%4, which is where the
-                // 16x16 output layout of S left P and dS.
 #pragma unroll
-                for (int ks = 0; ks < KSQ; ++ks) {
-                    V8 aP[NT], aS[NT];
-#pragma unroll
-                    for (int nt = 0; nt < NT; ++nt)
-#pragma unroll
-                        for (int e = 0; e < 4; ++e) {
-                            aP[nt][e] = E::from_f(S[2 * ks][nt][e]);
-                            aP[nt][4 + e] = E::from_f(S[2 * ks + 1][nt][e]);
-                            aS[nt][e] = E::from_f(dP[2 * ks][nt][e]);
-                            aS[nt][4 + e] = E::from_f(dP[2 * ks + 1][nt][e]);
-                        }
-                    const int rA = ks * 32 + 4 * g, rB = ks * 32 + 16 + 4 * g;
-#pragma unroll
-                    for (int dt = 0; dt < DT; ++dt) {
-                        const V8 vq = frag_col<T, D>(sQ, rA, rB, dt * 16, c16);
-                        const V8 vo = frag_col<T, D>(sdO, rA, rB, dt * 16, c16);
-#pragma unroll
-                        for (int nt = 0; nt < NT; ++nt) {
-                            dV[nt][dt] = E::mma(dV[nt][dt], aP[nt], vo);
-                            dK[nt][dt] = E::mma(dK[nt][dt], aS[nt], vq);
-                        }
-                    }
+                for (int dt = 0; dt < DT; ++dt) {
+                    dK[nt][dt] = zero_vec<f32x4>();
+                    dV[nt][dt] = zero_vec<f32x4>();
                 }
-
-                // ---- dS to LDS as [query][key] for the dQ contraction
-#pragma unroll
-                for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-                    for (int nt = 0; nt < NT; ++nt)
-#pragma unroll
-                        for (int i = 0; i < 4; ++i)
-                            sdS[(sub * BQ + mt * 16 + 4 * g + i) * LDSS + w * RW + nt * 16 + c16] =
-                                E::from_f(dP[mt][nt][i]);
-                // No barrier here: the next sub-step's first barrier orders
-                // these reads of the Q/dO buffer before its refill, and the
-                // dS rows are read only after the barrier that ends the task's
-                // last sub-step (below).
+                s_init[nt] = row < s ? 0.f : -__builtin_inff();
             }
+            // the whole K tile in LDS (A operand of dQ^T), once every wave is
+            // done with the previous tile's
+            __syncthreads();
+            load_tile_async<T, D, TILE, NW>(lds_base + L::OFF_K, rk, kv * TILE, w, lane);
 
-            // ---- R phase, first half: wait for this tile's turn and start the
-            // accumulator loads now, so that their latency overlaps the dQ
-            // contraction below.  The previous task's release was published
-            // at this task's first barrier, so the work group holds no
-            // unpublished release while it waits.
-            float* acc = p.dq_acc + (size_t)head * p.s_pad * D;
-            const __amdgpu_buffer_rsrc_t racc = make_rsrc(acc, (unsigned)(p.s_pad * D * sizeof(float)));
-            const int col0 = w * DW + 4 * g;
-            f32x4 prev[NDT][MTT];
-            // One barrier ends the last sub-step (all of dS is in LDS) and, for
-            // rank > 0, the wait for this tile's turn: thread 0 waits for the
-            // flag before arriving.
-            if (DET && rank > 0) {
-                if (tid == 0) {
+            bool more;
+            do {
+                const i32x4 rec = stask[(t - t_beg) % L::MAXT];
+                const int qt = __builtin_amdgcn_readfirstlane(rec[1]);
+
+                // Causal mask: key column kloc of the tile is kept for query row
+                // qloc when kloc <= qloc + (qt - kv) * TILE, which holds for every
+                // element of a tile below the diagonal.
+                const int diag_off = (qt - kv) * TILE;
+
+                const int rank = DET ? __builtin_amdgcn_readfirstlane(rec[2]) : 0;
+                const int cnt = DET ? __builtin_amdgcn_readfirstlane(rec[3]) : 1;
+                unsigned* flag = p.flags + (size_t)head * n + qt;
+                unsigned early = 0;  // tid 0: the flag as read before the last sub-step
+                float* acc = p.dq_acc + (size_t)head * p.s_pad * D;
+
+#pragma unroll 1
+                for (int sub = 0; sub < NSUB; ++sub) {
+                    const int q0 = qt * TILE + sub * BQ;
+                    // ---- the Q/dO rows [q0, q0+BQ) are in buffer `buf` (prefetched
+                    // during the previous sub-step, or loaded now at an item start)
+                    if (!staged) issue_q(buf, q0);
+                    // first row of the next sub-step (of this task or the next; at
+                    // the item's end, a harmless copy of these rows again, which
+                    // the item waits for before it ends)
+                    const int q_next = sub + 1 < NSUB ? q0 + BQ : (t + 1 < t_end ? next_q_of(t) * TILE : q0);
+                    // landed for every wave, every wave done with the previous
+                    // sub-step's dS, and the previous release's stores acknowledged
+                    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+                    __syncthreads();
+                    // the next sub-step's rows go to the other buffer, issued
+                    // during this sub-step's first MFMA steps
+                    const int pf_buf = buf ^ 1;
+                    staged = true;
+                    // publish the previous release; then read this task's flag early:
+                    // its latency hides behind the last sub-step (and a wait usually
+                    // finds it already set).  Nothing waits on either here.
+                    if (pend_flag) {
+                        if (tid == 0) __hip_atomic_store(pend_flag, pend_val, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                        pend_flag = nullptr;
+                    }
+                    if (DET && sub == NSUB - 1 && rank > 0 && tid == 0)
+                        early = __hip_atomic_load(flag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                    const unsigned char* sQ = smem + L::OFF_Q + buf * L::QB;
+                    const unsigned char* sdO = smem + L::OFF_DO + buf * L::QB;
+                    const float* slse = reinterpret_cast<const float*>(smem + L::OFF_LSE) + buf * BQ;
+                    const float* sdelta = reinterpret_cast<const float*>(smem + L::OFF_DEL) + buf * BQ;
+                    buf ^= 1;
+
+                    // ---- the sub-step, in groups of 32 query rows: S and dP for the
+                    // group, P and dS, dS to LDS, then the group's share of dV and dK.
+                    // Groups are independent until they accumulate into dV/dK, so the
+                    // scheduler can overlap one group's MFMAs with the other's
+                    // softmax.
+                    static_for<0, KSQ>([&](auto gqc) {
+                        constexpr int GQ = decltype(gqc)::value;
+                        const int gq = GQ;
+                        // S = Q K^T and dP = dO V^T (rows: queries, cols: this wave's keys)
+                        f32x4 S[2][NT], dP[2][NT];
+#pragma unroll
+                        for (int m = 0; m < 2; ++m)
+#pragma unroll
+                            for (int nt = 0; nt < NT; ++nt) {
+#pragma unroll
+                                for (int i = 0; i < 4; ++i) S[m][nt][i] = s_init[nt];
+                                dP[m][nt] = zero_vec<f32x4>();
+                            }
+                        static_for<0, KSD>([&](auto ksc) {
+                            constexpr int ks = decltype(ksc)::value;
+                            if constexpr (GQ == 0) issue_q_part(ksc, std::integral_constant<int, KSD>{}, pf_buf, q_next);
+                            V8 aq[2], ao[2];
+#pragma unroll
+                            for (int m = 0; m < 2; ++m) {
+                                aq[m] = frag_row<T, D>(sQ, (2 * gq + m) * 16 + c16, ks * 32 + 8 * g);
+                                ao[m] = frag_row<T, D>(sdO, (2 * gq + m) * 16 + c16, ks * 32 + 8 * g);
+                            }
+#pragma unroll
+                            for (int m = 0; m < 2; ++m)
+#pragma unroll
+                                for (int nt = 0; nt < NT; ++nt) {
+                                    S[m][nt] = E::mma(S[m][nt], aq[m], Kr[nt][ks]);
+                                    dP[m][nt] = E::mma(dP[m][nt], ao[m], Vr[nt][ks]);
+                                }
+                        });
+                        // P = exp(scale*S - lse), dS = P (dP - D), in place
+#pragma unroll
+                        for (int m = 0; m < 2; ++m)
+#pragma unroll
+                            for (int i = 0; i < 4; ++i) {
+                                const int ql = (2 * gq + m) * 16 + 4 * g + i;
+                                const float l2 = slse[ql] * kLog2e, dl = sdelta[ql];
+#pragma unroll
+                                for (int nt = 0; nt < NT; ++nt) {
+                                    float pv = __builtin_amdgcn_exp2f(S[m][nt][i] * p.scale_log2 - l2);
+                                    if constexpr (CAUSAL)
+                                        pv = (w * RW + nt * 16 + c16 <= sub * BQ + ql + diag_off) ? pv : 0.f;
+                                    S[m][nt][i] = pv;
+                                    dP[m][nt][i] = pv * (dP[m][nt][i] - dl);
+                                }
+                            }
+                        // dS to LDS as [query][key] for the dQ contraction
+#pragma unroll
+                        for (int m = 0; m < 2; ++m)
+#pragma unroll
+                            for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+                                for (int i = 0; i < 4; ++i)
+                                    sdS[(sub * BQ + (2 * gq + m) * 16 + 4 * g + i) * LDSS + w * RW + nt * 16 + c16] =
+                                        E::from_f(dP[m][nt][i]);
+                        // dV += P^T dO, dK += dS^T Q over the group's rows.  The
+                        // contraction index (query row) is permuted alike in both
+                        // operands: slot (g, e) is row 32gq + 16(e/4) + 4g + e%4,
+                        // which is where the 16x16 output layout of S left P and dS.
+                        V8 aP[NT], aS[NT];
+#pragma unroll
+                        for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+                            for (int e = 0; e < 4; ++e) {
+                                aP[nt][e] = E::from_f(S[0][nt][e]);
+                                aP[nt][4 + e] = E::from_f(S[1][nt][e]);
+                                aS[nt][e] = E::from_f(dP[0][nt][e]);
+                                aS[nt][4 + e] = E::from_f(dP[1][nt][e]);
+                            }
+                        if constexpr (sizeof(T) == 2) {
+                            // dO and Q column operands one 16-column step ahead of
+                            // the MFMAs that use them
+                            using P = Pad<T, D>;
+                            constexpr int ODO = L::OFF_DO - L::OFF_Q;
+                            const lds_u8* tq = (const lds_u8*)sQ + (4 * g + (c16 >> 2)) * P::RS + 8 * (c16 & 3);
+                            auto fetch = [&](auto dtc, V8& vq, V8& vo) {
+                                constexpr int o = GQ * 32 * P::RS + decltype(dtc)::value * 32;
+                                vq = tr_frag<o, o + 16 * P::RS>(tq);
+                                vo = tr_frag<o + ODO, o + ODO + 16 * P::RS>(tq);
+                            };
+                            V8 cq, co, nq, no;
+                            fetch(std::integral_constant<int, 0>{}, cq, co);
+                            static_for<0, DT>([&](auto dtc) {
+                                constexpr int dt = decltype(dtc)::value;
+                                if constexpr (dt + 1 < DT) fetch(std::integral_constant<int, dt + 1>{}, nq, no);
+#pragma unroll
+                                for (int nt = 0; nt < NT; ++nt) {
+                                    dV[nt][dt] = E::mma(dV[nt][dt], aP[nt], co);
+                                    dK[nt][dt] = E::mma(dK[nt][dt], aS[nt], cq);
+                                }
+                                if constexpr (dt + 1 < DT) {
+                                    cq = nq;
+                                    co = no;
+                                }
+                            });
+                        } else {
+                            const int rA = GQ * 32 + 4 * g, rB = GQ * 32 + 16 + 4 * g;
+#pragma unroll
+                            for (int dt = 0; dt < DT; ++dt) {
+                                const V8 vq = frag_col<T, D>(sQ, rA, rB, dt * 16, c16);
+                                const V8 vo = frag_col<T, D>(sdO, rA, rB, dt * 16, c16);
+#pragma unroll
+                                for (int nt = 0; nt < NT; ++nt) {
+                                    dV[nt][dt] = E::mma(dV[nt][dt], aP[nt], vo);
+                                    dK[nt][dt] = E::mma(dK[nt][dt], aS[nt], vq);
+                                }
+                            }
+                        }
+                    });
+                }
+
+                // ---- R phase.  One barrier ends the last sub-step (all of dS is in
+                // LDS) and, for rank > 0, the wait for this tile's turn: thread 0
+                // waits for the flag before arriving.
+                if (DET && rank > 0 && tid == 0) {
                     const unsigned long long t0 = p.stats ? __builtin_readcyclecounter() : 0;
                     unsigned spins = 0;
                     unsigned seen = early;
                     while (seen != (unsigned)rank) {
-                        if ((spins & 1023u) == 0 &&
-                            __hip_atomic_load(p.abort, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT))
+                        if ((spins & 1023u) == 0 && __hip_atomic_load(p.abort, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT))
                             break;
                         __builtin_amdgcn_s_sleep(1);
                         if (++spins >= kSpinLimit) {
@@ -566,99 +759,95 @@ __global__ __launch_bounds__((Waves<T, D>::NTHREADS), 1) void bwd_main_kernel(KP
                         polls += spins + 1;
                     }
                 }
-            }
-            __syncthreads();
-            if (DET && rank > 0) {
-#pragma unroll
-                for (int dtw = 0; dtw < NDT; ++dtw)
-#pragma unroll
-                    for (int mt = 0; mt < MTT; ++mt)
-                        prev[dtw][mt] =
-                            load_sc1(racc, (unsigned)(((qt * TILE + mt * 16 + c16) * D + col0 + dtw * 16) * 4));
-            }
-
-            // ---- dQ^T[d][q] = K^T[d][key] dS^T[key][q] over the tile, for this
-            // wave's d columns (lane: 4 consecutive d of one query row), in two
-            // halves of query rows; each half is added into the accumulator
-            // as soon as it is done (R phase, second half).
-            constexpr int MTH = MTT / 2;
-#pragma unroll
-            for (int half = 0; half < 2; ++half) {
-                f32x4 dQt[NDT][MTH];
-#pragma unroll
-                for (int dtw = 0; dtw < NDT; ++dtw)
-#pragma unroll
-                    for (int j = 0; j < MTH; ++j) dQt[dtw][j] = zero_vec<f32x4>();
-#pragma unroll
-                for (int ks = 0; ks < KSKV; ++ks) {
-                    V8 a[NDT];
-#pragma unroll
-                    for (int dtw = 0; dtw < NDT; ++dtw)
-                        a[dtw] = frag_col<T, D>(sK, ks * 32 + 8 * g, ks * 32 + 8 * g + 4, w * DW + dtw * 16, c16);
-#pragma unroll
-                    for (int j = 0; j < MTH; ++j) {
-                        const int mt = half * MTH + j;
-                        const V8 b = *reinterpret_cast<const V8*>(sdS + (mt * 16 + c16) * LDSS + ks * 32 + 8 * g);
-#pragma unroll
-                        for (int dtw = 0; dtw < NDT; ++dtw)
-                            // deterministic: dQ^T tiles (lane: 4 consecutive d of one
-                            // query row, 16-byte accumulator accesses); atomic: dQ
-                            // tiles (16 lanes: 16 consecutive d of one query row, so
-                            // each atomic instruction covers 64 contiguous bytes per row)
-                            dQt[dtw][j] = DET ? E::mma(dQt[dtw][j], a[dtw], b) : E::mma(dQt[dtw][j], b, a[dtw]);
-                    }
-                }
+                __syncthreads();
                 if (DET) {
-                    if (rank > 0) {
+                    const __amdgpu_buffer_rsrc_t racc = make_rsrc(acc, (unsigned)(p.s_pad * D * sizeof(float)));
+                    const int col0 = w * DW + 4 * g;
+                    // The accumulator is stored as whole 16x16 tiles in the MFMA
+                    // output layout (lane l's 4 values at 16*l bytes of the
+                    // tile's 1 KiB), so every load and store instruction covers
+                    // one contiguous KiB.
+                    auto acc_off = [&](int mtt, int dtw) {
+                        return (unsigned)((((qt * MTT + mtt) * (D / 16) + w * NDT + dtw) * 64 + lane) * 16);
+                    };
+                    // the accumulator rows of the whole tile, requested a few at a
+                    // time between the 32-key steps of the dQ contraction, so that
+                    // their issue and latency overlap it; every part's contraction
+                    // comes before the first use of them
+                    constexpr int NPREV = NDT * MTT, NSTEP = NSUB * KSKV, PER = (NPREV + NSTEP - 1) / NSTEP;
+                    f32x4 prev[NDT][MTT];
+                    f32x4 dq[NSUB][NDT][MT];
+                    static_for<0, NSUB>([&](auto pc) {
+                        constexpr int part = decltype(pc)::value;
+                        dq_rows(dq[part], part * BQ, [&](auto ksc) {
+                            // (rank 0 does not use them: no branch for it)
+                            constexpr int step = part * KSKV + decltype(ksc)::value;
+                            static_for<0, PER>([&](auto jc) {
+                                constexpr int i = step * PER + decltype(jc)::value;
+                                if constexpr (i < NPREV)
+                                    prev[i / MTT][i % MTT] = load_sc1(racc, acc_off(i % MTT, i / MTT));
+                            });
+                            // keep them here: the scheduler would otherwise sink
+                            // every load below the contraction
+                            __builtin_amdgcn_sched_barrier(0);
+                        });
+                    });
+#pragma unroll
+                    for (int part = 0; part < NSUB; ++part) {
 #pragma unroll
                         for (int dtw = 0; dtw < NDT; ++dtw)
 #pragma unroll
-                            for (int j = 0; j < MTH; ++j) dQt[dtw][j] = prev[dtw][half * MTH + j] + dQt[dtw][j];
-                    }
-                    if (rank == cnt - 1) {
-                        // the last contributor writes dQ = scale * sum in the output type
+                            for (int mt = 0; mt < MT; ++mt) {
+                                const int mtt = part * MT + mt;  // 16-row tile of the task's Q tile
+                                f32x4 v = dq[part][dtw][mt];
+                                if (rank > 0) v = prev[dtw][mtt] + v;
+                                const int row = qt * TILE + mtt * 16 + c16;
+                                if (rank == cnt - 1) {
+                                    // the last contributor writes dQ = scale * sum in the output type
+                                    V4 o;
 #pragma unroll
-                        for (int dtw = 0; dtw < NDT; ++dtw)
-#pragma unroll
-                            for (int j = 0; j < MTH; ++j) {
-                                const int row = qt * TILE + (half * MTH + j) * 16 + c16;
-                                V4 o;
-#pragma unroll
-                                for (int e = 0; e < 4; ++e) o[e] = E::from_f(p.scale * dQt[dtw][j][e]);
-                                if (row < s)
-                                    *reinterpret_cast<V4*>(gdQ + hoff + (size_t)row * D + col0 + dtw * 16) = o;
+                                    for (int e = 0; e < 4; ++e) o[e] = E::from_f(p.scale * v[e]);
+                                    if (row < s) *reinterpret_cast<V4*>(gdQ + hoff + (size_t)row * D + col0 + dtw * 16) = o;
+                                } else {
+                                    store_sc1(racc, acc_off(mtt, dtw), v);
+                                }
                             }
-                    } else {
-#pragma unroll
-                        for (int dtw = 0; dtw < NDT; ++dtw)
-#pragma unroll
-                            for (int j = 0; j < MTH; ++j)
-                                store_sc1(racc,
-                                          (unsigned)(((qt * TILE + (half * MTH + j) * 16 + c16) * D + col0 +
-                                                      dtw * 16) * 4),
-                                          dQt[dtw][j]);
+                    }
+                    if (rank != cnt - 1) {
+                        // published after the next barrier that follows a full
+                        // s_waitcnt (next task's staging, or the end of the item)
+                        pend_flag = flag;
+                        pend_val = (unsigned)(rank + 1);
                     }
                 } else {
 #pragma unroll
-                    for (int dtw = 0; dtw < NDT; ++dtw)
+                    for (int part = 0; part < NSUB; ++part) {
+                        f32x4 dq[NDT][MT];
+                        dq_rows(dq, part * BQ, [](auto) {});
 #pragma unroll
-                        for (int j = 0; j < MTH; ++j)
+                        for (int dtw = 0; dtw < NDT; ++dtw)
 #pragma unroll
-                            for (int i = 0; i < 4; ++i)
-                                unsafeAtomicAdd(acc + (size_t)(qt * TILE + (half * MTH + j) * 16 + 4 * g + i) * D +
-                                                    w * DW + dtw * 16 + c16,
-                                                dQt[dtw][j][i]);
+                            for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+                                for (int i = 0; i < 4; ++i)
+                                    unsafeAtomicAdd(acc + (size_t)(qt * TILE + part * BQ + mt * 16 + 4 * g + i) * D + w * DW +
+                                                        dtw * 16 + c16,
+                                                    dq[dtw][mt][i]);
+                    }
                 }
-            }
-            if (DET && rank != cnt - 1) {
-                // published after the next barrier that follows a full
-                // s_waitcnt (next task's staging, or the end of the item)
-                pend_flag = p.flags + (size_t)head * n + qt;
-                pend_val = (unsigned)(rank + 1);
-            }
+                ++t;
+                more = false;
+                if (t < t_end) {
+                    if ((t - t_beg) % L::MAXT == 0) load_tasks(t);
+                    more = __builtin_amdgcn_readfirstlane(stask[(t - t_beg) % L::MAXT][0]) == kv;
+                }
+            } while (more);
+            store_dkdv(kv);
         }
+        // the prefetch issued by the item's last sub-step lands before the
+        // next item's first copies are issued
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
         if (pend_flag) publish();
-        if (cur_kv >= 0) store_dkdv(cur_kv);
         if (p.stats) item_cycles += __builtin_readcyclecounter() - t_item0;
     }
     if (p.stats && tid == 0) {
@@ -732,7 +921,7 @@ static int launch_main_t(const KParams& kp, const BwdLaunch& L) {
         attr_set = true;
     }
     int per_cu = 0;
-    constexpr int nthreads = Waves<T, D>::NTHREADS;
+    constexpr int nthreads = kThreads;
     if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, (const void*)kern, nthreads, smem) != hipSuccess ||
         per_cu < 1)
         return fail(ATTN_ERR_HIP, "occupancy query failed for the main kernel");
