@@ -620,82 +620,77 @@ void bwd_main_kernel(KParams p) {
                     const float* sdelta = reinterpret_cast<const float*>(smem + L::OFF_DEL) + buf * BQ;
                     buf ^= 1;
 
-                    // ---- the sub-step, in groups of 32 query rows: S and dP for the
-                    // group, P and dS, dS to LDS, then the group's share of dV and dK.
-                    // Groups are independent until they accumulate into dV/dK, so the
-                    // scheduler can overlap one group's MFMAs with the other's
-                    // softmax.
-                    static_for<0, KSQ>([&](auto gqc) {
+                    // ---- the sub-step, in groups of 32 query rows.  Per group: S and
+                    // dP (phase 1), P and dS (softmax), dV and dK (phase 2).  The
+                    // source order below lets the scheduler overlap one group's
+                    // MFMAs with the other group's softmax; the dS stores to LDS
+                    // come last, so that no LDS store sits between the loads of
+                    // the two groups.
+                    f32x4 S[KSQ][2][NT], dP[KSQ][2][NT];
+                    V8 aP[KSQ][NT], aS[KSQ][NT];
+                    // S = Q K^T and dP = dO V^T (rows: queries, cols: this wave's keys)
+                    auto phase1 = [&](auto gqc) {
                         constexpr int GQ = decltype(gqc)::value;
-                        const int gq = GQ;
-                        // S = Q K^T and dP = dO V^T (rows: queries, cols: this wave's keys)
-                        f32x4 S[2][NT], dP[2][NT];
 #pragma unroll
                         for (int m = 0; m < 2; ++m)
 #pragma unroll
                             for (int nt = 0; nt < NT; ++nt) {
 #pragma unroll
-                                for (int i = 0; i < 4; ++i) S[m][nt][i] = s_init[nt];
-                                dP[m][nt] = zero_vec<f32x4>();
+                                for (int i = 0; i < 4; ++i) S[GQ][m][nt][i] = s_init[nt];
+                                dP[GQ][m][nt] = zero_vec<f32x4>();
                             }
+                        // LDS operands one 32-wide step ahead of the MFMAs that use them
+                        V8 aq[2][2], ao[2][2];
+                        auto fetch = [&](auto ksc) {
+                            constexpr int ks = decltype(ksc)::value;
+#pragma unroll
+                            for (int m = 0; m < 2; ++m) {
+                                aq[ks % 2][m] = frag_row<T, D>(sQ, (2 * GQ + m) * 16 + c16, ks * 32 + 8 * g);
+                                ao[ks % 2][m] = frag_row<T, D>(sdO, (2 * GQ + m) * 16 + c16, ks * 32 + 8 * g);
+                            }
+                        };
+                        fetch(std::integral_constant<int, 0>{});
                         static_for<0, KSD>([&](auto ksc) {
                             constexpr int ks = decltype(ksc)::value;
                             if constexpr (GQ == 0) issue_q_part(ksc, std::integral_constant<int, KSD>{}, pf_buf, q_next);
-                            V8 aq[2], ao[2];
-#pragma unroll
-                            for (int m = 0; m < 2; ++m) {
-                                aq[m] = frag_row<T, D>(sQ, (2 * gq + m) * 16 + c16, ks * 32 + 8 * g);
-                                ao[m] = frag_row<T, D>(sdO, (2 * gq + m) * 16 + c16, ks * 32 + 8 * g);
-                            }
+                            if constexpr (ks + 1 < KSD) fetch(std::integral_constant<int, ks + 1>{});
 #pragma unroll
                             for (int m = 0; m < 2; ++m)
 #pragma unroll
                                 for (int nt = 0; nt < NT; ++nt) {
-                                    S[m][nt] = E::mma(S[m][nt], aq[m], Kr[nt][ks]);
-                                    dP[m][nt] = E::mma(dP[m][nt], ao[m], Vr[nt][ks]);
+                                    S[GQ][m][nt] = E::mma(S[GQ][m][nt], aq[ks % 2][m], Kr[nt][ks]);
+                                    dP[GQ][m][nt] = E::mma(dP[GQ][m][nt], ao[ks % 2][m], Vr[nt][ks]);
                                 }
                         });
-                        // P = exp(scale*S - lse), dS = P (dP - D), in place
+                    };
+                    // P = exp(scale*S - lse), dS = P (dP - D), as the A operands of
+                    // phase 2.  The contraction index (query row) is permuted alike
+                    // in both operands there: slot (g, e) is row 32gq + 16(e/4) +
+                    // 4g + e%4, which is where the 16x16 output layout of S left P
+                    // and dS.
+                    auto softmax = [&](auto gqc) {
+                        constexpr int GQ = decltype(gqc)::value;
 #pragma unroll
                         for (int m = 0; m < 2; ++m)
 #pragma unroll
                             for (int i = 0; i < 4; ++i) {
-                                const int ql = (2 * gq + m) * 16 + 4 * g + i;
+                                const int ql = (2 * GQ + m) * 16 + 4 * g + i;
                                 const float l2 = slse[ql] * kLog2e, dl = sdelta[ql];
 #pragma unroll
                                 for (int nt = 0; nt < NT; ++nt) {
-                                    float pv = __builtin_amdgcn_exp2f(S[m][nt][i] * p.scale_log2 - l2);
+                                    float pv = __builtin_amdgcn_exp2f(S[GQ][m][nt][i] * p.scale_log2 - l2);
                                     if constexpr (CAUSAL)
                                         pv = (w * RW + nt * 16 + c16 <= sub * BQ + ql + diag_off) ? pv : 0.f;
-                                    S[m][nt][i] = pv;
-                                    dP[m][nt][i] = pv * (dP[m][nt][i] - dl);
+                                    aP[GQ][nt][4 * m + i] = E::from_f(pv);
+                                    aS[GQ][nt][4 * m + i] = E::from_f(pv * (dP[GQ][m][nt][i] - dl));
                                 }
                             }
-                        // dS to LDS as [query][key] for the dQ contraction
-#pragma unroll
-                        for (int m = 0; m < 2; ++m)
-#pragma unroll
-                            for (int nt = 0; nt < NT; ++nt)
-#pragma unroll
-                                for (int i = 0; i < 4; ++i)
-                                    sdS[(sub * BQ + (2 * gq + m) * 16 + 4 * g + i) * LDSS + w * RW + nt * 16 + c16] =
-                                        E::from_f(dP[m][nt][i]);
-                        // dV += P^T dO, dK += dS^T Q over the group's rows.  The
-                        // contraction index (query row) is permuted alike in both
-                        // operands: slot (g, e) is row 32gq + 16(e/4) + 4g + e%4,
-                        // which is where the 16x16 output layout of S left P and dS.
-                        V8 aP[NT], aS[NT];
-#pragma unroll
-                        for (int nt = 0; nt < NT; ++nt)
-#pragma unroll
-                            for (int e = 0; e < 4; ++e) {
-                                aP[nt][e] = E::from_f(S[0][nt][e]);
-                                aP[nt][4 + e] = E::from_f(S[1][nt][e]);
-                                aS[nt][e] = E::from_f(dP[0][nt][e]);
-                                aS[nt][4 + e] = E::from_f(dP[1][nt][e]);
-                            }
+                    };
+                    // dV += P^T dO, dK += dS^T Q over the group's rows
+                    auto phase2 = [&](auto gqc) {
+                        constexpr int GQ = decltype(gqc)::value;
                         if constexpr (sizeof(T) == 2) {
-                            // dO and Q column operands one 16-column step ahead of
+                            // dO and Q column operands PF 16-column steps ahead of
                             // the MFMAs that use them
                             using P = Pad<T, D>;
                             constexpr int ODO = L::OFF_DO - L::OFF_Q;
@@ -705,19 +700,20 @@ void bwd_main_kernel(KParams p) {
                                 vq = tr_frag<o, o + 16 * P::RS>(tq);
                                 vo = tr_frag<o + ODO, o + ODO + 16 * P::RS>(tq);
                             };
-                            V8 cq, co, nq, no;
-                            fetch(std::integral_constant<int, 0>{}, cq, co);
+                            constexpr int PF = 2;  // steps in flight ahead of the MFMAs
+                            V8 rq[PF + 1], ro[PF + 1];
+                            static_for<0, (PF < DT ? PF : DT)>([&](auto jc) {
+                                fetch(jc, rq[decltype(jc)::value], ro[decltype(jc)::value]);
+                            });
                             static_for<0, DT>([&](auto dtc) {
                                 constexpr int dt = decltype(dtc)::value;
-                                if constexpr (dt + 1 < DT) fetch(std::integral_constant<int, dt + 1>{}, nq, no);
+                                if constexpr (dt + PF < DT)
+                                    fetch(std::integral_constant<int, dt + PF>{}, rq[(dt + PF) % (PF + 1)],
+                                          ro[(dt + PF) % (PF + 1)]);
 #pragma unroll
                                 for (int nt = 0; nt < NT; ++nt) {
-                                    dV[nt][dt] = E::mma(dV[nt][dt], aP[nt], co);
-                                    dK[nt][dt] = E::mma(dK[nt][dt], aS[nt], cq);
-                                }
-                                if constexpr (dt + 1 < DT) {
-                                    cq = nq;
-                                    co = no;
+                                    dV[nt][dt] = E::mma(dV[nt][dt], aP[GQ][nt], ro[dt % (PF + 1)]);
+                                    dK[nt][dt] = E::mma(dK[nt][dt], aS[GQ][nt], rq[dt % (PF + 1)]);
                                 }
                             });
                         } else {
@@ -728,12 +724,164 @@ void bwd_main_kernel(KParams p) {
                                 const V8 vo = frag_col<T, D>(sdO, rA, rB, dt * 16, c16);
 #pragma unroll
                                 for (int nt = 0; nt < NT; ++nt) {
-                                    dV[nt][dt] = E::mma(dV[nt][dt], aP[nt], vo);
-                                    dK[nt][dt] = E::mma(dK[nt][dt], aS[nt], vq);
+                                    dV[nt][dt] = E::mma(dV[nt][dt], aP[GQ][nt], vo);
+                                    dK[nt][dt] = E::mma(dK[nt][dt], aS[GQ][nt], vq);
                                 }
                             }
                         }
-                    });
+                    };
+                    // dS to LDS as [query][key] for the dQ contraction
+                    auto store_ds = [&](auto gqc) {
+                        constexpr int GQ = decltype(gqc)::value;
+#pragma unroll
+                        for (int m = 0; m < 2; ++m)
+#pragma unroll
+                            for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+                                for (int i = 0; i < 4; ++i)
+                                    sdS[(sub * BQ + (2 * GQ + m) * 16 + 4 * g + i) * LDSS + w * RW + nt * 16 + c16] =
+                                        aS[GQ][nt][4 * m + i];
+                    };
+                    if constexpr (sizeof(T) == 2 && NT == 2 && KSQ == 2) {
+                        // The bf16 sub-step as an explicit instruction schedule.  The
+                        // wave is alone on its SIMD, so no other wave hides its LDS
+                        // latency or overlaps its VALU work with the matrix core.
+                        // The sub-step is a sequence of MFMA slots (phase 1 of both
+                        // groups, then phase 2 of both); each slot carries the work
+                        // placed beside its MFMA: LDS operand reads two MFMA steps
+                        // ahead of their use, the next sub-step's copies, a pair of
+                        // softmax values of the other group (phase 2 of a group
+                        // needs its whole softmax, phase 1 of the next does not),
+                        // and the dS stores.  A scheduling fence closes each slot.
+                        using P = Pad<T, D>;
+                        constexpr int A = 8 * KSD, B = 4 * DT, NMF = 2 * A + 2 * B;
+                        constexpr int ODO = L::OFF_DO - L::OFF_Q;
+                        V8 q1[3][2], o1[3][2];  // phase-1 operands, ring of 3 steps: [step][m]
+                        s16x4 t2[3][2][2];      // phase-2 operands, ring of 3 steps: [step][Q/dO][lo/hi]
+                        f32x4 lsev[2][2], delv[2][2];  // [group][m]: lse and D of rows 4g..4g+3
+                        const lds_u8* tq = (const lds_u8*)sQ + (4 * g + (c16 >> 2)) * P::RS + 8 * (c16 & 3);
+                        // read k (0..3) of phase-1 step j = (group, 32-wide d step)
+                        auto rd1 = [&](auto jc, auto kc) {
+                            constexpr int j = decltype(jc)::value, k = decltype(kc)::value;
+                            constexpr int G = j / KSD, ks = j % KSD, m = k % 2;
+                            if constexpr (k < 2)
+                                q1[j % 3][m] = frag_row<T, D>(sQ, (2 * G + m) * 16 + c16, ks * 32 + 8 * g);
+                            else
+                                o1[j % 3][m] = frag_row<T, D>(sdO, (2 * G + m) * 16 + c16, ks * 32 + 8 * g);
+                        };
+                        // transposed read k (0..3) of phase-2 step u = (group, 16-wide d step)
+                        auto rd2 = [&](auto uc, auto kc) {
+                            constexpr int u = decltype(uc)::value, k = decltype(kc)::value;
+                            constexpr int G = u / DT, dt = u % DT, isdo = k / 2, hi = k % 2;
+                            constexpr int o = G * 32 * P::RS + dt * 32 + isdo * ODO + hi * 16 * P::RS;
+                            t2[u % 3][isdo][hi] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(tq + o));
+                        };
+                        auto op2 = [&](int slot, int isdo) {
+                            return __builtin_bit_cast(V8, __builtin_shufflevector(t2[slot][isdo][0], t2[slot][isdo][1], 0,
+                                                                                 1, 2, 3, 4, 5, 6, 7));
+                        };
+                        auto rd_lse = [&](auto Gc, auto kc) {
+                            constexpr int G = decltype(Gc)::value, k = decltype(kc)::value, m = k % 2;
+                            if constexpr (k < 2)
+                                lsev[G][m] = *reinterpret_cast<const f32x4*>(slse + (2 * G + m) * 16 + 4 * g);
+                            else
+                                delv[G][m] = *reinterpret_cast<const f32x4*>(sdelta + (2 * G + m) * 16 + 4 * g);
+                        };
+                        // softmax pair k (0..7) of group G: rows (m, 2ip..2ip+1), key tile nt
+                        auto sm_pair = [&](auto Gc, auto kc) {
+                            constexpr int G = decltype(Gc)::value, k = decltype(kc)::value;
+                            constexpr int m = k / 4, nt = (k / 2) % 2, ip = k % 2;
+#pragma unroll
+                            for (int i = 2 * ip; i < 2 * ip + 2; ++i) {
+                                const int ql = (2 * G + m) * 16 + 4 * g + i;
+                                float pv = __builtin_amdgcn_exp2f(S[G][m][nt][i] * p.scale_log2 - lsev[G][m][i] * kLog2e);
+                                if constexpr (CAUSAL) pv = (w * RW + nt * 16 + c16 <= sub * BQ + ql + diag_off) ? pv : 0.f;
+                                aP[G][nt][4 * m + i] = E::from_f(pv);
+                                aS[G][nt][4 * m + i] = E::from_f(pv * (dP[G][m][nt][i] - delv[G][m][i]));
+                            }
+                        };
+                        // dS store k (0..31): group, m, key tile, row
+                        auto st_ds = [&](auto kc) {
+                            constexpr int k = decltype(kc)::value, G = k / 16, m = (k / 8) % 2, nt = (k / 4) % 2, i = k % 4;
+                            sdS[(sub * BQ + (2 * G + m) * 16 + 4 * g + i) * LDSS + w * RW + nt * 16 + c16] =
+                                aS[G][nt][4 * m + i];
+                        };
+                        auto mfma = [&](auto ic) {
+                            constexpr int i = decltype(ic)::value;
+                            if constexpr (i < 2 * A) {
+                                constexpr int G = i / A, r = i % A, ks = r / 8, m = (r % 8) / 4, nt = (r % 4) / 2;
+                                constexpr int j = G * KSD + ks;
+                                if constexpr (r % 2 == 0)
+                                    S[G][m][nt] = E::mma(S[G][m][nt], q1[j % 3][m], Kr[nt][ks]);
+                                else
+                                    dP[G][m][nt] = E::mma(dP[G][m][nt], o1[j % 3][m], Vr[nt][ks]);
+                            } else {
+                                constexpr int i2 = i - 2 * A, G = i2 / B, r = i2 % B, dt = r / 4, nt = (r % 4) / 2;
+                                constexpr int u = G * DT + dt;
+                                if constexpr (r % 2 == 0)
+                                    dV[nt][dt] = E::mma(dV[nt][dt], aP[G][nt], op2(u % 3, 1));
+                                else
+                                    dK[nt][dt] = E::mma(dK[nt][dt], aS[G][nt], op2(u % 3, 0));
+                            }
+                        };
+#pragma unroll
+                        for (int G = 0; G < 2; ++G)
+#pragma unroll
+                            for (int m = 0; m < 2; ++m)
+#pragma unroll
+                                for (int nt = 0; nt < NT; ++nt) {
+#pragma unroll
+                                    for (int i = 0; i < 4; ++i) S[G][m][nt][i] = s_init[nt];
+                                    dP[G][m][nt] = zero_vec<f32x4>();
+                                }
+                        using I0 = std::integral_constant<int, 0>;
+                        using I1 = std::integral_constant<int, 1>;
+                        static_for<0, 4>([&](auto kc) { rd1(I0{}, kc); });
+                        static_for<0, 4>([&](auto kc) { rd1(I1{}, kc); });
+                        static_for<0, NMF>([&](auto ic) {
+                            constexpr int i = decltype(ic)::value;
+                            mfma(ic);
+                            // the next sub-step's copies, a part at each d step of group 0
+                            if constexpr (i < A && i % 8 == 0)
+                                issue_q_part(std::integral_constant<int, i / 8>{}, std::integral_constant<int, KSD>{},
+                                             pf_buf, q_next);
+                            // phase-1 operands: step j during step j - 2, one read per two MFMAs
+                            if constexpr (i < 2 * A - 16 && i % 2 == 0)
+                                rd1(std::integral_constant<int, i / 8 + 2>{}, std::integral_constant<int, (i % 8) / 2>{});
+                            // lse and D of a group, a step before its softmax starts
+                            if constexpr (i % 2 == 1 && i >= A - 16 && i < A - 8)
+                                rd_lse(I0{}, std::integral_constant<int, (i - (A - 16)) / 2>{});
+                            if constexpr (i % 2 == 1 && i >= 2 * A - 16 && i < 2 * A - 8)
+                                rd_lse(I1{}, std::integral_constant<int, (i - (2 * A - 16)) / 2>{});
+                            // phase-2 operands: steps 0 and 1 during the last phase-1
+                            // step, step u during step u - 2
+                            if constexpr (i >= 2 * A - 8 && i < 2 * A)
+                                rd2(std::integral_constant<int, (i - (2 * A - 8)) / 4>{}, std::integral_constant<int, i % 4>{});
+                            if constexpr (i >= 2 * A && i < 2 * A + 2 * B - 8)
+                                rd2(std::integral_constant<int, (i - 2 * A) / 4 + 2>{}, std::integral_constant<int, i % 4>{});
+                            // softmax of group 0 beside phase 1 of group 1, of group 1
+                            // beside phase 2 of group 0
+                            if constexpr (i >= A && i < 2 * A && (i - A) % (A / 8) == 0)
+                                sm_pair(I0{}, std::integral_constant<int, (i - A) / (A / 8)>{});
+                            if constexpr (i >= 2 * A && i < 2 * A + B && (i - 2 * A) % (B / 8) == 0)
+                                sm_pair(I1{}, std::integral_constant<int, (i - 2 * A) / (B / 8)>{});
+                            // dS stores beside phase 2 of group 1
+                            if constexpr (i >= 2 * A + B) {
+                                constexpr int per = 32 / B;
+                                static_for<0, per>([&](auto jc) {
+                                    st_ds(std::integral_constant<int, (i - 2 * A - B) * per + decltype(jc)::value>{});
+                                });
+                            }
+                            __builtin_amdgcn_sched_barrier(0);
+                        });
+                    } else {
+                        static_for<0, KSQ>([&](auto gqc) { phase1(gqc); });
+                        static_for<0, KSQ>([&](auto gqc) {
+                            softmax(gqc);
+                            phase2(gqc);
+                        });
+                        static_for<0, KSQ>([&](auto gqc) { store_ds(gqc); });
+                    }
                 }
 
                 // ---- R phase.  One barrier ends the last sub-step (all of dS is in
