@@ -793,9 +793,7 @@ void bwd_main_kernel(KParams p) {
                             constexpr int m = k / 4, nt = (k / 2) % 2, ip = k % 2;
 #pragma unroll
                             for (int i = 2 * ip; i < 2 * ip + 2; ++i) {
-                                const int ql = (2 * G + m) * 16 + 4 * g + i;
-                                float pv = __builtin_amdgcn_exp2f(S[G][m][nt][i] * p.scale_log2 - lsev[G][m][i] * kLog2e);
-                                if constexpr (CAUSAL) pv = (w * RW + nt * 16 + c16 <= sub * BQ + ql + diag_off) ? pv : 0.f;
+                                const float pv = __builtin_amdgcn_exp2f(S[G][m][nt][i] * p.scale_log2 - lsev[G][m][i] * kLog2e);
                                 aP[G][nt][4 * m + i] = E::from_f(pv);
                                 aS[G][nt][4 * m + i] = E::from_f(pv * (dP[G][m][nt][i] - delv[G][m][i]));
                             }
@@ -824,6 +822,10 @@ void bwd_main_kernel(KParams p) {
                                     dK[nt][dt] = E::mma(dK[nt][dt], aS[G][nt], op2(u % 3, 0));
                             }
                         };
+                        // S starts at 0, or at -inf where P must be 0: key rows
+                        // past s, and (on the diagonal tile only) keys after the
+                        // query, so the slots below need no mask
+                        const bool diag = CAUSAL && diag_off == 0;
 #pragma unroll
                         for (int G = 0; G < 2; ++G)
 #pragma unroll
@@ -834,6 +836,18 @@ void bwd_main_kernel(KParams p) {
                                     for (int i = 0; i < 4; ++i) S[G][m][nt][i] = s_init[nt];
                                     dP[G][m][nt] = zero_vec<f32x4>();
                                 }
+                        if (diag) {
+#pragma unroll
+                            for (int G = 0; G < 2; ++G)
+#pragma unroll
+                                for (int m = 0; m < 2; ++m)
+#pragma unroll
+                                    for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+                                        for (int i = 0; i < 4; ++i)
+                                            if (w * RW + nt * 16 + c16 > sub * BQ + (2 * G + m) * 16 + 4 * g + i)
+                                                S[G][m][nt][i] = -__builtin_inff();
+                        }
                         using I0 = std::integral_constant<int, 0>;
                         using I1 = std::integral_constant<int, 1>;
                         static_for<0, 4>([&](auto kc) { rd1(I0{}, kc); });
