@@ -855,10 +855,10 @@ void bwd_main_kernel(KParams p) {
                         static_for<0, NMF>([&](auto ic) {
                             constexpr int i = decltype(ic)::value;
                             mfma(ic);
-                            // the next sub-step's copies, a part at each d step of group 0
-                            if constexpr (i < A && i % 8 == 0)
-                                issue_q_part(std::integral_constant<int, i / 8>{}, std::integral_constant<int, KSD>{},
-                                             pf_buf, q_next);
+                            // the next sub-step's copies, one every DSTEP slots of phase 1
+                            constexpr int DSTEP = (2 * A - 8) / NSLOT;
+                            if constexpr (i % DSTEP == 1 && i / DSTEP < NSLOT)
+                                issue_slot(std::integral_constant<int, i / DSTEP>{}, pf_buf, q_next);
                             // phase-1 operands: step j during step j - 2, one read per two MFMAs
                             if constexpr (i < 2 * A - 16 && i % 2 == 0)
                                 rd1(std::integral_constant<int, i / 8 + 2>{}, std::integral_constant<int, (i % 8) / 2>{});
