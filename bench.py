@@ -79,6 +79,20 @@ def time_calls(tsa, pb, schedule, steps, warmup, torch):
             "ms_preprocess": pre, "ms_main": main, "ms_finalize": fin}
 
 
+def flag_wait_stats(tsa, pb, schedule, torch):
+    """One extra, untimed call with the kernel's wait counters on: the share of
+    work-item cycles that work groups spent polling dQ flags for their turn."""
+    out = [torch.empty_like(pb.q) for _ in range(3)]
+    tsa.attn_bwd_set_wait_stats(True)
+    try:
+        pb.run(schedule, out=out)
+        wait, item, polls = tsa.attn_bwd_get_wait_stats()
+    finally:
+        tsa.attn_bwd_set_wait_stats(False)
+    return {"wait_cycles": wait, "item_cycles": item, "polls": polls,
+            "fraction": round(wait / item, 5) if item else None}
+
+
 def cpu_baseline(pb, heads, flops_per_head):
     """The fp64 oracle backward (as it stands) on `heads` heads of the same
     workload, using the O and lse of the forward pass; backward stage only."""
@@ -110,7 +124,7 @@ def main():
     ap.add_argument("--schedule", default=None, help="default: shift (full) / descending (causal)")
     ap.add_argument("--compare", default="naive,atomic",
                     help="comma list of schedules also timed for context ('none' for none)")
-    ap.add_argument("--cpu-heads", type=int, default=4, help="heads in the CPU oracle sample (0: skip)")
+    ap.add_argument("--cpu-heads", type=int, default=16, help="heads in the CPU oracle sample (0: skip)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of MIB MiB five times (scales the HBM "
                          "traffic counters of a profiler run) and exit")
@@ -170,6 +184,9 @@ def main():
                 "kernel": "bwd_main_kernel",
                 "algorithmic_flop_per_launch": flops}
 
+    waits = flag_wait_stats(tsa, pb, schedule, torch)
+    log(f"dQ flag waits: {waits['fraction']} of work-item cycles ({waits['polls']} polls)")
+
     cpu = None
     if args.cpu_heads > 0:
         log(f"timing the CPU oracle on {args.cpu_heads} head(s)")
@@ -198,6 +215,7 @@ def main():
                       "finalize": round(res["ms_finalize"], 4)},
         "compare": extra,
         "roofline": roofline,
+        "flag_wait": waits,
         "cpu_baseline": cpu,
     }
     if "atomic" in extra:
