@@ -184,6 +184,39 @@ int attn_sched_min_workers(int n, int causal, int schedule);
 int attn_dagsim(int n, int causal, int schedule, int heads, int workers, int placement,
                 double c, double r, double* makespan, double* wait_time, double* busy_time);
 
+/* ------------------------------------------------------------------------
+ * Schedule selection (host).  The review page ("If this is right") calls the
+ * schedules complementary and has an implementation pick one per
+ * configuration; this picks, among NAIVE, DESCENDING, SHIFT and
+ * SYMMETRIC_SHIFT, the one with the smallest simulated makespan
+ * (attn_dagsim, placement 1) for `heads` heads of n tiles on `workers`
+ * resident work groups with task costs c and r.  Schedules that the shape
+ * does not admit (SYMMETRIC_SHIFT with odd n under the causal mask) or that
+ * need more resident work groups than `workers` are skipped; ties go to the
+ * lower schedule id.  Outputs (may be NULL): the schedule and its makespan.
+ * Returns ATTN_OK, ATTN_ERR_INVALID_ARG, or ATTN_ERR_UNSUPPORTED when no
+ * schedule qualifies.
+ * ------------------------------------------------------------------------ */
+int attn_sched_select(int n, int causal, int heads, int workers, double c, double r, int* schedule,
+                      double* makespan);
+
+/* ------------------------------------------------------------------------
+ * Cost calibration of the DAG model (host).  The review page ("What would
+ * settle it") asks whether measured kernels reach the model's bound
+ * m*n*(c+r); this fits the model's two costs to measurements.  Sample k is
+ * a launch of `heads[k]` heads of n[k] tiles with mask causal[k] and
+ * schedule schedule[k] on workers[k] resident work groups that took
+ * measured[k] (> 0, any time unit).  Returns c and r (per task, same unit)
+ * minimising the RMS relative error between the simulated makespans
+ * (attn_dagsim, placement 1) and the measurements, and that error.  The
+ * search runs over r/c in [1e-4, 1e2]: a log grid, then golden-section
+ * refinement.  Arrays are host memory of `count` elements, read only.
+ * Returns ATTN_OK, ATTN_ERR_INVALID_ARG, or ATTN_ERR_UNSUPPORTED when a
+ * sample cannot be simulated (unsupported schedule, deadlock).
+ * ------------------------------------------------------------------------ */
+int attn_sched_fit(int count, const int* n, const int* causal, const int* schedule, const int* heads,
+                   const int* workers, const double* measured, double* c, double* r, double* rms);
+
 #ifdef __cplusplus
 }
 #endif

@@ -106,3 +106,79 @@ def test_schedule_argument_errors():
         tsa.attn_sched_size(4, False, 9)
     with pytest.raises(tsa.AttnError):
         tsa.attn_dagsim(4, False, "naive", 1, 0, 0, 1.0, 1.0)
+
+
+# ---------------------------------------------------------------- selection
+@pytest.mark.parametrize("m,n", [(1, 4), (2, 8), (4, 16)])
+@pytest.mark.parametrize("c,r", [(1, 1), (3, 1), (1, 0.25)])
+def test_select_full_mask_picks_shift_at_the_bound(m, n, c, r):
+    name, t = tsa.attn_sched_select(n, False, m, n, c, r)
+    assert name == "shift"
+    assert t == float(dag.closed_form_full(m, n, Fraction(c), Fraction(r)))
+
+
+@pytest.mark.parametrize("m,n", [(2, 4), (2, 8), (4, 16)])
+@pytest.mark.parametrize("c,r", [(1, 1), (3, 1), (1, 0.25)])
+def test_select_causal_picks_symmetric_shift_at_the_bound(m, n, c, r):
+    """With at least two heads the workers Symmetric Shift leaves free are
+    used by the next head, and it reaches m(n+1)(c+r)/2."""
+    name, t = tsa.attn_sched_select(n, True, m, n, c, r)
+    assert name == "symmetric_shift"
+    assert t == float(dag.closed_form_causal(m, n, Fraction(c), Fraction(r)))
+
+
+def test_select_causal_single_head_prefers_descending():
+    """One head on n workers: the fold leaves half the workers idle, and
+    Descending (tied with the causal Shift; the lower id wins) is faster."""
+    name, t = tsa.attn_sched_select(8, True, 1, 8, 1.0, 1.0)
+    assert name == "descending"
+    assert t == tsa.attn_dagsim(8, True, "descending", 1, 8, 1, 1.0, 1.0)[0]
+    assert t < tsa.attn_dagsim(8, True, "symmetric_shift", 1, 8, 1, 1.0, 1.0)[0]
+
+
+def test_select_skips_schedules_that_cannot_run():
+    # Shift needs n resident workers; with fewer the baseline orders remain
+    name, t = tsa.attn_sched_select(8, False, 2, 4, 1.0, 1.0)
+    assert name in ("naive", "descending")
+    assert t == tsa.attn_dagsim(8, False, name, 2, 4, 1, 1.0, 1.0)[0]
+    # the fold needs an even tile count
+    name, _ = tsa.attn_sched_select(5, True, 4, 5, 1.0, 1.0)
+    assert name != "symmetric_shift"
+    with pytest.raises(tsa.AttnError):
+        tsa.attn_sched_select(0, False, 1, 1, 1.0, 1.0)
+
+
+# ---------------------------------------------------------------- calibration
+def _samples(c, r, scale=None):
+    cases = [(8, False, "shift", 2, 8), (8, False, "naive", 2, 8), (8, True, "descending", 2, 8),
+             (8, True, "symmetric_shift", 2, 8), (16, True, "naive", 3, 16)]
+    out = []
+    for k, (n, causal, name, heads, workers) in enumerate(cases):
+        t = tsa.attn_dagsim(n, causal, name, heads, workers, 1, c, r)[0]
+        out.append((n, causal, name, heads, workers, t * (scale[k] if scale else 1.0)))
+    return out
+
+
+@pytest.mark.parametrize("c,r", [(2.0, 0.7), (1.0, 1.0), (0.3, 2.5), (5.0, 0.05)])
+def test_fit_recovers_the_costs_of_simulated_timings(c, r):
+    fc, fr, rms = tsa.attn_sched_fit(_samples(c, r))
+    assert fc == pytest.approx(c, rel=1e-5)
+    assert fr == pytest.approx(r, rel=1e-4)
+    assert rms < 1e-6
+
+
+def test_fit_tolerates_noise():
+    noise = [1.02, 0.98, 1.01, 0.99, 1.015]
+    fc, fr, rms = tsa.attn_sched_fit(_samples(2.0, 0.7, noise))
+    assert fc == pytest.approx(2.0, rel=0.1)
+    assert fr == pytest.approx(0.7, rel=0.25)
+    assert rms < 0.03
+
+
+def test_fit_argument_errors():
+    with pytest.raises(tsa.AttnError):
+        tsa.attn_sched_fit([])
+    with pytest.raises(tsa.AttnError):
+        tsa.attn_sched_fit([(8, False, "shift", 1, 8, 0.0)])
+    with pytest.raises(tsa.AttnError):  # Shift on fewer workers than it needs deadlocks
+        tsa.attn_sched_fit([(8, False, "shift", 1, 4, 1.0)])

@@ -27,7 +27,7 @@ EXPORTS = ("attn_bwd_deterministic", "attn_bwd_deterministic_ex", "attn_bwd_work
            "attn_bwd_query_status", "attn_bwd_last_error", "attn_bwd_tile_size",
            "attn_bwd_set_timing", "attn_bwd_get_kernel_times", "attn_bwd_set_wait_stats",
            "attn_bwd_get_wait_stats", "attn_sched_size", "attn_sched_get",
-           "attn_sched_min_workers", "attn_dagsim")
+           "attn_sched_min_workers", "attn_dagsim", "attn_sched_select", "attn_sched_fit")
 
 
 class AttnError(RuntimeError):
@@ -43,7 +43,7 @@ def _load():
     import torch  # noqa: F401
     if not os.path.exists(LIB_PATH):
         raise ImportError(f"{LIB_PATH} is missing: build it with "
-                          "`python -m tile_scheduling_attn_amd.build`")
+                          "`python tile_scheduling_attn_amd/build.py`")
     lib = ctypes.CDLL(LIB_PATH)
     vp, i, f, d, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_double, ctypes.c_size_t
     ip, dp = ctypes.POINTER(ctypes.c_int), ctypes.POINTER(ctypes.c_double)
@@ -77,6 +77,10 @@ def _load():
     lib.attn_sched_min_workers.restype = i
     lib.attn_dagsim.argtypes = [i, i, i, i, i, i, d, d, dp, dp, dp]
     lib.attn_dagsim.restype = i
+    lib.attn_sched_select.argtypes = [i, i, i, i, d, d, ip, dp]
+    lib.attn_sched_select.restype = i
+    lib.attn_sched_fit.argtypes = [i, ip, ip, ip, ip, ip, dp, dp, dp, dp]
+    lib.attn_sched_fit.restype = i
     return lib
 
 
@@ -194,6 +198,31 @@ def attn_dagsim(n, causal, schedule, heads, workers, placement, c, r):
                            float(c), float(r), ctypes.byref(m), ctypes.byref(w), ctypes.byref(b_)),
            "attn_dagsim")
     return m.value, w.value, b_.value
+
+
+def attn_sched_select(n, causal, heads, workers, c, r):
+    """Returns (schedule name, simulated makespan)."""
+    sch, ms = ctypes.c_int(), ctypes.c_double()
+    _check(lib.attn_sched_select(n, int(causal), heads, workers, float(c), float(r), ctypes.byref(sch),
+                                 ctypes.byref(ms)), "attn_sched_select")
+    name = {v: k for k, v in SCHEDULES.items()}[sch.value]
+    return name, ms.value
+
+
+def attn_sched_fit(samples):
+    """samples: iterable of (n, causal, schedule, heads, workers, measured).
+    Returns (c, r, rms relative error)."""
+    samples = list(samples)
+    k = len(samples)
+    I = ctypes.c_int * k
+    cols = [I(*[int(s[0]) for s in samples]), I(*[int(bool(s[1])) for s in samples]),
+            I(*[_sched_id(s[2]) for s in samples]), I(*[int(s[3]) for s in samples]),
+            I(*[int(s[4]) for s in samples])]
+    meas = (ctypes.c_double * k)(*[float(s[5]) for s in samples])
+    c, r, e = ctypes.c_double(), ctypes.c_double(), ctypes.c_double()
+    _check(lib.attn_sched_fit(k, *cols, meas, ctypes.byref(c), ctypes.byref(r), ctypes.byref(e)),
+           "attn_sched_fit")
+    return c.value, r.value, e.value
 
 
 # ---------------------------------------------------------------------------

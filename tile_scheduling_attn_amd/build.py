@@ -1,5 +1,6 @@
 """Build libattn_bwd.so (HIP kernels for gfx950 + host schedule/simulator +
-C ABI) in-tree with hipcc.  `python -m tile_scheduling_attn_amd.build`."""
+C ABI) in-tree with hipcc.  `python tile_scheduling_attn_amd/build.py` (run as a
+file: importing the package loads the library this builds)."""
 from __future__ import annotations
 
 import os

@@ -1,0 +1,104 @@
+"""Calibrate the DAG model's task costs on this GPU, then pick schedules.
+
+    python tile_scheduling_attn_amd/calibrate.py [--steps K]
+
+Times the main kernel of the backward for every (workload, mask, schedule)
+below with the library's own launch-stream events, fits the model's compute
+and reduction costs c and r per head dimension with `attn_sched_fit` (the
+DAG of the review page's "What carries the argument", with the kernel's
+ticket queue as placement), and prints one JSON document: the fitted costs,
+measured against simulated makespan for every sample, and the schedule
+`attn_sched_select` picks for each shape.  Inputs are seeded N(0, 1) Q, K, V,
+dO with O and lse of the right scale; the kernel's running time does not
+depend on the values.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, os.path.dirname(HERE))
+
+# (workload name, causal, schedules timed)
+PLAN = [
+    ("s2k_d64_causal", True, ("naive", "descending", "shift", "symmetric_shift")),
+    ("s8k_d128_full", False, ("naive", "descending", "shift")),
+    ("s8k_d128_causal", True, ("naive", "descending", "shift", "symmetric_shift")),
+    ("s16k_d128", False, ("naive", "shift")),
+    ("s16k_d128", True, ("descending", "symmetric_shift")),
+]
+
+
+def inputs(wl, torch):
+    g = torch.Generator(device="cuda").manual_seed(wl.seed)
+    shape = (wl.b, wl.h, wl.s, wl.d)
+    dt = torch.bfloat16 if wl.dtype == "bf16" else torch.float32
+    q, k, v, o, do = (torch.randn(shape, generator=g, device="cuda", dtype=torch.float32).to(dt) for _ in range(5))
+    # lse of the scale a softmax over s keys has: log(s) plus a small spread
+    lse = (math.log(wl.s) + 0.1 * torch.randn(shape[:3], generator=g, device="cuda")).contiguous()
+    return q, k, v, o, do, lse
+
+
+def time_main(tsa, args, schedule, causal, steps, torch):
+    q, k, v, o, do, lse = args
+    out = [torch.empty_like(q) for _ in range(3)]
+    for _ in range(2):
+        tsa.backward(q, k, v, o, do, lse, causal, schedule, out=out)
+    torch.cuda.synchronize()
+    tsa.attn_bwd_set_timing(True)
+    for _ in range(steps):
+        tsa.backward(q, k, v, o, do, lse, causal, schedule, out=out)
+    torch.cuda.synchronize()
+    tsa.attn_bwd_set_timing(False)
+    if tsa.attn_bwd_query_status() != 0:
+        raise RuntimeError(tsa.last_error())
+    return tsa.attn_bwd_get_kernel_times()[1]
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__)
+    ap.add_argument("--steps", type=int, default=5)
+    a = ap.parse_args()
+    import torch
+    import tile_scheduling_attn_amd as tsa
+    import workloads
+
+    workers = torch.cuda.get_device_properties(0).multi_processor_count  # one work group per CU
+    samples = {}  # d -> list of (n, causal, schedule, heads, workers, ms, workload)
+    for name, causal, scheds in PLAN:
+        wl = workloads.WORKLOADS[name]
+        tile = tsa.attn_bwd_tile_size(wl.dtype)
+        n = -(-wl.s // tile)
+        args = inputs(wl, torch)
+        for sched in scheds:
+            ms = time_main(tsa, args, sched, causal, a.steps, torch)
+            print(f"{name} causal={causal} {sched}: {ms:.4f} ms", file=sys.stderr, flush=True)
+            samples.setdefault(wl.d, []).append((n, causal, sched, wl.b * wl.h, workers, ms, name))
+        del args
+        torch.cuda.empty_cache()
+
+    report = {"workers": workers, "fits": {}}
+    for d, ss in samples.items():
+        c, r, rms = tsa.attn_sched_fit([s[:6] for s in ss])
+        rows = []
+        for n, causal, sched, heads, w, ms, name in ss:
+            pred = tsa.attn_dagsim(n, causal, sched, heads, w, 1, c, r)[0]
+            rows.append({"workload": name, "causal": causal, "schedule": sched, "measured_ms": round(ms, 4),
+                         "model_ms": round(pred, 4), "ratio": round(ms / pred, 4)})
+        picks = {}
+        for n, causal, _, heads, w, _, name in ss:
+            key = f"{name} {'causal' if causal else 'full'}"
+            if key not in picks:
+                sel, t = tsa.attn_sched_select(n, causal, heads, w, c, r)
+                picks[key] = {"schedule": sel, "model_ms": round(t, 4)}
+        report["fits"][f"d{d}"] = {"c_us": round(c * 1e3, 4), "r_us": round(r * 1e3, 4),
+                                   "rms_rel_err": round(rms, 4), "samples": rows, "selected": picks}
+    print(json.dumps(report, indent=1))
+
+
+if __name__ == "__main__":
+    main()

@@ -22,6 +22,7 @@
 #include "internal.h"
 
 #include <algorithm>
+#include <cmath>
 #include <cstring>
 #include <queue>
 #include <vector>
@@ -293,5 +294,117 @@ extern "C" int attn_dagsim(int n, int causal, int schedule, int heads, int worke
     rc = attn::simulate(sc, heads, workers, placement, c, r, makespan, wait_time, busy_time);
     if (rc == ATTN_ERR_DEADLOCK) return attn::fail(rc, "attn_dagsim: the schedule deadlocks with this many workers");
     if (rc != ATTN_OK) return attn::fail(rc, "attn_dagsim: invalid arguments");
+    return ATTN_OK;
+}
+
+// ---------------------------------------------------------------------------
+// Schedule selection and cost calibration on the DAG model
+// ---------------------------------------------------------------------------
+extern "C" int attn_sched_select(int n, int causal, int heads, int workers, double c, double r,
+                                 int* schedule, double* makespan) {
+    if (n <= 0 || heads <= 0 || workers <= 0 || !(c >= 0) || !(r >= 0))
+        return attn::fail(ATTN_ERR_INVALID_ARG, "attn_sched_select: invalid arguments");
+    int best = -1;
+    double best_t = 0;
+    for (int s : {ATTN_SCHED_NAIVE, ATTN_SCHED_DESCENDING, ATTN_SCHED_SHIFT, ATTN_SCHED_SYMMETRIC_SHIFT}) {
+        attn::Schedule sc;
+        if (attn::build_schedule(n, causal != 0, s, sc) != ATTN_OK) continue;  // e.g. odd n, fold
+        if (attn::min_workers(sc) > workers) continue;                          // cannot be co-scheduled
+        double t = 0;
+        if (attn::simulate(sc, heads, workers, 1, c, r, &t, nullptr, nullptr) != ATTN_OK) continue;
+        if (best < 0 || t < best_t * (1 - 1e-12)) {
+            best = s;
+            best_t = t;
+        }
+    }
+    if (best < 0) return attn::fail(ATTN_ERR_UNSUPPORTED, "attn_sched_select: no schedule runs on this many workers");
+    if (schedule) *schedule = best;
+    if (makespan) *makespan = best_t;
+    return ATTN_OK;
+}
+
+namespace {
+// Simulated makespans of every sample with compute cost 1 and reduction
+// cost rho; false when a sample cannot be simulated.
+bool unit_makespans(int count, const int* n, const int* causal, const int* schedule, const int* heads,
+                    const int* workers, double rho, std::vector<double>& m) {
+    m.resize(count);
+    for (int k = 0; k < count; ++k) {
+        attn::Schedule sc;
+        if (attn::build_schedule(n[k], causal[k] != 0, schedule[k], sc) != ATTN_OK) return false;
+        if (attn::simulate(sc, heads[k], workers[k], 1, 1.0, rho, &m[k], nullptr, nullptr) != ATTN_OK) return false;
+    }
+    return true;
+}
+
+// For fixed rho the makespan is proportional to c: the c minimising the
+// relative squared error sum (c m_k / T_k - 1)^2 is sum(x) / sum(x^2) with
+// x_k = m_k / T_k.  Returns the RMS relative error at that c.
+double best_scale(const std::vector<double>& m, const double* measured, double* c) {
+    double sx = 0, sxx = 0;
+    for (size_t k = 0; k < m.size(); ++k) {
+        const double x = m[k] / measured[k];
+        sx += x;
+        sxx += x * x;
+    }
+    *c = sxx > 0 ? sx / sxx : 0;
+    double e = 0;
+    for (size_t k = 0; k < m.size(); ++k) {
+        const double d = *c * m[k] / measured[k] - 1;
+        e += d * d;
+    }
+    return std::sqrt(e / (double)m.size());
+}
+}  // namespace
+
+extern "C" int attn_sched_fit(int count, const int* n, const int* causal, const int* schedule, const int* heads,
+                              const int* workers, const double* measured, double* c, double* r, double* rms) {
+    if (count <= 0 || !n || !causal || !schedule || !heads || !workers || !measured)
+        return attn::fail(ATTN_ERR_INVALID_ARG, "attn_sched_fit: invalid arguments");
+    for (int k = 0; k < count; ++k)
+        if (!(measured[k] > 0) || n[k] <= 0 || heads[k] <= 0 || workers[k] <= 0)
+            return attn::fail(ATTN_ERR_INVALID_ARG, "attn_sched_fit: invalid sample");
+    // coarse search over rho = r / c on a log grid (1e-4 .. 1e2), then a
+    // golden-section refinement of log(rho) around the best grid point
+    std::vector<double> m;
+    auto err_at = [&](double lr, double* cc) {
+        if (!unit_makespans(count, n, causal, schedule, heads, workers, std::exp(lr), m)) return -1.0;
+        return best_scale(m, measured, cc);
+    };
+    const double lo = std::log(1e-4), hi = std::log(1e2);
+    const int steps = 60;
+    double best_lr = lo, best_e = -1, cc = 0;
+    for (int i = 0; i <= steps; ++i) {
+        const double lr = lo + (hi - lo) * i / steps;
+        const double e = err_at(lr, &cc);
+        if (e < 0) return attn::fail(ATTN_ERR_UNSUPPORTED, "attn_sched_fit: a sample cannot be simulated");
+        if (best_e < 0 || e < best_e) {
+            best_e = e;
+            best_lr = lr;
+        }
+    }
+    const double h = (hi - lo) / steps, g = 0.6180339887498949;
+    double a = best_lr - h, b = best_lr + h;
+    double x1 = b - g * (b - a), x2 = a + g * (b - a);
+    double f1 = err_at(x1, &cc), f2 = err_at(x2, &cc);
+    for (int it = 0; it < 40; ++it) {
+        if (f1 < f2) {
+            b = x2; x2 = x1; f2 = f1; x1 = b - g * (b - a); f1 = err_at(x1, &cc);
+        } else {
+            a = x1; x1 = x2; f1 = f2; x2 = a + g * (b - a); f2 = err_at(x2, &cc);
+        }
+    }
+    double lr = 0.5 * (a + b);
+    double e = err_at(lr, &cc);
+    double cg = 0;
+    const double eg = err_at(best_lr, &cg);  // keep the grid point if the refinement did not help
+    if (eg <= e) {
+        lr = best_lr;
+        e = eg;
+        cc = cg;
+    }
+    if (c) *c = cc;
+    if (r) *r = cc * std::exp(lr);
+    if (rms) *rms = e;
     return ATTN_OK;
 }
