@@ -149,30 +149,56 @@ def test_select_skips_schedules_that_cannot_run():
 
 
 # ---------------------------------------------------------------- calibration
-def _samples(c, r, scale=None):
+def _samples(c, r, e=0.0, scale=None):
     cases = [(8, False, "shift", 2, 8), (8, False, "naive", 2, 8), (8, True, "descending", 2, 8),
              (8, True, "symmetric_shift", 2, 8), (16, True, "naive", 3, 16)]
     out = []
     for k, (n, causal, name, heads, workers) in enumerate(cases):
-        t = tsa.attn_dagsim(n, causal, name, heads, workers, 1, c, r)[0]
+        t = tsa.attn_dagsim_edge(n, causal, name, heads, workers, 1, c, r, e)[0]
         out.append((n, causal, name, heads, workers, t * (scale[k] if scale else 1.0)))
     return out
 
 
-@pytest.mark.parametrize("c,r", [(2.0, 0.7), (1.0, 1.0), (0.3, 2.5), (5.0, 0.05)])
-def test_fit_recovers_the_costs_of_simulated_timings(c, r):
-    fc, fr, rms = tsa.attn_sched_fit(_samples(c, r))
-    assert fc == pytest.approx(c, rel=1e-5)
-    assert fr == pytest.approx(r, rel=1e-4)
-    assert rms < 1e-6
+@pytest.mark.parametrize("c,r,e", [(2.0, 0.7, 0.0), (1.0, 1.0, 0.0), (0.3, 2.5, 0.0), (5.0, 0.05, 0.0),
+                                   (2.0, 0.7, 0.4), (1.0, 0.5, 1.5)])
+def test_fit_reproduces_simulated_timings(c, r, e):
+    """Timings pin down c + r (a worker's time per task) and r + e (a link of
+    a reduction chain), not the three costs one by one, so the check is on
+    what the fitted model predicts: every sample, to the fit's tolerance."""
+    samples = _samples(c, r, e)
+    fc, fr, fe, rms = tsa.attn_sched_fit(samples)
+    assert rms < 1e-4
+    assert fc + fr == pytest.approx(c + r, rel=1e-3)
+    assert fr + fe == pytest.approx(r + e, rel=1e-2, abs=1e-3)
+    for (n, causal, name, heads, workers, t) in samples:
+        assert tsa.attn_dagsim_edge(n, causal, name, heads, workers, 1, fc, fr, fe)[0] == pytest.approx(t, rel=1e-3)
 
 
 def test_fit_tolerates_noise():
     noise = [1.02, 0.98, 1.01, 0.99, 1.015]
-    fc, fr, rms = tsa.attn_sched_fit(_samples(2.0, 0.7, noise))
+    fc, fr, fe, rms = tsa.attn_sched_fit(_samples(2.0, 0.7, 0.0, noise))
     assert fc == pytest.approx(2.0, rel=0.1)
-    assert fr == pytest.approx(0.7, rel=0.25)
     assert rms < 0.03
+    for (n, causal, name, heads, workers, t) in _samples(2.0, 0.7, 0.0, noise):
+        pred = tsa.attn_dagsim_edge(n, causal, name, heads, workers, 1, fc, fr, fe)[0]
+        assert pred == pytest.approx(t, rel=0.06)
+
+
+def test_edge_cost_of_zero_is_the_pages_model():
+    for name, causal in (("naive", False), ("shift", False), ("descending", True), ("symmetric_shift", True)):
+        assert tsa.attn_dagsim_edge(8, causal, name, 2, 8, 1, 1.5, 0.5, 0.0) == \
+            tsa.attn_dagsim(8, causal, name, 2, 8, 1, 1.5, 0.5)
+
+
+def test_edge_cost_delays_the_serial_chain_but_not_shift():
+    """Naive full: every contributor waits on the previous one, so each edge
+    adds to the critical path; Shift staggers the contributors by a whole
+    task, so an edge shorter than the compute phase costs nothing."""
+    c, r = 1.0, 0.5
+    base = tsa.attn_dagsim(8, False, "naive", 1, 8, 1, c, r)[0]
+    assert tsa.attn_dagsim_edge(8, False, "naive", 1, 8, 1, c, r, 0.25)[0] > base
+    assert tsa.attn_dagsim_edge(8, False, "shift", 1, 8, 1, c, r, 0.25)[0] == \
+        float(dag.closed_form_full(1, 8, Fraction(c), Fraction(r)))
 
 
 def test_fit_argument_errors():

@@ -27,7 +27,8 @@ EXPORTS = ("attn_bwd_deterministic", "attn_bwd_deterministic_ex", "attn_bwd_work
            "attn_bwd_query_status", "attn_bwd_last_error", "attn_bwd_tile_size",
            "attn_bwd_set_timing", "attn_bwd_get_kernel_times", "attn_bwd_set_wait_stats",
            "attn_bwd_get_wait_stats", "attn_sched_size", "attn_sched_get",
-           "attn_sched_min_workers", "attn_dagsim", "attn_sched_select", "attn_sched_fit")
+           "attn_sched_min_workers", "attn_dagsim", "attn_dagsim_edge", "attn_sched_select",
+           "attn_sched_fit")
 
 
 class AttnError(RuntimeError):
@@ -77,9 +78,11 @@ def _load():
     lib.attn_sched_min_workers.restype = i
     lib.attn_dagsim.argtypes = [i, i, i, i, i, i, d, d, dp, dp, dp]
     lib.attn_dagsim.restype = i
-    lib.attn_sched_select.argtypes = [i, i, i, i, d, d, ip, dp]
+    lib.attn_dagsim_edge.argtypes = [i, i, i, i, i, i, d, d, d, dp, dp, dp]
+    lib.attn_dagsim_edge.restype = i
+    lib.attn_sched_select.argtypes = [i, i, i, i, d, d, d, ip, dp]
     lib.attn_sched_select.restype = i
-    lib.attn_sched_fit.argtypes = [i, ip, ip, ip, ip, ip, dp, dp, dp, dp]
+    lib.attn_sched_fit.argtypes = [i, ip, ip, ip, ip, ip, dp, dp, dp, dp, dp]
     lib.attn_sched_fit.restype = i
     return lib
 
@@ -200,18 +203,27 @@ def attn_dagsim(n, causal, schedule, heads, workers, placement, c, r):
     return m.value, w.value, b_.value
 
 
-def attn_sched_select(n, causal, heads, workers, c, r):
+def attn_dagsim_edge(n, causal, schedule, heads, workers, placement, c, r, e):
+    """Returns (makespan, wait_time, busy_time); raises AttnError on deadlock."""
+    m, w, b_ = ctypes.c_double(), ctypes.c_double(), ctypes.c_double()
+    _check(lib.attn_dagsim_edge(n, int(causal), _sched_id(schedule), heads, workers, placement, float(c),
+                                float(r), float(e), ctypes.byref(m), ctypes.byref(w), ctypes.byref(b_)),
+           "attn_dagsim_edge")
+    return m.value, w.value, b_.value
+
+
+def attn_sched_select(n, causal, heads, workers, c, r, e=0.0):
     """Returns (schedule name, simulated makespan)."""
     sch, ms = ctypes.c_int(), ctypes.c_double()
-    _check(lib.attn_sched_select(n, int(causal), heads, workers, float(c), float(r), ctypes.byref(sch),
-                                 ctypes.byref(ms)), "attn_sched_select")
+    _check(lib.attn_sched_select(n, int(causal), heads, workers, float(c), float(r), float(e),
+                                 ctypes.byref(sch), ctypes.byref(ms)), "attn_sched_select")
     name = {v: k for k, v in SCHEDULES.items()}[sch.value]
     return name, ms.value
 
 
 def attn_sched_fit(samples):
     """samples: iterable of (n, causal, schedule, heads, workers, measured).
-    Returns (c, r, rms relative error)."""
+    Returns (c, r, e, rms relative error)."""
     samples = list(samples)
     k = len(samples)
     I = ctypes.c_int * k
@@ -219,10 +231,10 @@ def attn_sched_fit(samples):
             I(*[_sched_id(s[2]) for s in samples]), I(*[int(s[3]) for s in samples]),
             I(*[int(s[4]) for s in samples])]
     meas = (ctypes.c_double * k)(*[float(s[5]) for s in samples])
-    c, r, e = ctypes.c_double(), ctypes.c_double(), ctypes.c_double()
-    _check(lib.attn_sched_fit(k, *cols, meas, ctypes.byref(c), ctypes.byref(r), ctypes.byref(e)),
-           "attn_sched_fit")
-    return c.value, r.value, e.value
+    c, r, e, rms = ctypes.c_double(), ctypes.c_double(), ctypes.c_double(), ctypes.c_double()
+    _check(lib.attn_sched_fit(k, *cols, meas, ctypes.byref(c), ctypes.byref(r), ctypes.byref(e),
+                              ctypes.byref(rms)), "attn_sched_fit")
+    return c.value, r.value, e.value, rms.value
 
 
 # ---------------------------------------------------------------------------

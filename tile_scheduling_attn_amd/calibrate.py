@@ -4,10 +4,12 @@
 
 Times the main kernel of the backward for every (workload, mask, schedule)
 below with the library's own launch-stream events, fits the model's compute
-and reduction costs c and r per head dimension with `attn_sched_fit` (the
-DAG of the review page's "What carries the argument", with the kernel's
-ticket queue as placement), and prints one JSON document: the fitted costs,
-measured against simulated makespan for every sample, and the schedule
+and reduction costs c and r and the edge cost e (a release reaching the next
+contributor) per head dimension with `attn_sched_fit` (the DAG of the review
+page's "What carries the argument", with the kernel's ticket queue as
+placement), fits the pages' model (e = 0) too, and prints one JSON document:
+the fitted costs, measured against simulated makespan for every sample, and
+the schedule
 `attn_sched_select` picks for each shape.  Inputs are seeded N(0, 1) Q, K, V,
 dO with O and lse of the right scale; the kernel's running time does not
 depend on the values.
@@ -59,6 +61,19 @@ def time_main(tsa, args, schedule, causal, steps, torch):
     return tsa.attn_bwd_get_kernel_times()[1]
 
 
+def zero_edge_fit(tsa, ss):
+    """The pages' model (e = 0): the best r/c on a log grid, c in closed form."""
+    best = None
+    for i in range(121):
+        rho = 10 ** (-4 + 6 * i / 120)
+        x = [tsa.attn_dagsim(n, causal, sched, heads, w, 1, 1.0, rho)[0] / ms for n, causal, sched, heads, w, ms, _ in ss]
+        c = sum(x) / sum(v * v for v in x)
+        err = math.sqrt(sum((c * v - 1) ** 2 for v in x) / len(x))
+        if best is None or err < best[3]:
+            best = (c, c * rho, 0.0, err)
+    return best
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__)
     ap.add_argument("--steps", type=int, default=5)
@@ -83,20 +98,26 @@ def main():
 
     report = {"workers": workers, "fits": {}}
     for d, ss in samples.items():
-        c, r, rms = tsa.attn_sched_fit([s[:6] for s in ss])
+        print(f"fitting d={d} ({len(ss)} samples)", file=sys.stderr, flush=True)
+        c, r, e, rms = tsa.attn_sched_fit([s[:6] for s in ss])
+        c0, r0, _, rms0 = zero_edge_fit(tsa, ss)
         rows = []
         for n, causal, sched, heads, w, ms, name in ss:
-            pred = tsa.attn_dagsim(n, causal, sched, heads, w, 1, c, r)[0]
+            pred = tsa.attn_dagsim_edge(n, causal, sched, heads, w, 1, c, r, e)[0]
+            pred0 = tsa.attn_dagsim(n, causal, sched, heads, w, 1, c0, r0)[0]
             rows.append({"workload": name, "causal": causal, "schedule": sched, "measured_ms": round(ms, 4),
-                         "model_ms": round(pred, 4), "ratio": round(ms / pred, 4)})
+                         "model_ms": round(pred, 4), "model_e0_ms": round(pred0, 4)})
         picks = {}
         for n, causal, _, heads, w, _, name in ss:
             key = f"{name} {'causal' if causal else 'full'}"
             if key not in picks:
-                sel, t = tsa.attn_sched_select(n, causal, heads, w, c, r)
+                sel, t = tsa.attn_sched_select(n, causal, heads, w, c, r, e)
                 picks[key] = {"schedule": sel, "model_ms": round(t, 4)}
-        report["fits"][f"d{d}"] = {"c_us": round(c * 1e3, 4), "r_us": round(r * 1e3, 4),
-                                   "rms_rel_err": round(rms, 4), "samples": rows, "selected": picks}
+        report["fits"][f"d{d}"] = {"c_us": round(c * 1e3, 4), "r_us": round(r * 1e3, 4), "e_us": round(e * 1e3, 4),
+                                   "rms_rel_err": round(rms, 4),
+                                   "e0": {"c_us": round(c0 * 1e3, 4), "r_us": round(r0 * 1e3, 4),
+                                          "rms_rel_err": round(rms0, 4)},
+                                   "samples": rows, "selected": picks}
     print(json.dumps(report, indent=1))
 
 

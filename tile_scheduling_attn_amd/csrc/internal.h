@@ -20,7 +20,7 @@ struct Schedule {
 
 int build_schedule(int n, bool causal, int schedule, Schedule& out);
 int min_workers(const Schedule& sc);
-int simulate(const Schedule& sc, int heads, int workers, int placement, double c, double r,
+int simulate(const Schedule& sc, int heads, int workers, int placement, double c, double r, double e,
              double* makespan, double* wait_time, double* busy_time);
 
 // Records `msg` as the calling thread's last error and returns `code`.

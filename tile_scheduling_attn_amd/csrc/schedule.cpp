@@ -126,9 +126,9 @@ int min_workers(const Schedule& sc) {
 
 // Discrete-event simulation of `heads` copies of the schedule on `workers`
 // workers.  Events are processed in (time, worker) order.
-int simulate(const Schedule& sc, int heads, int workers, int placement, double c, double r,
+int simulate(const Schedule& sc, int heads, int workers, int placement, double c, double r, double e,
              double* makespan, double* wait_time, double* busy_time) {
-    if (heads < 0 || workers <= 0 || c < 0 || r < 0 || (placement != 0 && placement != 1))
+    if (heads < 0 || workers <= 0 || c < 0 || r < 0 || e < 0 || (placement != 0 && placement != 1))
         return ATTN_ERR_INVALID_ARG;
     const int n = sc.n, items_per_head = sc.num_items();
     const long long total_items = (long long)heads * items_per_head;
@@ -190,9 +190,9 @@ int simulate(const Schedule& sc, int heads, int workers, int placement, double c
             int kv2 = sc.task_kv[s2.task];
             if (sc.rank[(size_t)kv2 * n + q] == next_rank[key]) {
                 lst.erase(lst.begin() + x);
-                waited += fin - s2.wait_since;
+                waited += fin + e - s2.wait_since;
                 s2.waiting_key = -1;
-                self_pq.push({fin, w2 + workers});  // +workers: "reduction may start"
+                self_pq.push({fin + e, w2 + workers});  // +workers: "reduction may start"
                 break;
             }
         }
@@ -238,7 +238,10 @@ int simulate(const Schedule& sc, int heads, int workers, int placement, double c
         const int kv = sc.task_kv[s.task], q = sc.task_q[s.task];
         const size_t key = (size_t)head * n + q;
         if (!ordered || sc.rank[(size_t)kv * n + q] == next_rank[key]) {
-            double st = ordered ? std::max(t, last_finish[key]) : t;
+            // a contributor after the first starts once the previous one's
+            // release has reached it (edge cost e)
+            double st = t;
+            if (ordered && next_rank[key] > 0) st = std::max(t, last_finish[key] + e);
             if (st > t) waited += st - t;
             start_reduction(w, st, pq);
         } else {
@@ -288,10 +291,17 @@ extern "C" int attn_sched_min_workers(int n, int causal, int schedule) {
 extern "C" int attn_dagsim(int n, int causal, int schedule, int heads, int workers, int placement,
                            double c, double r, double* makespan, double* wait_time,
                            double* busy_time) {
+    return attn_dagsim_edge(n, causal, schedule, heads, workers, placement, c, r, 0.0, makespan, wait_time,
+                            busy_time);
+}
+
+extern "C" int attn_dagsim_edge(int n, int causal, int schedule, int heads, int workers, int placement,
+                                double c, double r, double e, double* makespan, double* wait_time,
+                                double* busy_time) {
     attn::Schedule sc;
     int rc = attn::build_schedule(n, causal != 0, schedule, sc);
     if (rc != ATTN_OK) return attn::fail(rc, "attn_dagsim: invalid or unsupported schedule");
-    rc = attn::simulate(sc, heads, workers, placement, c, r, makespan, wait_time, busy_time);
+    rc = attn::simulate(sc, heads, workers, placement, c, r, e, makespan, wait_time, busy_time);
     if (rc == ATTN_ERR_DEADLOCK) return attn::fail(rc, "attn_dagsim: the schedule deadlocks with this many workers");
     if (rc != ATTN_OK) return attn::fail(rc, "attn_dagsim: invalid arguments");
     return ATTN_OK;
@@ -300,9 +310,9 @@ extern "C" int attn_dagsim(int n, int causal, int schedule, int heads, int worke
 // ---------------------------------------------------------------------------
 // Schedule selection and cost calibration on the DAG model
 // ---------------------------------------------------------------------------
-extern "C" int attn_sched_select(int n, int causal, int heads, int workers, double c, double r,
+extern "C" int attn_sched_select(int n, int causal, int heads, int workers, double c, double r, double e,
                                  int* schedule, double* makespan) {
-    if (n <= 0 || heads <= 0 || workers <= 0 || !(c >= 0) || !(r >= 0))
+    if (n <= 0 || heads <= 0 || workers <= 0 || !(c >= 0) || !(r >= 0) || !(e >= 0))
         return attn::fail(ATTN_ERR_INVALID_ARG, "attn_sched_select: invalid arguments");
     int best = -1;
     double best_t = 0;
@@ -311,7 +321,7 @@ extern "C" int attn_sched_select(int n, int causal, int heads, int workers, doub
         if (attn::build_schedule(n, causal != 0, s, sc) != ATTN_OK) continue;  // e.g. odd n, fold
         if (attn::min_workers(sc) > workers) continue;                          // cannot be co-scheduled
         double t = 0;
-        if (attn::simulate(sc, heads, workers, 1, c, r, &t, nullptr, nullptr) != ATTN_OK) continue;
+        if (attn::simulate(sc, heads, workers, 1, c, r, e, &t, nullptr, nullptr) != ATTN_OK) continue;
         if (best < 0 || t < best_t * (1 - 1e-12)) {
             best = s;
             best_t = t;
@@ -324,87 +334,82 @@ extern "C" int attn_sched_select(int n, int causal, int heads, int workers, doub
 }
 
 namespace {
-// Simulated makespans of every sample with compute cost 1 and reduction
-// cost rho; false when a sample cannot be simulated.
-bool unit_makespans(int count, const int* n, const int* causal, const int* schedule, const int* heads,
-                    const int* workers, double rho, std::vector<double>& m) {
-    m.resize(count);
-    for (int k = 0; k < count; ++k) {
-        attn::Schedule sc;
-        if (attn::build_schedule(n[k], causal[k] != 0, schedule[k], sc) != ATTN_OK) return false;
-        if (attn::simulate(sc, heads[k], workers[k], 1, 1.0, rho, &m[k], nullptr, nullptr) != ATTN_OK) return false;
-    }
-    return true;
-}
+struct FitData {
+    int count;
+    const int *n, *causal, *schedule, *heads, *workers;
+    const double* measured;
+};
 
-// For fixed rho the makespan is proportional to c: the c minimising the
-// relative squared error sum (c m_k / T_k - 1)^2 is sum(x) / sum(x^2) with
-// x_k = m_k / T_k.  Returns the RMS relative error at that c.
-double best_scale(const std::vector<double>& m, const double* measured, double* c) {
+// RMS relative error of the model with c = 1, r = rho, e = eps scaled by the
+// best c (for fixed rho and eps every makespan is proportional to c, and
+// the c minimising sum (c m_k / T_k - 1)^2 is sum(x) / sum(x^2) with
+// x_k = m_k / T_k).  Negative when a sample cannot be simulated.
+double fit_error(const FitData& f, double rho, double eps, double* c_out) {
     double sx = 0, sxx = 0;
-    for (size_t k = 0; k < m.size(); ++k) {
-        const double x = m[k] / measured[k];
-        sx += x;
-        sxx += x * x;
+    std::vector<double> x(f.count);
+    for (int k = 0; k < f.count; ++k) {
+        attn::Schedule sc;
+        double m = 0;
+        if (attn::build_schedule(f.n[k], f.causal[k] != 0, f.schedule[k], sc) != ATTN_OK) return -1;
+        if (attn::simulate(sc, f.heads[k], f.workers[k], 1, 1.0, rho, eps, &m, nullptr, nullptr) != ATTN_OK)
+            return -1;
+        x[k] = m / f.measured[k];
+        sx += x[k];
+        sxx += x[k] * x[k];
     }
-    *c = sxx > 0 ? sx / sxx : 0;
-    double e = 0;
-    for (size_t k = 0; k < m.size(); ++k) {
-        const double d = *c * m[k] / measured[k] - 1;
-        e += d * d;
-    }
-    return std::sqrt(e / (double)m.size());
+    const double c = sxx > 0 ? sx / sxx : 0;
+    double err = 0;
+    for (int k = 0; k < f.count; ++k) err += (c * x[k] - 1) * (c * x[k] - 1);
+    if (c_out) *c_out = c;
+    return std::sqrt(err / f.count);
 }
 }  // namespace
 
 extern "C" int attn_sched_fit(int count, const int* n, const int* causal, const int* schedule, const int* heads,
-                              const int* workers, const double* measured, double* c, double* r, double* rms) {
+                              const int* workers, const double* measured, double* c, double* r, double* e,
+                              double* rms) {
     if (count <= 0 || !n || !causal || !schedule || !heads || !workers || !measured)
         return attn::fail(ATTN_ERR_INVALID_ARG, "attn_sched_fit: invalid arguments");
     for (int k = 0; k < count; ++k)
         if (!(measured[k] > 0) || n[k] <= 0 || heads[k] <= 0 || workers[k] <= 0)
             return attn::fail(ATTN_ERR_INVALID_ARG, "attn_sched_fit: invalid sample");
-    // coarse search over rho = r / c on a log grid (1e-4 .. 1e2), then a
-    // golden-section refinement of log(rho) around the best grid point
-    std::vector<double> m;
-    auto err_at = [&](double lr, double* cc) {
-        if (!unit_makespans(count, n, causal, schedule, heads, workers, std::exp(lr), m)) return -1.0;
-        return best_scale(m, measured, cc);
+    const FitData f{count, n, causal, schedule, heads, workers, measured};
+    // search in u = log(r/c) in [log 1e-4, log 1e2] and v = log(e/c) in
+    // [log 1e-4, log 1e2], with v at its lower end standing for e = 0
+    const double ulo = std::log(1e-4), uhi = std::log(1e2), vlo = std::log(1e-4), vhi = std::log(1e2);
+    auto eval = [&](double u, double v) {
+        return fit_error(f, std::exp(u), v <= vlo ? 0.0 : std::exp(v), nullptr);
     };
-    const double lo = std::log(1e-4), hi = std::log(1e2);
-    const int steps = 60;
-    double best_lr = lo, best_e = -1, cc = 0;
-    for (int i = 0; i <= steps; ++i) {
-        const double lr = lo + (hi - lo) * i / steps;
-        const double e = err_at(lr, &cc);
-        if (e < 0) return attn::fail(ATTN_ERR_UNSUPPORTED, "attn_sched_fit: a sample cannot be simulated");
-        if (best_e < 0 || e < best_e) {
-            best_e = e;
-            best_lr = lr;
+    // 1. r/c alone on a grid (e = 0)
+    double bu = ulo, bv = vlo, be = -1;
+    for (int i = 0; i <= 30; ++i) {
+        const double u = ulo + (uhi - ulo) * i / 30, er = eval(u, vlo);
+        if (er < 0) return attn::fail(ATTN_ERR_UNSUPPORTED, "attn_sched_fit: a sample cannot be simulated");
+        if (be < 0 || er < be) { be = er; bu = u; }
+    }
+    // 2. e/c on a grid at that r/c
+    for (int j = 1; j <= 15; ++j) {
+        const double v = vlo + (vhi - vlo) * j / 15, er = eval(bu, v);
+        if (er < be) { be = er; bv = v; }
+    }
+    // 3. pattern search in (u, v), halving the step when no neighbour helps
+    double step = (uhi - ulo) / 30;
+    while (step > 1e-4) {
+        bool moved = false;
+        const double du[4] = {step, -step, 0, 0}, dv[4] = {0, 0, step, -step};
+        for (int d = 0; d < 4; ++d) {
+            const double u = std::min(uhi, std::max(ulo, bu + du[d]));
+            const double v = std::min(vhi, std::max(vlo, bv + dv[d]));
+            const double er = eval(u, v);
+            if (er >= 0 && er < be * (1 - 1e-12)) { be = er; bu = u; bv = v; moved = true; }
         }
+        if (!moved) step *= 0.5;
     }
-    const double h = (hi - lo) / steps, g = 0.6180339887498949;
-    double a = best_lr - h, b = best_lr + h;
-    double x1 = b - g * (b - a), x2 = a + g * (b - a);
-    double f1 = err_at(x1, &cc), f2 = err_at(x2, &cc);
-    for (int it = 0; it < 40; ++it) {
-        if (f1 < f2) {
-            b = x2; x2 = x1; f2 = f1; x1 = b - g * (b - a); f1 = err_at(x1, &cc);
-        } else {
-            a = x1; x1 = x2; f1 = f2; x2 = a + g * (b - a); f2 = err_at(x2, &cc);
-        }
-    }
-    double lr = 0.5 * (a + b);
-    double e = err_at(lr, &cc);
-    double cg = 0;
-    const double eg = err_at(best_lr, &cg);  // keep the grid point if the refinement did not help
-    if (eg <= e) {
-        lr = best_lr;
-        e = eg;
-        cc = cg;
-    }
+    double cc = 0;
+    fit_error(f, std::exp(bu), bv <= vlo ? 0.0 : std::exp(bv), &cc);
     if (c) *c = cc;
-    if (r) *r = cc * std::exp(lr);
-    if (rms) *rms = e;
+    if (r) *r = cc * std::exp(bu);
+    if (e) *e = bv <= vlo ? 0.0 : cc * std::exp(bv);
+    if (rms) *rms = be;
     return ATTN_OK;
 }
