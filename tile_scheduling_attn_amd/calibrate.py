@@ -1,6 +1,6 @@
 """Calibrate the DAG model's task costs on this GPU, then pick schedules.
 
-    python tile_scheduling_attn_amd/calibrate.py [--steps K]
+    python tile_scheduling_attn_amd/calibrate.py [--steps K] [--measure-only | --samples FILE]
 
 Times the main kernel of the backward for every (workload, mask, schedule)
 below with the library's own launch-stream events, fits the model's compute
@@ -10,7 +10,9 @@ page's "What carries the argument", with the kernel's ticket queue as
 placement), fits the pages' model (e = 0) too, and prints one JSON document:
 the fitted costs, measured against simulated makespan for every sample, and
 the schedule
-`attn_sched_select` picks for each shape.  Inputs are seeded N(0, 1) Q, K, V,
+`attn_sched_select` picks for each shape.  `--measure-only` prints the
+timings as JSON and stops (the fit is host work of a minute or two);
+`--samples FILE` fits timings saved that way.  Inputs are seeded N(0, 1) Q, K, V,
 dO with O and lse of the right scale; the kernel's running time does not
 depend on the values.
 """
@@ -74,30 +76,33 @@ def zero_edge_fit(tsa, ss):
     return best
 
 
-def main():
-    ap = argparse.ArgumentParser(description=__doc__)
-    ap.add_argument("--steps", type=int, default=5)
-    a = ap.parse_args()
+def measure(steps):
     import torch
     import tile_scheduling_attn_amd as tsa
     import workloads
 
     workers = torch.cuda.get_device_properties(0).multi_processor_count  # one work group per CU
-    samples = {}  # d -> list of (n, causal, schedule, heads, workers, ms, workload)
+    samples = []  # (n, causal, schedule, heads, workers, ms, workload, d)
     for name, causal, scheds in PLAN:
         wl = workloads.WORKLOADS[name]
         tile = tsa.attn_bwd_tile_size(wl.dtype)
         n = -(-wl.s // tile)
         args = inputs(wl, torch)
         for sched in scheds:
-            ms = time_main(tsa, args, sched, causal, a.steps, torch)
+            ms = time_main(tsa, args, sched, causal, steps, torch)
             print(f"{name} causal={causal} {sched}: {ms:.4f} ms", file=sys.stderr, flush=True)
-            samples.setdefault(wl.d, []).append((n, causal, sched, wl.b * wl.h, workers, ms, name))
+            samples.append((n, causal, sched, wl.b * wl.h, workers, ms, name, wl.d))
         del args
         torch.cuda.empty_cache()
+    return samples
 
-    report = {"workers": workers, "fits": {}}
-    for d, ss in samples.items():
+
+def fit(samples):
+    import tile_scheduling_attn_amd as tsa
+
+    report = {"fits": {}}
+    for d in sorted({s[7] for s in samples}):
+        ss = [tuple(s[:7]) for s in samples if s[7] == d]
         print(f"fitting d={d} ({len(ss)} samples)", file=sys.stderr, flush=True)
         c, r, e, rms = tsa.attn_sched_fit([s[:6] for s in ss])
         c0, r0, _, rms0 = zero_edge_fit(tsa, ss)
@@ -118,7 +123,25 @@ def main():
                                    "e0": {"c_us": round(c0 * 1e3, 4), "r_us": round(r0 * 1e3, 4),
                                           "rms_rel_err": round(rms0, 4)},
                                    "samples": rows, "selected": picks}
-    print(json.dumps(report, indent=1))
+    return report
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__)
+    ap.add_argument("--steps", type=int, default=5)
+    g = ap.add_mutually_exclusive_group()
+    g.add_argument("--measure-only", action="store_true")
+    g.add_argument("--samples", metavar="FILE")
+    a = ap.parse_args()
+    if a.samples:
+        with open(a.samples) as f:
+            samples = json.load(f)["samples"]
+    else:
+        samples = measure(a.steps)
+        if a.measure_only:
+            print(json.dumps({"samples": samples}))
+            return
+    print(json.dumps(fit(samples), indent=1))
 
 
 if __name__ == "__main__":
