@@ -140,6 +140,26 @@ int attn_bwd_get_wait_stats(unsigned long long* wait_cycles, unsigned long long*
                             unsigned long long* polls);
 
 /* ------------------------------------------------------------------------
+ * Attention forward (device).  Not on the pages, which take O and lse as
+ * given: Fig. 1 of the paper (review page caption) shows the tiled
+ * FlashAttention whose forward this is, and the summary page's Experimental
+ * setup benchmarks the backward, which consumes O and lse.  Computes, per
+ * (b, h) and query row i, S_ij = scale * q_i . k_j (keys j > i masked when
+ * causal), lse_i = log sum_j exp(S_ij) (natural log, fp32) and
+ * O_i = sum_j exp(S_ij - lse_i) v_j, with online softmax over key tiles.
+ * q, k, v, o: contiguous [b][h][s][d] device tensors of `dtype` (16-byte
+ * aligned); lse: [b][h][s] fp32 device tensor (written).  Each work group
+ * owns a block of output rows, so the result is bitwise reproducible and
+ * independent of how work groups are scheduled.  Asynchronous on `stream`
+ * (hipStream_t; NULL = default stream).  Returns ATTN_OK,
+ * ATTN_ERR_INVALID_ARG (negative sizes, null or misaligned pointers, bad
+ * causal or dtype, non-finite scale), ATTN_ERR_UNSUPPORTED (d not 64 or 128)
+ * or ATTN_ERR_HIP (launch failure).  b*h == 0 or s == 0 is a no-op.
+ * ------------------------------------------------------------------------ */
+int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int b, int h, int s, int d,
+             int causal, int dtype, float scale, void* stream);
+
+/* ------------------------------------------------------------------------
  * Schedule generator (host, no GPU needed).
  * Within one head with n = ceil(s/T) tiles, a schedule is a list of work
  * items; each item is an ordered list of (KV tile, Q tile) tasks and runs on

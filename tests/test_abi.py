@@ -70,3 +70,23 @@ def test_empty_problem_is_a_no_op():
     assert _call(h=0) == 0
     assert _call(s=0) == 0
     assert tsa.attn_bwd_deterministic(0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 4, 128, 64, 0, 0) == 0
+
+
+def _fwd(**kw):
+    args = dict(q=0, k=0, v=0, o=0, lse=0, b=1, h=1, s=128, d=64, causal=0, dtype=0, scale=0.125, stream=0)
+    args.update(kw)
+    return tsa.attn_fwd(**args)
+
+
+def test_forward_argument_errors_need_no_gpu():
+    assert _fwd() == -1                        # null pointers
+    assert "null" in tsa.last_error()
+    assert _fwd(b=-1) == -1
+    assert _fwd(causal=2) == -1
+    assert _fwd(dtype=3) == -1
+    assert _fwd(scale=float("inf")) == -1
+    assert _fwd(d=32) == -2
+    assert _fwd(q=8, k=16, v=16, o=16, lse=16) == -1
+    assert "aligned" in tsa.last_error()
+    assert _fwd(q=16, k=16, v=16, o=16, lse=2) == -1
+    assert _fwd(b=0) == 0 and _fwd(s=0) == 0

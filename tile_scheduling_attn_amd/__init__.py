@@ -23,7 +23,7 @@ STATUS = {0: "ATTN_OK", -1: "ATTN_ERR_INVALID_ARG", -2: "ATTN_ERR_UNSUPPORTED",
           -6: "ATTN_ERR_WORKSPACE", -7: "ATTN_ERR_DEADLOCK"}
 
 # every function declared in include/attn_bwd.h
-EXPORTS = ("attn_bwd_deterministic", "attn_bwd_deterministic_ex", "attn_bwd_workspace_bytes",
+EXPORTS = ("attn_fwd", "attn_bwd_deterministic", "attn_bwd_deterministic_ex", "attn_bwd_workspace_bytes",
            "attn_bwd_query_status", "attn_bwd_last_error", "attn_bwd_tile_size",
            "attn_bwd_set_timing", "attn_bwd_get_kernel_times", "attn_bwd_set_wait_stats",
            "attn_bwd_get_wait_stats", "attn_sched_size", "attn_sched_get",
@@ -50,6 +50,8 @@ def _load():
     ip, dp = ctypes.POINTER(ctypes.c_int), ctypes.POINTER(ctypes.c_double)
     ull = ctypes.POINTER(ctypes.c_ulonglong)
     fp = ctypes.POINTER(ctypes.c_float)
+    lib.attn_fwd.argtypes = [vp] * 5 + [i] * 6 + [f, vp]
+    lib.attn_fwd.restype = i
     lib.attn_bwd_deterministic.argtypes = [vp] * 9 + [i] * 6
     lib.attn_bwd_deterministic.restype = i
     lib.attn_bwd_deterministic_ex.argtypes = [vp] * 9 + [i] * 7 + [f, vp, sz, vp]
@@ -117,6 +119,12 @@ def _ptr(x) -> int:
 # ---------------------------------------------------------------------------
 # C ABI, same names and arguments (pointers may be ints or tensors)
 # ---------------------------------------------------------------------------
+def attn_fwd(q, k, v, o, lse, b, h, s, d, causal, dtype, scale, stream) -> int:
+    dt = DTYPES[dtype] if isinstance(dtype, str) else int(dtype)
+    return lib.attn_fwd(*(_ptr(t) for t in (q, k, v, o, lse)), b, h, s, d, int(causal), dt, float(scale),
+                        int(stream or 0))
+
+
 def attn_bwd_deterministic(q, k, v, o, dO, lse, dq, dk, dv, b, h, s, d, causal, schedule) -> int:
     return lib.attn_bwd_deterministic(*(_ptr(t) for t in (q, k, v, o, dO, lse, dq, dk, dv)),
                                       b, h, s, d, int(causal), _sched_id(schedule))
@@ -240,6 +248,31 @@ def attn_sched_fit(samples):
 # ---------------------------------------------------------------------------
 # Torch convenience wrapper (allocation and stream only)
 # ---------------------------------------------------------------------------
+def forward(q, k, v, causal: bool, scale=None, out=None, stream=None):
+    """Attention forward on torch tensors [b, h, s, d] (bf16 or fp32,
+    contiguous, on the current HIP device).  Returns (o, lse) with lse
+    [b, h, s] fp32, allocated unless `out` gives them.  Asynchronous on
+    `stream` (default: torch's current stream)."""
+    import torch
+    b, h, s, d = q.shape
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        if tuple(t.shape) != (b, h, s, d) or t.dtype != q.dtype or not t.is_contiguous() or not t.is_cuda:
+            raise ValueError(f"{name} must be a contiguous device tensor of shape {(b, h, s, d)} "
+                             f"and dtype {q.dtype}")
+    dtype = {torch.bfloat16: "bf16", torch.float32: "fp32"}.get(q.dtype)
+    if dtype is None:
+        raise ValueError("q must be bfloat16 or float32")
+    if out is None:
+        out = (torch.empty_like(q), torch.empty((b, h, s), dtype=torch.float32, device=q.device))
+    o, lse = out
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    if stream is None:
+        stream = torch.cuda.current_stream().cuda_stream
+    _check(attn_fwd(q, k, v, o, lse, b, h, s, d, causal, dtype, scale, stream), "attn_fwd")
+    return o, lse
+
+
 def backward(q, k, v, o, do, lse, causal: bool, schedule="shift", scale=None, out=None,
              workspace=None, stream=None):
     """Run the backward on torch tensors [b, h, s, d] (bf16 or fp32, contiguous,

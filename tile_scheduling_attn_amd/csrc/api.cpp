@@ -269,6 +269,28 @@ extern "C" int attn_bwd_deterministic_ex(const void* q, const void* k, const voi
                     workspace_bytes, stream);
 }
 
+extern "C" int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int b, int h, int s,
+                        int d, int causal, int dtype, float scale, void* stream) {
+    g_last_error.clear();
+    if (b < 0 || h < 0 || s < 0) return fail(ATTN_ERR_INVALID_ARG, "b, h and s must be >= 0");
+    if (causal != 0 && causal != 1) return fail(ATTN_ERR_INVALID_ARG, "causal must be 0 or 1");
+    if (dtype != ATTN_BF16 && dtype != ATTN_FP32) return fail(ATTN_ERR_INVALID_ARG, "unknown dtype");
+    if (!std::isfinite(scale)) return fail(ATTN_ERR_INVALID_ARG, "scale must be finite");
+    if (d != 64 && d != 128) return fail(ATTN_ERR_UNSUPPORTED, "head dimension must be 64 or 128");
+    const long long H = (long long)b * h;
+    if (H == 0 || s == 0) return ATTN_OK;
+    if (H * (long long)s * d >= (1LL << 40)) return fail(ATTN_ERR_INVALID_ARG, "problem too large");
+    if (!q || !k || !v || !o || !lse) return fail(ATTN_ERR_INVALID_ARG, "null tensor pointer");
+    if (((uintptr_t)q | (uintptr_t)k | (uintptr_t)v | (uintptr_t)o) & 15)
+        return fail(ATTN_ERR_INVALID_ARG, "tensor pointers must be 16-byte aligned");
+    if ((uintptr_t)lse & 3) return fail(ATTN_ERR_INVALID_ARG, "lse must be 4-byte aligned");
+    FwdArgs a{};
+    a.q = q; a.k = k; a.v = v; a.o = o; a.lse = lse;
+    a.H = (int)H; a.s = s; a.d = d; a.causal = causal != 0; a.dtype = dtype; a.scale = scale;
+    a.stream = stream;
+    return launch_forward(a);
+}
+
 extern "C" size_t attn_bwd_workspace_bytes(int b, int h, int s, int d, int causal, int schedule) {
     (void)causal;
     (void)schedule;

@@ -61,4 +61,18 @@ struct BwdLaunch {
 
 int launch_backward(const BwdArgs& a, const BwdLaunch& L);
 
+// Parameters of one forward launch (device pointers; validated by the caller).
+struct FwdArgs {
+    const void *q, *k, *v;
+    void* o;
+    float* lse;
+    int H, s, d;
+    bool causal;
+    int dtype;
+    float scale;
+    void* stream;
+};
+
+int launch_forward(const FwdArgs& a);
+
 }  // namespace attn
