@@ -79,6 +79,25 @@ def time_calls(tsa, pb, schedule, steps, warmup, torch):
             "ms_preprocess": pre, "ms_main": main, "ms_finalize": fin}
 
 
+def time_forward(tsa, pb, steps, torch):
+    """The library's attention forward on the same inputs (context only: the
+    forward is not part of the timed backward).  FLOP convention: 2
+    contractions x 2*s*s*d per head, halved under the causal mask."""
+    o, lse = torch.empty_like(pb.q), torch.empty_like(pb.lse)
+    for _ in range(2):
+        tsa.forward(pb.q, pb.k, pb.v, pb.causal, pb.scale, out=(o, lse))
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record()
+    for _ in range(steps):
+        tsa.forward(pb.q, pb.k, pb.v, pb.causal, pb.scale, out=(o, lse))
+    end.record()
+    torch.cuda.synchronize()
+    ms = start.elapsed_time(end) / steps
+    flops = 4.0 * pb.b * pb.h * pb.s * pb.s * pb.d / (2 if pb.causal else 1)
+    return {"ms": round(ms, 4), "tflops": round(flops / (ms * 1e-3) / 1e12, 2)}
+
+
 def flag_wait_stats(tsa, pb, schedule, torch):
     """One extra, untimed call with the kernel's wait counters on: the share of
     work-item cycles that work groups spent polling dQ flags for their turn."""
@@ -184,6 +203,9 @@ def main():
                 "kernel": "bwd_main_kernel",
                 "algorithmic_flop_per_launch": flops}
 
+    fwd = time_forward(tsa, pb, max(5, args.steps // 2), torch)
+    log(f"forward (context): {fwd['ms']:.3f} ms, {fwd['tflops']:.1f} TFLOPS")
+
     waits = flag_wait_stats(tsa, pb, schedule, torch)
     log(f"dQ flag waits: {waits['fraction']} of work-item cycles ({waits['polls']} polls)")
 
@@ -216,6 +238,7 @@ def main():
         "compare": extra,
         "roofline": roofline,
         "flag_wait": waits,
+        "forward": fwd,
         "cpu_baseline": cpu,
     }
     if "atomic" in extra:
