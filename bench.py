@@ -27,7 +27,8 @@ PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
 PEAK_FP32_MFMA_TFLOPS = 157.3
 METRIC = "deterministic attn-bwd TFLOPS (bf16, 1 GPU) & % of MFMA peak; vs non-det"
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_bwd_main_s8k_d128_full_shift.json")
-KERNEL_SOURCE = os.path.join(ROOT, "tile_scheduling_attn_amd", "csrc", "bwd_kernels.hip")
+# the backward kernel's source: its own file and the device helpers it includes
+KERNEL_SOURCES = [os.path.join(ROOT, "tile_scheduling_attn_amd", "csrc", f) for f in ("bwd_kernels.hip", "attn_device.h")]
 
 
 def log(msg):
@@ -35,8 +36,11 @@ def log(msg):
 
 
 def kernel_source_sha():
-    with open(KERNEL_SOURCE, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()
+    h = hashlib.sha256()
+    for path in KERNEL_SOURCES:
+        with open(path, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
 
 
 def traffic_per_launch(workload, schedule):
