@@ -148,6 +148,8 @@ def main():
     ap.add_argument("--compare", default="naive,atomic",
                     help="comma list of schedules also timed for context ('none' for none)")
     ap.add_argument("--cpu-heads", type=int, default=16, help="heads in the CPU oracle sample (0: skip)")
+    ap.add_argument("--placement", default="xcd", choices=("xcd", "global"),
+                    help="work placement of the deterministic kernel (per-XCD queues or one global queue)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of MIB MiB five times (scales the HBM "
                          "traffic counters of a profiler run) and exit")
@@ -175,6 +177,7 @@ def main():
     import workloads
     from tests.support import Problem
 
+    tsa.attn_bwd_set_placement(args.placement)
     wl = workloads.WORKLOADS[args.workload]
     causal = (wl.masks[0] == "causal") if args.causal is None else bool(args.causal)
     schedule = args.schedule or ("descending" if causal else "shift")
@@ -235,7 +238,8 @@ def main():
         "config": {"workload": f"{wl.name}: b={wl.b} h={wl.h} s={wl.s} d={wl.d} "
                                f"{'causal' if causal else 'full'} mask, schedule {schedule}",
                    "b": wl.b, "h": wl.h, "s": wl.s, "d": wl.d, "causal": causal,
-                   "schedule": schedule, "tile": tsa.attn_bwd_tile_size(wl.dtype)},
+                   "schedule": schedule, "tile": tsa.attn_bwd_tile_size(wl.dtype),
+                   "placement": args.placement},
         "pct_of_peak": round(100 * tflops / peak, 2),
         "kernel_ms": {"preprocess": round(res["ms_preprocess"], 4), "main": round(res["ms_main"], 4),
                       "finalize": round(res["ms_finalize"], 4)},

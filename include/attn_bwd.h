@@ -69,7 +69,11 @@ typedef enum {
     ATTN_ERR_HIP = -4,          /* a HIP runtime call failed                */
     ATTN_ERR_TIMEOUT = -5,      /* a device-side flag wait expired          */
     ATTN_ERR_WORKSPACE = -6,    /* caller workspace too small               */
-    ATTN_ERR_DEADLOCK = -7      /* simulator: the schedule cannot finish    */
+    ATTN_ERR_DEADLOCK = -7,     /* simulator: the schedule cannot finish    */
+    ATTN_ERR_PLACEMENT = -8     /* XCD placement found work groups it could
+                                   not use as planned: an XCD without work
+                                   groups or an unknown XCD id (results of
+                                   that call invalid)                       */
 } attn_status_t;
 
 /* ------------------------------------------------------------------------
@@ -102,9 +106,13 @@ int attn_bwd_deterministic_ex(const void* q, const void* k, const void* v, const
                               int dtype, float scale, void* workspace, size_t workspace_bytes,
                               void* stream);
 
-/* Bytes of workspace a call with these sizes needs: fp32 dQ accumulator
- * (b*h*s_pad*d*4), per-(head, Q tile) flags, D = rowsum(dO*O), counters.
- * s_pad is s rounded up to 128.  Returns 0 for invalid sizes. */
+/* Bytes of workspace a call with these sizes needs on the current device:
+ * fp32 dQ accumulator (b*h*s_pad*d*4, or the per-XCD copies of XCD
+ * placement, for either element type), per-(head, Q tile) flags,
+ * D = rowsum(dO*O), counters.  s_pad is s rounded up to 128.  Without a
+ * usable device, or under ATTN_PLACE_GLOBAL, the size for the single global
+ * queue, which is also the smallest workspace a call accepts.  Returns 0
+ * for invalid sizes. */
 size_t attn_bwd_workspace_bytes(int b, int h, int s, int d, int causal, int schedule);
 
 /* Synchronises `stream` (hipStream_t or NULL), then reports and clears the
@@ -129,6 +137,25 @@ int attn_bwd_tile_size(int dtype);
  * ATTN_OK, ATTN_ERR_INVALID_ARG (nothing recorded) or ATTN_ERR_HIP. */
 int attn_bwd_set_timing(int on);
 int attn_bwd_get_kernel_times(float* ms_preprocess, float* ms_main, float* ms_finalize);
+
+/* Work placement of the deterministic main kernel for later calls.
+ * ATTN_PLACE_XCD (the default): one work queue per XCD of MI355X, served by
+ * the work groups running on that XCD; a head's items are split into the
+ * fewest contiguous chunks (1, 2, 4 or 8) that fit one XCD's work groups,
+ * each chunk on one XCD.  Every XCD keeps its own copy of the fp32 dQ
+ * accumulator: a hand-off between work groups of one XCD stays in its L2,
+ * only a hand-off to another XCD goes through memory.  The copies make the
+ * accumulator part of the workspace about `chunks` times larger (see
+ * attn_bwd_workspace_bytes).  Used when the device deals work groups evenly
+ * over 8 XCDs (checked once per device) and the launch has at least 8
+ * resident work groups and, for the Shift family, a chunk that fits one
+ * XCD; otherwise, and for a caller workspace too small for the copies, the
+ * call keeps the single global queue.  ATTN_PLACE_GLOBAL: always the one
+ * global queue and one accumulator, every hand-off through memory.  Results
+ * are bitwise the same under both: the reduction order comes from the
+ * schedule alone.  Returns ATTN_OK or ATTN_ERR_INVALID_ARG (unknown mode). */
+typedef enum { ATTN_PLACE_GLOBAL = 0, ATTN_PLACE_XCD = 1 } attn_placement_t;
+int attn_bwd_set_placement(int mode);
 
 /* Flag-wait instrumentation.  When enabled, the main kernel of later calls
  * accumulates, per launch, the clock cycles its work groups spent inside

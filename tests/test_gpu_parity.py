@@ -182,10 +182,52 @@ def test_caller_workspace_and_stream_match_library_workspace():
     st.synchronize()
     for a, b_ in zip(ref, out):
         assert torch.equal(a.view(torch.int16), b_.view(torch.int16))
-    small = torch.empty(nbytes - 256, dtype=torch.uint8, device="cuda")
+    # the size the single global queue needs (no per-XCD accumulator copies)
+    tsa.attn_bwd_set_placement("global")
+    try:
+        nglobal = tsa.attn_bwd_workspace_bytes(1, 4, 640, 128, 1, "descending")
+    finally:
+        tsa.attn_bwd_set_placement("xcd")
+    assert nglobal <= nbytes
+    # between the two: runs with the global queue, same bits
+    mid = torch.empty(nglobal, dtype=torch.uint8, device="cuda")
+    out = tsa.backward(pb.q, pb.k, pb.v, pb.o, pb.do, pb.lse, True, "descending", workspace=mid)
+    for a, b_ in zip(ref, out):
+        assert torch.equal(a.view(torch.int16), b_.view(torch.int16))
+    small = torch.empty(nglobal - 256, dtype=torch.uint8, device="cuda")
     with pytest.raises(tsa.AttnError) as e:
         tsa.backward(pb.q, pb.k, pb.v, pb.o, pb.do, pb.lse, True, "descending", workspace=small)
     assert e.value.code == -6
+
+
+# (b, h, s, d, causal): shapes whose launches use XCD placement with 1, 2
+# and 4 chunks per head and the global fallback (fewer than 8 items)
+PLACEMENT_SHAPES = [(2, 8, 2048, 128, False), (1, 16, 4096, 64, True), (1, 4, 8192, 128, False),
+                    (1, 2, 16384, 128, True), (2, 16, 1024, 64, True), (1, 1, 512, 64, False)]
+
+
+@pytest.mark.parametrize("shape", PLACEMENT_SHAPES, ids=lambda x: "-".join(map(str, x)))
+def test_xcd_and_global_placement_give_the_same_bits(shape):
+    """The reduction order comes from the schedule alone: per-XCD queues with
+    per-XCD accumulator copies (hand-offs within an XCD through its L2) and
+    the single global queue give bitwise identical gradients, and no call
+    reports a placement error."""
+    b, h, s, d, causal = shape
+    pb = Problem(b, h, s, d, "bf16", 4242, causal)
+    for sched in _schedules_for(pb, DET):
+        _say(f"placement {shape} {sched}")
+        outs = {}
+        for place in ("global", "xcd"):
+            tsa.attn_bwd_set_placement(place)
+            try:
+                outs[place] = [t.clone() for t in pb.run(sched)]
+            finally:
+                tsa.attn_bwd_set_placement("xcd")
+            assert tsa.attn_bwd_query_status() == 0, tsa.last_error()
+        for a, b_ in zip(outs["global"], outs["xcd"]):
+            assert torch.equal(a.view(torch.int16), b_.view(torch.int16)), f"{shape} {sched}"
+    if s <= 8192:  # the oracle's s x s matrices stay small enough
+        _check_parity(pb, outs["xcd"], [0, b * h - 1], f"placement {shape}")
 
 
 def test_default_entry_point_bf16():

@@ -20,12 +20,12 @@ SCHEDULES = {"naive": 0, "descending": 1, "shift": 2, "symmetric_shift": 3, "ato
 DTYPES = {"bf16": 0, "fp32": 1}
 STATUS = {0: "ATTN_OK", -1: "ATTN_ERR_INVALID_ARG", -2: "ATTN_ERR_UNSUPPORTED",
           -3: "ATTN_ERR_COSCHEDULE", -4: "ATTN_ERR_HIP", -5: "ATTN_ERR_TIMEOUT",
-          -6: "ATTN_ERR_WORKSPACE", -7: "ATTN_ERR_DEADLOCK"}
+          -6: "ATTN_ERR_WORKSPACE", -7: "ATTN_ERR_DEADLOCK", -8: "ATTN_ERR_PLACEMENT"}
 
 # every function declared in include/attn_bwd.h
 EXPORTS = ("attn_fwd", "attn_bwd_deterministic", "attn_bwd_deterministic_ex", "attn_bwd_workspace_bytes",
            "attn_bwd_query_status", "attn_bwd_last_error", "attn_bwd_tile_size",
-           "attn_bwd_set_timing", "attn_bwd_get_kernel_times", "attn_bwd_set_wait_stats",
+           "attn_bwd_set_timing", "attn_bwd_get_kernel_times", "attn_bwd_set_placement", "attn_bwd_set_wait_stats",
            "attn_bwd_get_wait_stats", "attn_sched_size", "attn_sched_get",
            "attn_sched_min_workers", "attn_dagsim", "attn_dagsim_edge", "attn_sched_select",
            "attn_sched_fit")
@@ -68,6 +68,8 @@ def _load():
     lib.attn_bwd_set_timing.restype = i
     lib.attn_bwd_get_kernel_times.argtypes = [fp, fp, fp]
     lib.attn_bwd_get_kernel_times.restype = i
+    lib.attn_bwd_set_placement.argtypes = [i]
+    lib.attn_bwd_set_placement.restype = i
     lib.attn_bwd_set_wait_stats.argtypes = [i]
     lib.attn_bwd_set_wait_stats.restype = i
     lib.attn_bwd_get_wait_stats.argtypes = [ull, ull, ull]
@@ -164,6 +166,16 @@ def attn_bwd_get_kernel_times():
     _check(lib.attn_bwd_get_kernel_times(ctypes.byref(a), ctypes.byref(b_), ctypes.byref(c)),
            "attn_bwd_get_kernel_times")
     return a.value, b_.value, c.value
+
+
+PLACEMENTS = {"global": 0, "xcd": 1}
+
+
+def attn_bwd_set_placement(mode) -> None:
+    """Work placement of later deterministic calls: "xcd" (per-XCD queues,
+    the default) or "global" (one queue)."""
+    _check(lib.attn_bwd_set_placement(PLACEMENTS[mode] if isinstance(mode, str) else int(mode)),
+           "attn_bwd_set_placement")
 
 
 def attn_bwd_set_wait_stats(on: bool) -> int:

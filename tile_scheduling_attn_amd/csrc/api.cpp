@@ -3,6 +3,7 @@
 // are declared, with their contracts, in include/attn_bwd.h.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cmath>
 #include <cstdint>
 #include <cstring>
@@ -41,13 +42,15 @@ struct WsLayout {
     int nflags;
 };
 
-static bool ws_layout(long long H, long long s, int d, WsLayout& w) {
+// acc_heads: heads of fp32 accumulator (H, or kQueues copies of an XCD
+// plan's slots)
+static bool ws_layout(long long H, long long s, int d, long long acc_heads, WsLayout& w) {
     if (H < 0 || s < 0 || (d != 64 && d != 128)) return false;
     w.s_pad = (size_t)((s + kPadRows - 1) / kPadRows) * kPadRows;
     const size_t nmax = w.s_pad / kMinTile;
     w.nflags = (int)(H * nmax);
     w.acc = 0;
-    w.delta = align_up(w.acc + (size_t)H * w.s_pad * d * sizeof(float));
+    w.delta = align_up(w.acc + (size_t)acc_heads * w.s_pad * d * sizeof(float));
     w.flags = align_up(w.delta + (size_t)H * w.s_pad * sizeof(float));
     w.counters = align_up(w.flags + (size_t)w.nflags * sizeof(unsigned));
     w.total = align_up(w.counters + kCounterWords * sizeof(unsigned));
@@ -56,14 +59,17 @@ static bool ws_layout(long long H, long long s, int d, WsLayout& w) {
 
 struct DevSchedule {
     // item_begin (items+1 ints, padded to a multiple of 4) | one 16-byte
-    // record per task: {kv tile, q tile, rank, contributors of the q tile}
+    // record per task: {kv tile, q tile, rank, item of the q tile's next
+    // contributor or -1 for its last}
     int* buf = nullptr;
     int items = 0, tasks = 0, n = 0, min_workers = 1;
+    std::vector<int> item_begin;  // host copy
 };
 
 struct DevState {
     bool init = false;
     int num_cus = 0;
+    bool xcd_ok = false;  // work group b runs on XCD b % kQueues
     void* ws = nullptr;
     size_t ws_bytes = 0;
     unsigned* status = nullptr;
@@ -83,6 +89,7 @@ static std::mutex g_mutex;
 static std::map<int, DevState> g_dev;
 static bool g_timing = false;
 static bool g_wait_stats = false;
+static bool g_xcd_placement = true;
 static int g_last_dev = -1;
 
 static int dev_init(int dev, DevState& ds) {
@@ -95,6 +102,8 @@ static int dev_init(int dev, DevState& ds) {
     if (e != hipSuccess) return fail_hip(e, "hipMalloc(status)");
     e = hipMemset(ds.status, 0, sizeof(unsigned));
     if (e != hipSuccess) return fail_hip(e, "hipMemset(status)");
+    int rc = probe_xcd_dispatch(ds.num_cus, &ds.xcd_ok);
+    if (rc != ATTN_OK) return rc;
     ds.init = true;
     return ATTN_OK;
 }
@@ -113,12 +122,20 @@ static int get_schedule(DevState& ds, int n, bool causal, int schedule, DevSched
     if (rc != ATTN_OK) return fail(rc, "invalid schedule");
     std::vector<int> host(sc.item_begin.begin(), sc.item_begin.end());
     host.resize((host.size() + 3) / 4 * 4, 0);
+    // item that makes contribution `rank` to Q tile q: item_of[q * n + rank]
+    std::vector<int> item_of((size_t)n * n, -1);
+    for (int it = 0; it < sc.num_items(); ++it)
+        for (int t = sc.item_begin[it]; t < sc.item_begin[it + 1]; ++t) {
+            const int r = sc.rank[(size_t)sc.task_kv[t] * n + sc.task_q[t]];
+            if (r >= 0) item_of[(size_t)sc.task_q[t] * n + r] = it;
+        }
     for (size_t t = 0; t < sc.task_kv.size(); ++t) {
         const int kv = sc.task_kv[t], q = sc.task_q[t];
+        const int r = sc.rank[(size_t)kv * n + q];
         host.push_back(kv);
         host.push_back(q);
-        host.push_back(sc.rank[(size_t)kv * n + q]);
-        host.push_back(sc.count[q]);
+        host.push_back(r);
+        host.push_back(r >= 0 && r + 1 < sc.count[q] ? item_of[(size_t)q * n + r + 1] : -1);
     }
     DevSchedule d;
     hipError_t e = hipMalloc(&d.buf, host.size() * sizeof(int));
@@ -129,6 +146,7 @@ static int get_schedule(DevState& ds, int n, bool causal, int schedule, DevSched
         return fail_hip(e, "hipMemcpy(schedule)");
     }
     d.items = sc.num_items();
+    d.item_begin = sc.item_begin;
     d.tasks = (int)sc.task_kv.size();
     d.n = n;
     d.min_workers = min_workers(sc);
@@ -138,6 +156,14 @@ static int get_schedule(DevState& ds, int n, bool causal, int schedule, DevSched
 }
 
 static int tile_for(int dtype) { return dtype == ATTN_FP32 ? 64 : 128; }
+
+// XCD placement of a deterministic call, planned for one resident work group
+// per CU (the main kernel's LDS allows no more; a launch with more resident
+// work groups only has more per queue)
+static XcdPlan placement_plan(const DevState& ds, const DevSchedule& sch, int schedule, long long H) {
+    if (schedule == ATTN_SCHED_ATOMIC || !g_xcd_placement || !ds.xcd_ok) return XcdPlan{};
+    return xcd_plan(sch.item_begin, sch.min_workers, std::min<long long>(ds.num_cus, H * sch.items), H);
+}
 
 static int backward(const void* q, const void* k, const void* v, const void* o, const void* dO,
                     const float* lse, void* dq, void* dk, void* dv, int b, int h, int s, int d,
@@ -164,8 +190,7 @@ static int backward(const void* q, const void* k, const void* v, const void* o, 
 
     const int tile = tile_for(dtype);
     const int n = (s + tile - 1) / tile;
-    WsLayout wl;
-    ws_layout(H, s, d, wl);
+    if (n >= (1 << 24)) return fail(ATTN_ERR_UNSUPPORTED, "sequence too long: more than 2^24 - 1 tiles");
 
     std::lock_guard<std::mutex> lock(g_mutex);
     int dev = 0;
@@ -178,10 +203,21 @@ static int backward(const void* q, const void* k, const void* v, const void* o, 
     rc = get_schedule(ds, n, causal != 0, schedule, &sch);
     if (rc != ATTN_OK) return rc;
 
+    // XCD placement needs an accumulator copy per XCD; a caller workspace
+    // too small for it but large enough for the global queue runs with that
+    WsLayout wl;
+    ws_layout(H, s, d, H, wl);
+    const XcdPlan plan = placement_plan(ds, *sch, schedule, H);
+    WsLayout wl_xcd = wl;
+    if (plan.chunks) ws_layout(H, s, d, kQueues * plan.slots, wl_xcd);
     char* ws = static_cast<char*>(workspace);
+    bool use_xcd = plan.chunks > 0;
     if (ws) {
         if (workspace_bytes < wl.total) return fail(ATTN_ERR_WORKSPACE, "workspace smaller than attn_bwd_workspace_bytes()");
-    } else {
+        use_xcd = use_xcd && workspace_bytes >= wl_xcd.total;
+    }
+    if (use_xcd) wl = wl_xcd;
+    if (!ws) {
         if (ds.ws_bytes < wl.total) {
             if (ds.ws) {
                 e = hipDeviceSynchronize();
@@ -211,6 +247,7 @@ static int backward(const void* q, const void* k, const void* v, const void* o, 
     a.delta = reinterpret_cast<float*>(ws + wl.delta);
     a.flags = reinterpret_cast<unsigned*>(ws + wl.flags);
     a.counters = reinterpret_cast<unsigned*>(ws + wl.counters);
+    a.acc_slots = use_xcd ? plan.slots : H;
 
     void** ev = nullptr;
     if (g_timing && ds.ev_used < kMaxTimedCalls) {
@@ -235,6 +272,7 @@ static int backward(const void* q, const void* k, const void* v, const void* o, 
     L.items_per_head = sch->items;
     // flags and counters are contiguous: one clear covers both
     L.nclear32 = (int)((wl.total - wl.flags) / sizeof(unsigned));
+    if (use_xcd) L.plan = plan;
 
     rc = launch_backward(a, L);
     if (rc != ATTN_OK) return rc;
@@ -292,12 +330,36 @@ extern "C" int attn_fwd(const void* q, const void* k, const void* v, void* o, fl
 }
 
 extern "C" size_t attn_bwd_workspace_bytes(int b, int h, int s, int d, int causal, int schedule) {
-    (void)causal;
-    (void)schedule;
     if (b < 0 || h < 0 || s < 0) return 0;
+    const long long H = (long long)b * h;
     WsLayout wl;
-    if (!ws_layout((long long)b * h, s, d, wl)) return 0;
-    return wl.total;
+    if (!ws_layout(H, s, d, H, wl)) return 0;
+    size_t total = wl.total;
+    // what XCD placement needs on the current device (either tile edge)
+    if (H > 0 && s > 0 && (causal == 0 || causal == 1) && schedule >= ATTN_SCHED_NAIVE &&
+        schedule < ATTN_SCHED_ATOMIC) {
+        std::lock_guard<std::mutex> lock(g_mutex);
+        int dev = 0;
+        if (hipGetDevice(&dev) == hipSuccess) {
+            DevState& ds = g_dev[dev];
+            if (dev_init(dev, ds) == ATTN_OK) {
+                for (int tile : {64, 128}) {
+                    const int n = (s + tile - 1) / tile;
+                    Schedule sc;
+                    if (n >= (1 << 24) || build_schedule(n, causal != 0, schedule, sc) != ATTN_OK) continue;
+                    DevSchedule shape;
+                    shape.items = sc.num_items();
+                    shape.item_begin = sc.item_begin;
+                    shape.min_workers = min_workers(sc);
+                    const XcdPlan plan = placement_plan(ds, shape, schedule, H);
+                    WsLayout w2;
+                    if (plan.chunks && ws_layout(H, s, d, kQueues * plan.slots, w2)) total = std::max(total, w2.total);
+                }
+            }
+        }
+        g_last_error.clear();
+    }
+    return total;
 }
 
 extern "C" int attn_bwd_query_status(void* stream) {
@@ -316,7 +378,10 @@ extern "C" int attn_bwd_query_status(void* stream) {
     if (st) {
         e = hipMemset(it->second.status, 0, sizeof(unsigned));
         if (e != hipSuccess) return fail_hip(e, "hipMemset(status)");
-        return fail(ATTN_ERR_TIMEOUT, "a dQ flag wait expired; the results of that call are invalid");
+        if (st & 1u) return fail(ATTN_ERR_TIMEOUT, "a dQ flag wait expired; the results of that call are invalid");
+        return fail(ATTN_ERR_PLACEMENT, "XCD placement could not use the work groups as planned (an XCD "
+                                        "without work groups or an unknown XCD id); the results of that call "
+                                        "are invalid");
     }
     return ATTN_OK;
 }
@@ -361,6 +426,14 @@ extern "C" int attn_bwd_get_kernel_times(float* ms_pre, float* ms_main, float* m
     if (ms_pre) *ms_pre = (float)(sum[0] / calls);
     if (ms_main) *ms_main = (float)(sum[1] / calls);
     if (ms_fin) *ms_fin = (float)(sum[2] / calls);
+    return ATTN_OK;
+}
+
+extern "C" int attn_bwd_set_placement(int mode) {
+    if (mode != ATTN_PLACE_GLOBAL && mode != ATTN_PLACE_XCD)
+        return fail(ATTN_ERR_INVALID_ARG, "attn_bwd_set_placement: mode must be ATTN_PLACE_GLOBAL or ATTN_PLACE_XCD");
+    std::lock_guard<std::mutex> lock(g_mutex);
+    g_xcd_placement = mode == ATTN_PLACE_XCD;
     return ATTN_OK;
 }
 

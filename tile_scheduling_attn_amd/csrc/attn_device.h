@@ -50,10 +50,22 @@ template <> struct Elem<float> {
     __device__ static inline float to_f(float x) { return x; }
 };
 
-// Agent-scope coherent (sc1) 16-byte accesses through a raw buffer resource
-// (dword 3 = 0x00020000 is the raw-buffer format word of the gfx9 family;
-// out-of-range offsets read 0 and drop writes).
+// 16-byte accesses through a raw buffer resource (dword 3 = 0x00020000 is
+// the raw-buffer format word of the gfx9 family; out-of-range offsets read 0
+// and drop writes) with a cache policy: sc1 is agent scope (a load misses
+// every cache that is not coherent device-wide, a store is written through
+// to memory), sc0 alone is the scope of the L2 of the issuing XCD (a load
+// misses the CU's L1 and may hit that L2).
 constexpr int kCpolSc1 = 16;
+constexpr int kCpolSc0 = 1;
+__device__ inline f32x4 load_sc0(__amdgpu_buffer_rsrc_t r, unsigned off) {
+    return __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, kCpolSc0));
+}
+// plain store: written to the XCD's L2 (written back to memory later)
+__device__ inline void store_l2(__amdgpu_buffer_rsrc_t r, unsigned off, f32x4 v) {
+    typedef unsigned u32x4_ __attribute__((ext_vector_type(4)));
+    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4_, v), r, (int)off, 0, 0);
+}
 __device__ inline __amdgpu_buffer_rsrc_t make_rsrc(void* base, unsigned bytes) {
     return __builtin_amdgcn_make_buffer_rsrc(base, 0, (int)bytes, 0x00020000);
 }

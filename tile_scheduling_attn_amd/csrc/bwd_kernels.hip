@@ -58,6 +58,25 @@ namespace attn {
 // schedule ends the kernel quickly instead of hanging the device.
 constexpr unsigned kSpinLimit = 1u << 20;
 
+// XCD placement.  A work group takes its items from the queue of the XCD it
+// runs on (HW_REG_XCC_ID), so a head's items run on one or a few XCDs and
+// consecutive contributors of a dQ tile mostly share an L2.  The hardware
+// deals the work groups of a launch to the eight XCDs of MI355X in turn
+// (from an XCD that depends on the hardware queue), so every XCD holds at
+// least grid / 8 of them, which the plan's chunk size fits.  The last work
+// group to finish checks that every queue handed out all of its items.
+// Each XCD keeps its own
+// copy of the accumulator, written only through its own L2: a hand-off
+// between work groups of one XCD stays in that L2 (plain stores, loads that
+// skip only the CU's L1), and only a hand-off to another XCD is written
+// through to memory and read from there.  One writer per copy means no
+// line of a copy is ever dirty in two L2s, so no write-back can overwrite a
+// newer value.  A flag word holds the
+// contributions made so far (bits 0-23), the XCD id (bits 24-27) and queue
+// (bits 28-30) of the last contributor, and whether it wrote its partial
+// through to memory (bit 31).
+constexpr unsigned kRankMask = 0xffffffu, kWroteThrough = 1u << 31;
+
 struct KParams {
     const void *q, *k, *v, *dO;
     const float* lse;
@@ -65,13 +84,18 @@ struct KParams {
     void *dq, *dk, *dv;
     float* dq_acc;
     unsigned* flags;
-    unsigned* ticket;   // counters[0]: next work item
+    unsigned* ticket;   // counters[0]: next work item (one global queue)
+    unsigned* queues;   // kQueues per-XCD tickets, then a count of finished work groups
     unsigned* abort;    // counters[1]: a wait of this call expired
     unsigned* status;   // device status word, reported by attn_bwd_query_status
     unsigned long long* stats;  // null unless wait statistics are on
     const int* item_begin;
     const i32x4* tasks;  // {kv tile, q tile, rank, contributors} per task
     int H, s, n, items_per_head, s_pad;
+    // XCD placement (XcdPlan; chunks == 0: one global queue and one
+    // accumulator, every hand-off through memory)
+    int chunks, chunk_items, groups;
+    long long acc_slots;  // heads of one XCD's accumulator copy
     long long total_items;
     float scale, scale_log2;
 };
@@ -133,6 +157,7 @@ void bwd_main_kernel(KParams p) {
     unsigned char* sK = smem + L::OFF_K;
     T* sdS = reinterpret_cast<T*>(smem + L::OFF_S);
     __shared__ long long s_item;
+    __shared__ unsigned s_prev;  // flag word left by the previous contributor
 
     const int tid = threadIdx.x, lane = tid & 63, g = lane >> 4, c16 = lane & 15;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave index, in an SGPR
@@ -142,6 +167,11 @@ void bwd_main_kernel(KParams p) {
     T* gdK = static_cast<T*>(p.dk);
     T* gdV = static_cast<T*>(p.dv);
     const int s = p.s, n = p.n;
+    unsigned xcc;  // this work group's XCD
+    asm volatile("s_getreg_b32 %0, hwreg(HW_REG_XCC_ID)" : "=s"(xcc));
+    xcc &= 0xfu;
+    const int queue = (int)(xcc % kQueues);  // XCD placement: this XCD's queue
+    if (DET && p.chunks && xcc >= (unsigned)kQueues && tid == 0) atomicOr(p.status, 2u);
 
     unsigned long long wait_cycles = 0, polls = 0, item_cycles = 0;
 
@@ -205,8 +235,24 @@ void bwd_main_kernel(KParams p) {
         }
     };
 
+    // The next work item (head * items_per_head + item of the head), or
+    // total_items when there is none.  XCD placement: queue q belongs to
+    // group q / chunks of `chunks` queues and serves chunk q % chunks of the
+    // group's heads (heads g, g + groups, ...), in head order; every queue
+    // of a group serves the same heads in the same order.
+    auto next_item = [&]() -> long long {
+        if (!DET || p.chunks == 0) return (long long)atomicAdd(p.ticket, 1u);
+        const int grp = queue / p.chunks, lo = (queue % p.chunks) * p.chunk_items;
+        const int size = min(p.chunk_items, p.items_per_head - lo);
+        if (size <= 0) return p.total_items;
+        const unsigned k = atomicAdd(p.queues + queue, 1u);
+        const long long head = grp + (long long)p.groups * (k / (unsigned)size);
+        if (head >= p.H) return p.total_items;
+        return head * p.items_per_head + lo + (int)(k % (unsigned)size);
+    };
+
     for (;;) {
-        if (tid == 0) s_item = (long long)atomicAdd(p.ticket, 1u);
+        if (tid == 0) s_item = next_item();
         __syncthreads();
         const long long item = s_item;
         __syncthreads();
@@ -351,10 +397,11 @@ void bwd_main_kernel(KParams p) {
                 const int diag_off = (qt - kv) * TILE;
 
                 const int rank = DET ? __builtin_amdgcn_readfirstlane(rec[2]) : 0;
-                const int cnt = DET ? __builtin_amdgcn_readfirstlane(rec[3]) : 1;
+                // item of the Q tile's next contributor (-1: this is the last)
+                const int succ = DET ? __builtin_amdgcn_readfirstlane(rec[3]) : -1;
                 unsigned* flag = p.flags + (size_t)head * n + qt;
                 unsigned early = 0;  // tid 0: the flag as read before the last sub-step
-                float* acc = p.dq_acc + (size_t)head * p.s_pad * D;
+                float* acc = p.dq_acc + (size_t)head * p.s_pad * D;  // atomic variant
 
 #pragma unroll 1
                 for (int sub = 0; sub < NSUB; ++sub) {
@@ -674,7 +721,7 @@ void bwd_main_kernel(KParams p) {
                     const unsigned long long t0 = p.stats ? __builtin_readcyclecounter() : 0;
                     unsigned spins = 0;
                     unsigned seen = early;
-                    while (seen != (unsigned)rank) {
+                    while ((seen & kRankMask) != (unsigned)rank) {
                         if ((spins & 1023u) == 0 && __hip_atomic_load(p.abort, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT))
                             break;
                         __builtin_amdgcn_s_sleep(1);
@@ -689,10 +736,27 @@ void bwd_main_kernel(KParams p) {
                         wait_cycles += __builtin_readcyclecounter() - t0;
                         polls += spins + 1;
                     }
+                    s_prev = seen;
                 }
                 __syncthreads();
                 if (DET) {
-                    const __amdgpu_buffer_rsrc_t racc = make_rsrc(acc, (unsigned)(p.s_pad * D * sizeof(float)));
+                    // this head's accumulator in the copy of queue qc
+                    auto acc_copy = [&](unsigned qc) {
+                        const size_t slot = p.chunks ? (size_t)qc * p.acc_slots + head / p.groups : (size_t)head;
+                        return make_rsrc(p.dq_acc + slot * p.s_pad * D, (unsigned)(p.s_pad * D * sizeof(float)));
+                    };
+                    // the previous contribution: from this XCD's L2 when it was made
+                    // on this XCD, else from memory (where the contributor wrote it
+                    // through; a hand-off between XCDs that was not written through
+                    // means the work groups did not run where placement put them)
+                    const unsigned pflag = rank > 0 ? __builtin_amdgcn_readfirstlane(s_prev) : 0u;
+                    const bool same = ((pflag >> 24) & 0xfu) == xcc;
+                    if (rank > 0 && !same && !(pflag & kWroteThrough) && tid == 0) atomicOr(p.status, 2u);
+                    const __amdgpu_buffer_rsrc_t rprev = acc_copy((pflag >> 28) & 7u), racc = acc_copy(queue);
+                    // write through unless the next contributor's item is served
+                    // by this work group's queue
+                    const bool wt = !p.chunks || succ < 0 ||
+                                    (queue / p.chunks) * p.chunks + succ / p.chunk_items != queue;
                     const int col0 = w * DW + 4 * g;
                     // The accumulator is stored as whole 16x16 tiles in the MFMA
                     // output layout (lane l's 4 values at 16*l bytes of the
@@ -708,47 +772,72 @@ void bwd_main_kernel(KParams p) {
                     constexpr int NPREV = NDT * MTT, NSTEP = NSUB * KSKV, PER = (NPREV + NSTEP - 1) / NSTEP;
                     f32x4 prev[NDT][MTT];
                     f32x4 dq[NSUB][NDT][MT];
-                    static_for<0, NSUB>([&](auto pc) {
-                        constexpr int part = decltype(pc)::value;
-                        dq_rows(dq[part], part * BQ, [&](auto ksc) {
-                            // (rank 0 does not use them: no branch for it)
-                            constexpr int step = part * KSKV + decltype(ksc)::value;
-                            static_for<0, PER>([&](auto jc) {
-                                constexpr int i = step * PER + decltype(jc)::value;
-                                if constexpr (i < NPREV)
-                                    prev[i / MTT][i % MTT] = load_sc1(racc, acc_off(i % MTT, i / MTT));
+                    // one copy of the contraction per load policy (a policy is an
+                    // immediate of the load: no branch between the MFMAs)
+                    auto contract = [&](auto polc) {
+                        constexpr int POL = decltype(polc)::value;
+                        static_for<0, NSUB>([&](auto pc) {
+                            constexpr int part = decltype(pc)::value;
+                            dq_rows(dq[part], part * BQ, [&](auto ksc) {
+                                // (rank 0 does not use them: no branch for it)
+                                constexpr int step = part * KSKV + decltype(ksc)::value;
+                                static_for<0, PER>([&](auto jc) {
+                                    constexpr int i = step * PER + decltype(jc)::value;
+                                    if constexpr (i < NPREV)
+                                        prev[i / MTT][i % MTT] = __builtin_bit_cast(
+                                            f32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                                                       rprev, (int)acc_off(i % MTT, i / MTT), 0, POL));
+                                });
+                                // keep them here: the scheduler would otherwise sink
+                                // every load below the contraction
+                                __builtin_amdgcn_sched_barrier(0);
                             });
-                            // keep them here: the scheduler would otherwise sink
-                            // every load below the contraction
-                            __builtin_amdgcn_sched_barrier(0);
                         });
-                    });
+                    };
+                    if (same)
+                        contract(std::integral_constant<int, kCpolSc0>{});
+                    else
+                        contract(std::integral_constant<int, kCpolSc1>{});
+                    // the sums, as the output dQ (last contributor), or stored
+                    // through to memory, or into this XCD's L2: one copy each
+                    auto emit = [&](auto modec) {
+                        constexpr int MODE = decltype(modec)::value;  // 0 output, 1 through, 2 L2
 #pragma unroll
-                    for (int part = 0; part < NSUB; ++part) {
+                        for (int part = 0; part < NSUB; ++part) {
 #pragma unroll
-                        for (int dtw = 0; dtw < NDT; ++dtw)
+                            for (int dtw = 0; dtw < NDT; ++dtw)
 #pragma unroll
-                            for (int mt = 0; mt < MT; ++mt) {
-                                const int mtt = part * MT + mt;  // 16-row tile of the task's Q tile
-                                f32x4 v = dq[part][dtw][mt];
-                                if (rank > 0) v = prev[dtw][mtt] + v;
-                                const int row = qt * TILE + mtt * 16 + c16;
-                                if (rank == cnt - 1) {
-                                    // the last contributor writes dQ = scale * sum in the output type
-                                    V4 o;
+                                for (int mt = 0; mt < MT; ++mt) {
+                                    const int mtt = part * MT + mt;  // 16-row tile of the task's Q tile
+                                    f32x4 v = dq[part][dtw][mt];
+                                    if (rank > 0) v = prev[dtw][mtt] + v;
+                                    if constexpr (MODE == 0) {
+                                        // dQ = scale * sum in the output type
+                                        const int row = qt * TILE + mtt * 16 + c16;
+                                        V4 o;
 #pragma unroll
-                                    for (int e = 0; e < 4; ++e) o[e] = E::from_f(p.scale * v[e]);
-                                    if (row < s) *reinterpret_cast<V4*>(gdQ + hoff + (size_t)row * D + col0 + dtw * 16) = o;
-                                } else {
-                                    store_sc1(racc, acc_off(mtt, dtw), v);
+                                        for (int e = 0; e < 4; ++e) o[e] = E::from_f(p.scale * v[e]);
+                                        if (row < s)
+                                            *reinterpret_cast<V4*>(gdQ + hoff + (size_t)row * D + col0 + dtw * 16) = o;
+                                    } else if constexpr (MODE == 1) {
+                                        store_sc1(racc, acc_off(mtt, dtw), v);
+                                    } else {
+                                        store_l2(racc, acc_off(mtt, dtw), v);
+                                    }
                                 }
-                            }
-                    }
-                    if (rank != cnt - 1) {
+                        }
+                    };
+                    if (succ < 0)
+                        emit(std::integral_constant<int, 0>{});
+                    else if (wt)
+                        emit(std::integral_constant<int, 1>{});
+                    else
+                        emit(std::integral_constant<int, 2>{});
+                    if (succ >= 0) {
                         // published after the next barrier that follows a full
                         // s_waitcnt (next task's staging, or the end of the item)
                         pend_flag = flag;
-                        pend_val = (unsigned)(rank + 1);
+                        pend_val = (unsigned)(rank + 1) | (xcc << 24) | ((unsigned)queue << 28) | (wt ? kWroteThrough : 0u);
                     }
                 } else {
 #pragma unroll
@@ -780,6 +869,18 @@ void bwd_main_kernel(KParams p) {
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
         if (pend_flag) publish();
         if (p.stats) item_cycles += __builtin_readcyclecounter() - t_item0;
+    }
+    // XCD placement: the last work group to finish checks that every queue
+    // handed out all of its items (an XCD without work groups would leave
+    // its items undone)
+    if (DET && p.chunks && tid == 0 && atomicAdd(p.queues + kQueues, 1u) == gridDim.x - 1) {
+        for (int q = 0; q < kQueues; ++q) {
+            const int grp = q / p.chunks, lo = (q % p.chunks) * p.chunk_items;
+            const int size = min(p.chunk_items, p.items_per_head - lo);
+            const long long heads = grp < p.H ? (p.H - grp + p.groups - 1) / p.groups : 0;
+            const unsigned handed = __hip_atomic_load(p.queues + q, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            if (size > 0 && (long long)handed < heads * size) atomicOr(p.status, 2u);
+        }
     }
     if (p.stats && tid == 0) {
         atomicAdd(p.stats + 0, wait_cycles);
@@ -841,6 +942,36 @@ __global__ __launch_bounds__(256) void bwd_finalize_kernel(const float* __restri
 // ---------------------------------------------------------------------------
 // Launch
 // ---------------------------------------------------------------------------
+// Records the XCD of every work group (one wave each).
+__global__ __launch_bounds__(64) void xcd_probe_kernel(unsigned* out) {
+    unsigned x;
+    asm volatile("s_getreg_b32 %0, hwreg(HW_REG_XCC_ID)" : "=s"(x));
+    if (threadIdx.x == 0) out[blockIdx.x] = x & 0xfu;
+}
+
+// Placement needs XCD ids 0..kQueues-1, each dealt an equal share of a grid.
+int probe_xcd_dispatch(int num_cus, bool* ok) {
+    *ok = false;
+    if (num_cus < kQueues || num_cus % kQueues) return ATTN_OK;
+    const int grid = 4 * num_cus;
+    unsigned* d = nullptr;
+    if (hipMalloc(&d, grid * sizeof(unsigned)) != hipSuccess) return fail(ATTN_ERR_HIP, "hipMalloc(xcd probe)");
+    std::vector<unsigned> h(grid, ~0u);
+    hipLaunchKernelGGL(xcd_probe_kernel, dim3(grid), dim3(64), 0, 0, d);
+    hipError_t e = hipGetLastError();
+    if (e == hipSuccess) e = hipMemcpy(h.data(), d, grid * sizeof(unsigned), hipMemcpyDeviceToHost);
+    if (hipFree(d) != hipSuccess || e != hipSuccess) return fail(ATTN_ERR_HIP, "XCD probe kernel failed");
+    std::vector<int> per(kQueues, 0);
+    bool all = true;
+    for (int b = 0; b < grid; ++b) {
+        all = all && h[b] < (unsigned)kQueues;
+        if (h[b] < (unsigned)kQueues) per[h[b]]++;
+    }
+    for (int q = 0; q < kQueues; ++q) all = all && per[q] == grid / kQueues;
+    *ok = all;
+    return ATTN_OK;
+}
+
 template <typename T, int D, int TILE, bool CAUSAL, bool DET>
 static int launch_main_t(const KParams& kp, const BwdLaunch& L) {
     auto kern = bwd_main_kernel<T, D, TILE, CAUSAL, DET>;
@@ -862,7 +993,18 @@ static int launch_main_t(const KParams& kp, const BwdLaunch& L) {
                     "schedule needs more simultaneously resident work groups than the device holds");
     const long long grid = std::min<long long>(resident, kp.total_items);
     if (grid <= 0) return ATTN_OK;
-    hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(nthreads), smem, (hipStream_t)L.stream, kp);
+    KParams k = kp;
+    // the XCD plan was made for one work group per CU: it holds for any
+    // larger grid (checked anyway; the accumulator always has room for the
+    // global queue's one copy)
+    const XcdPlan& pl = L.plan;
+    if (DET && pl.chunks && grid / kQueues >= 1 && (L.min_workers <= 1 || pl.chunk_items <= grid / kQueues)) {
+        k.chunks = pl.chunks;
+        k.chunk_items = pl.chunk_items;
+        k.groups = pl.groups;
+        k.acc_slots = pl.slots;
+    }
+    hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(nthreads), smem, (hipStream_t)L.stream, k);
     if (hipGetLastError() != hipSuccess) return fail(ATTN_ERR_HIP, "main kernel launch failed");
     return ATTN_OK;
 }
@@ -925,6 +1067,7 @@ int launch_backward(const BwdArgs& a, const BwdLaunch& L) {
     kp.dq_acc = a.dq_acc;
     kp.flags = a.flags;
     kp.ticket = a.counters;
+    kp.queues = a.counters + kQueueWord;
     kp.abort = a.counters + 1;
     kp.status = L.status;
     kp.stats = L.stats;

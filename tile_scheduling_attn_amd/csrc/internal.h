@@ -41,9 +41,28 @@ struct BwdArgs {
     float* dq_acc;
     float* delta;
     unsigned* flags;
-    unsigned* counters;   // [0] ticket, [1..] wait statistics
+    unsigned* counters;   // [0] ticket, [1] abort, [2..] wait statistics, [kQueueWord..] XCD queues
+    long long acc_slots;  // heads of dq_acc: H, or kQueues copies of XcdPlan::slots
     size_t s_pad;
 };
+
+// Work queues of XCD placement (one per XCD of MI355X).
+constexpr int kQueues = 8;
+
+// XCD placement of a deterministic launch: a head's items split into
+// `chunks` runs of `chunk_items`; queue q serves chunk q % chunks of the heads
+// g, g + groups, ... (g = q / chunks, groups = kQueues / chunks).  Each XCD
+// keeps its own dQ accumulator of `slots` heads (head h in slot h / groups).
+struct XcdPlan {
+    int chunks = 0, chunk_items = 0, groups = 0;
+    long long slots = 0;
+};
+// The plan for `grid` resident work groups, or chunks == 0 when the launch
+// keeps the global queue.  item_begin: the schedule's items_per_head + 1
+// task offsets (the work of each item).
+XcdPlan xcd_plan(const std::vector<int>& item_begin, int min_workers, long long grid, long long heads);
+// Whether work group b of a launch runs on XCD b % kQueues on this device.
+int probe_xcd_dispatch(int num_cus, bool* ok);
 
 // Launch-time context prepared by the API layer (device pointers).
 struct BwdLaunch {
@@ -57,7 +76,11 @@ struct BwdLaunch {
     const int* tasks;             // 4 ints per task: kv, q, rank, contributors
     int items_per_head;
     int nclear32;                 // flags + counters words to clear
+    XcdPlan plan;                 // XCD placement (chunks == 0: one global queue)
 };
+
+// first counter word of the per-XCD work queues
+constexpr int kQueueWord = 48;
 
 int launch_backward(const BwdArgs& a, const BwdLaunch& L);
 

@@ -117,6 +117,36 @@ int build_schedule(int n, bool causal, int schedule, Schedule& out) {
     return ATTN_OK;
 }
 
+// The fewest chunks (1, 2, 4 or 8 per head) whose size fits the work groups
+// of one queue.  A schedule whose items must all be resident at once
+// (min_workers > 1) needs that fit; the others only ever wait on items of
+// the head taken earlier from the same or a lower queue of the group, so any
+// chunk size keeps them deadlock-free.  The XCDs of a group work on the same
+// heads in step, so the chunks must also carry about equal work (within
+// kChunkImbalance of the mean); a causal head's consecutive items do not.
+constexpr double kChunkImbalance = 1.1;
+
+XcdPlan xcd_plan(const std::vector<int>& item_begin, int min_workers, long long grid, long long heads) {
+    XcdPlan p;
+    const int items_per_head = (int)item_begin.size() - 1;
+    const long long per_queue = grid / kQueues;
+    if (per_queue < 1 || items_per_head < 1 || heads < 1) return p;
+    int g = 1;
+    while (g < kQueues && (items_per_head + g - 1) / g > per_queue) g *= 2;
+    const int c = (items_per_head + g - 1) / g;
+    if (min_workers > 1 && c > per_queue) return p;
+    const double mean = (double)(item_begin[items_per_head] - item_begin[0]) / g;
+    for (int k = 0; k < g; ++k) {
+        const int lo = std::min(k * c, items_per_head), hi = std::min((k + 1) * c, items_per_head);
+        if (item_begin[hi] - item_begin[lo] > kChunkImbalance * mean) return p;
+    }
+    p.chunks = g;
+    p.chunk_items = c;
+    p.groups = kQueues / g;
+    p.slots = (heads + p.groups - 1) / p.groups;
+    return p;
+}
+
 int min_workers(const Schedule& sc) {
     if (sc.schedule == ATTN_SCHED_NAIVE || sc.schedule == ATTN_SCHED_DESCENDING ||
         sc.schedule == ATTN_SCHED_ATOMIC)
