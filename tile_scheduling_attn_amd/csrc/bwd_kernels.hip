@@ -95,6 +95,7 @@ struct KParams {
     // XCD placement (XcdPlan; chunks == 0: one global queue and one
     // accumulator, every hand-off through memory)
     int chunks, chunk_items, groups;
+    int chunk_shift, group_shift;  // log2 of chunks and of groups (both powers of two)
     long long acc_slots;  // heads of one XCD's accumulator copy
     long long total_items;
     float scale, scale_log2;
@@ -171,36 +172,51 @@ void bwd_main_kernel(KParams p) {
     asm volatile("s_getreg_b32 %0, hwreg(HW_REG_XCC_ID)" : "=s"(xcc));
     xcc &= 0xfu;
     const int queue = (int)(xcc % kQueues);  // XCD placement: this XCD's queue
+    // the items of a head that this queue serves: [chunk_lo(), chunk_hi())
+    auto chunk_lo = [&]() { return (queue & (p.chunks - 1)) * p.chunk_items; };
+    auto chunk_hi = [&]() { return min(chunk_lo() + p.chunk_items, p.items_per_head); };
     if (DET && p.chunks && xcc >= (unsigned)kQueues && tid == 0) atomicOr(p.status, 2u);
 
     unsigned long long wait_cycles = 0, polls = 0, item_cycles = 0;
 
-    // dQ^T (deterministic) or dQ (atomic) of query rows [r0, r0 + BQ) of
-    // the task's tile, for this wave's DW columns, contracted over the whole
-    // KV tile: A = K^T from sK (transposed reads), B = dS rows from sdS.
-    // Deterministic: C[d][q], a lane holds 4 consecutive d of one query row
-    // (16-byte accumulator accesses).  Atomic: C[q][d], 16 lanes hold 16
-    // consecutive d of one row (64 contiguous bytes per atomic instruction).
-    // hook(std::integral_constant<int, ks>) runs at the start of each 32-key
-    // step, so that a caller can spread other instructions over the steps.
-    auto dq_rows = [&](f32x4 (&acc)[NDT][MT], int r0, auto&& hook) {
+    // dQ^T (deterministic) or dQ (atomic) of the task's whole Q tile, as
+    // NSUB parts of BQ query rows, for this wave's DW columns, contracted
+    // over the whole KV tile: A = K^T from sK (transposed reads), B = dS rows
+    // from sdS.  Deterministic: C[d][q], a lane holds 4 consecutive d of one
+    // query row (16-byte accumulator accesses).  Atomic: C[q][d], 16 lanes
+    // hold 16 consecutive d of one row (64 contiguous bytes per atomic
+    // instruction).  The loop runs over (32-key step, part) pairs, part
+    // fastest, so each K^T operand feeds every part; the dS operands are
+    // read two pairs ahead and the K^T operands one key step ahead of the
+    // MFMAs that use them.  hook(std::integral_constant<int, pair>) runs at
+    // the start of each pair, so that a caller can spread other instructions
+    // over them.
+    auto dq_tile = [&](f32x4 (&acc)[NSUB][NDT][MT], auto&& hook) {
 #pragma unroll
-        for (int dtw = 0; dtw < NDT; ++dtw)
+        for (int part = 0; part < NSUB; ++part)
 #pragma unroll
-            for (int mt = 0; mt < MT; ++mt) acc[dtw][mt] = zero_vec<f32x4>();
-        auto step = [&](int ks, const V8 (&a)[NDT]) {
-            V8 b[MT];
+            for (int dtw = 0; dtw < NDT; ++dtw)
+#pragma unroll
+                for (int mt = 0; mt < MT; ++mt) acc[part][dtw][mt] = zero_vec<f32x4>();
+        constexpr int NP = KSKV * NSUB;
+        auto load_b = [&](auto pc, V8 (&b)[MT]) {
+            constexpr int pi = decltype(pc)::value, ks = pi / NSUB, part = pi % NSUB;
 #pragma unroll
             for (int mt = 0; mt < MT; ++mt)
-                b[mt] = *reinterpret_cast<const V8*>(sdS + (r0 + mt * 16 + c16) * LDSS + ks * 32 + 8 * g);
+                b[mt] = *reinterpret_cast<const V8*>(sdS + (part * BQ + mt * 16 + c16) * LDSS + ks * 32 + 8 * g);
+        };
+        auto mm = [&](int part, const V8 (&a)[NDT], const V8 (&b)[MT]) {
 #pragma unroll
             for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
                 for (int dtw = 0; dtw < NDT; ++dtw)
-                    acc[dtw][mt] = DET ? E::mma(acc[dtw][mt], a[dtw], b[mt]) : E::mma(acc[dtw][mt], b[mt], a[dtw]);
+                    acc[part][dtw][mt] = DET ? E::mma(acc[part][dtw][mt], a[dtw], b[mt])
+                                             : E::mma(acc[part][dtw][mt], b[mt], a[dtw]);
         };
+        V8 b[3][MT];  // dS operands, ring of three pairs
+        load_b(std::integral_constant<int, 0>{}, b[0]);
+        if constexpr (NP > 1) load_b(std::integral_constant<int, 1>{}, b[1]);
         if constexpr (sizeof(T) == 2) {
-            // K^T operands one 32-key step ahead of the MFMAs that use them
             using P = Pad<T, D>;
             const lds_u8* tk = lsm + L::OFF_K + (8 * g + (c16 >> 2)) * P::RS + (w * DW + 4 * (c16 & 3)) * 2;
             auto fetch = [&](auto ksc, V8 (&a)[NDT]) {
@@ -210,27 +226,27 @@ void bwd_main_kernel(KParams p) {
                     a[decltype(jc)::value] = tr_frag<o, o + 4 * P::RS>(tk);
                 });
             };
-            V8 cur[NDT], nxt[NDT];
-            fetch(std::integral_constant<int, 0>{}, cur);
-            static_for<0, KSKV>([&](auto ksc) {
-                constexpr int ks = decltype(ksc)::value;
-                if constexpr (ks + 1 < KSKV) fetch(std::integral_constant<int, ks + 1>{}, nxt);
-                hook(ksc);
-                step(ks, cur);
-                if constexpr (ks + 1 < KSKV) {
-#pragma unroll
-                    for (int j = 0; j < NDT; ++j) cur[j] = nxt[j];
-                }
+            V8 a[2][NDT];  // K^T operands, ring of two key steps
+            fetch(std::integral_constant<int, 0>{}, a[0]);
+            static_for<0, NP>([&](auto pc) {
+                constexpr int pi = decltype(pc)::value, ks = pi / NSUB, part = pi % NSUB;
+                if constexpr (part == 0 && ks + 1 < KSKV) fetch(std::integral_constant<int, ks + 1>{}, a[(ks + 1) % 2]);
+                if constexpr (pi + 2 < NP) load_b(std::integral_constant<int, pi + 2>{}, b[(pi + 2) % 3]);
+                hook(pc);
+                mm(part, a[ks % 2], b[pi % 3]);
             });
         } else {
-            static_for<0, KSKV>([&](auto ksc) {
-                constexpr int ks = decltype(ksc)::value;
-                V8 a[NDT];
+            V8 a[NDT];
+            static_for<0, NP>([&](auto pc) {
+                constexpr int pi = decltype(pc)::value, ks = pi / NSUB, part = pi % NSUB;
+                if constexpr (part == 0) {
 #pragma unroll
-                for (int dtw = 0; dtw < NDT; ++dtw)
-                    a[dtw] = frag_col<T, D>(sK, ks * 32 + 8 * g, ks * 32 + 8 * g + 4, w * DW + dtw * 16, c16);
-                hook(ksc);
-                step(ks, a);
+                    for (int dtw = 0; dtw < NDT; ++dtw)
+                        a[dtw] = frag_col<T, D>(sK, ks * 32 + 8 * g, ks * 32 + 8 * g + 4, w * DW + dtw * 16, c16);
+                }
+                if constexpr (pi + 2 < NP) load_b(std::integral_constant<int, pi + 2>{}, b[(pi + 2) % 3]);
+                hook(pc);
+                mm(part, a, b[pi % 3]);
             });
         }
     };
@@ -242,8 +258,7 @@ void bwd_main_kernel(KParams p) {
     // of a group serves the same heads in the same order.
     auto next_item = [&]() -> long long {
         if (!DET || p.chunks == 0) return (long long)atomicAdd(p.ticket, 1u);
-        const int grp = queue / p.chunks, lo = (queue % p.chunks) * p.chunk_items;
-        const int size = min(p.chunk_items, p.items_per_head - lo);
+        const int grp = queue >> p.chunk_shift, lo = chunk_lo(), size = chunk_hi() - lo;
         if (size <= 0) return p.total_items;
         const unsigned k = atomicAdd(p.queues + queue, 1u);
         const long long head = grp + (long long)p.groups * (k / (unsigned)size);
@@ -572,8 +587,17 @@ void bwd_main_kernel(KParams p) {
                         using P = Pad<T, D>;
                         constexpr int A = 8 * KSD, B = 4 * DT, NMF = 2 * A + 2 * B;
                         constexpr int ODO = L::OFF_DO - L::OFF_Q;
-                        V8 q1[3][2], o1[3][2];  // phase-1 operands, ring of 3 steps: [step][m]
-                        s16x4 t2[3][2][2];      // phase-2 operands, ring of 3 steps: [step][Q/dO][lo/hi]
+                        // phase-1 operands, PF1 steps ahead (a ring of PF1 + 1): [step][m]
+                        constexpr int PF1 = 2, R1 = PF1 + 1;
+                        V8 q1[R1][2], o1[R1][2];
+                        // phase-2 operands, PF2 steps ahead of their MFMAs (a ring of
+                        // PF2 + 1 steps): [step][Q/dO][lo/hi].  A wave's LDS throughput
+                        // is what it has in flight over the LDS latency (~270 cycles
+                        // under load), and a transposing read moves 512 bytes, so the
+                        // 2 KiB that a phase-2 step consumes per 64 MFMA cycles need
+                        // several steps in flight.
+                        constexpr int PF2 = 4, R2 = PF2 + 1;
+                        s16x4 t2[R2][2][2];
                         f32x4 lsev[2][2], delv[2][2];  // [group][m]: lse and D of rows 4g..4g+3
                         const lds_u8* tq = (const lds_u8*)sQ + (4 * g + (c16 >> 2)) * P::RS + 8 * (c16 & 3);
                         // read k (0..3) of phase-1 step j = (group, 32-wide d step)
@@ -581,16 +605,16 @@ void bwd_main_kernel(KParams p) {
                             constexpr int j = decltype(jc)::value, k = decltype(kc)::value;
                             constexpr int G = j / KSD, ks = j % KSD, m = k % 2;
                             if constexpr (k < 2)
-                                q1[j % 3][m] = frag_row<T, D>(sQ, (2 * G + m) * 16 + c16, ks * 32 + 8 * g);
+                                q1[j % R1][m] = frag_row<T, D>(sQ, (2 * G + m) * 16 + c16, ks * 32 + 8 * g);
                             else
-                                o1[j % 3][m] = frag_row<T, D>(sdO, (2 * G + m) * 16 + c16, ks * 32 + 8 * g);
+                                o1[j % R1][m] = frag_row<T, D>(sdO, (2 * G + m) * 16 + c16, ks * 32 + 8 * g);
                         };
                         // transposed read k (0..3) of phase-2 step u = (group, 16-wide d step)
                         auto rd2 = [&](auto uc, auto kc) {
                             constexpr int u = decltype(uc)::value, k = decltype(kc)::value;
                             constexpr int G = u / DT, dt = u % DT, isdo = k / 2, hi = k % 2;
                             constexpr int o = G * 32 * P::RS + dt * 32 + isdo * ODO + hi * 16 * P::RS;
-                            t2[u % 3][isdo][hi] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(tq + o));
+                            t2[u % R2][isdo][hi] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(tq + o));
                         };
                         auto op2 = [&](int slot, int isdo) {
                             return __builtin_bit_cast(V8, __builtin_shufflevector(t2[slot][isdo][0], t2[slot][isdo][1], 0,
@@ -626,16 +650,16 @@ void bwd_main_kernel(KParams p) {
                                 constexpr int G = i / A, r = i % A, ks = r / 8, m = (r % 8) / 4, nt = (r % 4) / 2;
                                 constexpr int j = G * KSD + ks;
                                 if constexpr (r % 2 == 0)
-                                    S[G][m][nt] = E::mma(S[G][m][nt], q1[j % 3][m], Kr[nt][ks]);
+                                    S[G][m][nt] = E::mma(S[G][m][nt], q1[j % R1][m], Kr[nt][ks]);
                                 else
-                                    dP[G][m][nt] = E::mma(dP[G][m][nt], o1[j % 3][m], Vr[nt][ks]);
+                                    dP[G][m][nt] = E::mma(dP[G][m][nt], o1[j % R1][m], Vr[nt][ks]);
                             } else {
                                 constexpr int i2 = i - 2 * A, G = i2 / B, r = i2 % B, dt = r / 4, nt = (r % 4) / 2;
                                 constexpr int u = G * DT + dt;
                                 if constexpr (r % 2 == 0)
-                                    dV[nt][dt] = E::mma(dV[nt][dt], aP[G][nt], op2(u % 3, 1));
+                                    dV[nt][dt] = E::mma(dV[nt][dt], aP[G][nt], op2(u % R2, 1));
                                 else
-                                    dK[nt][dt] = E::mma(dK[nt][dt], aS[G][nt], op2(u % 3, 0));
+                                    dK[nt][dt] = E::mma(dK[nt][dt], aS[G][nt], op2(u % R2, 0));
                             }
                         };
                         // S starts at 0, or at -inf where P must be 0: key rows
@@ -666,8 +690,9 @@ void bwd_main_kernel(KParams p) {
                         }
                         using I0 = std::integral_constant<int, 0>;
                         using I1 = std::integral_constant<int, 1>;
-                        static_for<0, 4>([&](auto kc) { rd1(I0{}, kc); });
-                        static_for<0, 4>([&](auto kc) { rd1(I1{}, kc); });
+                        static_for<0, PF1>([&](auto jc) {
+                            static_for<0, 4>([&](auto kc) { rd1(jc, kc); });
+                        });
                         static_for<0, NMF>([&](auto ic) {
                             constexpr int i = decltype(ic)::value;
                             mfma(ic);
@@ -675,20 +700,20 @@ void bwd_main_kernel(KParams p) {
                             constexpr int DSTEP = (2 * A - 8) / NSLOT;
                             if constexpr (i % DSTEP == 1 && i / DSTEP < NSLOT)
                                 issue_slot(std::integral_constant<int, i / DSTEP>{}, pf_buf, q_next);
-                            // phase-1 operands: step j during step j - 2, one read per two MFMAs
-                            if constexpr (i < 2 * A - 16 && i % 2 == 0)
-                                rd1(std::integral_constant<int, i / 8 + 2>{}, std::integral_constant<int, (i % 8) / 2>{});
+                            // phase-1 operands: step j during step j - PF1, one read per two MFMAs
+                            if constexpr (i < 2 * A - 8 * PF1 && i % 2 == 0)
+                                rd1(std::integral_constant<int, i / 8 + PF1>{}, std::integral_constant<int, (i % 8) / 2>{});
                             // lse and D of a group, a step before its softmax starts
                             if constexpr (i % 2 == 1 && i >= A - 16 && i < A - 8)
                                 rd_lse(I0{}, std::integral_constant<int, (i - (A - 16)) / 2>{});
                             if constexpr (i % 2 == 1 && i >= 2 * A - 16 && i < 2 * A - 8)
                                 rd_lse(I1{}, std::integral_constant<int, (i - (2 * A - 16)) / 2>{});
-                            // phase-2 operands: steps 0 and 1 during the last phase-1
-                            // step, step u during step u - 2
-                            if constexpr (i >= 2 * A - 8 && i < 2 * A)
-                                rd2(std::integral_constant<int, (i - (2 * A - 8)) / 4>{}, std::integral_constant<int, i % 4>{});
-                            if constexpr (i >= 2 * A && i < 2 * A + 2 * B - 8)
-                                rd2(std::integral_constant<int, (i - 2 * A) / 4 + 2>{}, std::integral_constant<int, i % 4>{});
+                            // phase-2 operands: steps 0 .. PF2-1 during the last PF2 / 2
+                            // phase-1 steps, step u during step u - PF2
+                            if constexpr (i >= 2 * A - 4 * PF2 && i < 2 * A)
+                                rd2(std::integral_constant<int, (i - (2 * A - 4 * PF2)) / 4>{}, std::integral_constant<int, i % 4>{});
+                            if constexpr (i >= 2 * A && i < 2 * A + 2 * B - 4 * PF2)
+                                rd2(std::integral_constant<int, (i - 2 * A) / 4 + PF2>{}, std::integral_constant<int, i % 4>{});
                             // softmax of group 0 beside phase 1 of group 1, of group 1
                             // beside phase 2 of group 0
                             if constexpr (i >= A && i < 2 * A && (i - A) % (A / 8) == 0)
@@ -742,7 +767,7 @@ void bwd_main_kernel(KParams p) {
                 if (DET) {
                     // this head's accumulator in the copy of queue qc
                     auto acc_copy = [&](unsigned qc) {
-                        const size_t slot = p.chunks ? (size_t)qc * p.acc_slots + head / p.groups : (size_t)head;
+                        const size_t slot = p.chunks ? (size_t)qc * p.acc_slots + (head >> p.group_shift) : (size_t)head;
                         return make_rsrc(p.dq_acc + slot * p.s_pad * D, (unsigned)(p.s_pad * D * sizeof(float)));
                     };
                     // the previous contribution: from this XCD's L2 when it was made
@@ -755,8 +780,7 @@ void bwd_main_kernel(KParams p) {
                     const __amdgpu_buffer_rsrc_t rprev = acc_copy((pflag >> 28) & 7u), racc = acc_copy(queue);
                     // write through unless the next contributor's item is served
                     // by this work group's queue
-                    const bool wt = !p.chunks || succ < 0 ||
-                                    (queue / p.chunks) * p.chunks + succ / p.chunk_items != queue;
+                    const bool wt = !p.chunks || succ < chunk_lo() || succ >= chunk_hi();
                     const int col0 = w * DW + 4 * g;
                     // The accumulator is stored as whole 16x16 tiles in the MFMA
                     // output layout (lane l's 4 values at 16*l bytes of the
@@ -776,22 +800,19 @@ void bwd_main_kernel(KParams p) {
                     // immediate of the load: no branch between the MFMAs)
                     auto contract = [&](auto polc) {
                         constexpr int POL = decltype(polc)::value;
-                        static_for<0, NSUB>([&](auto pc) {
-                            constexpr int part = decltype(pc)::value;
-                            dq_rows(dq[part], part * BQ, [&](auto ksc) {
-                                // (rank 0 does not use them: no branch for it)
-                                constexpr int step = part * KSKV + decltype(ksc)::value;
-                                static_for<0, PER>([&](auto jc) {
-                                    constexpr int i = step * PER + decltype(jc)::value;
-                                    if constexpr (i < NPREV)
-                                        prev[i / MTT][i % MTT] = __builtin_bit_cast(
-                                            f32x4, __builtin_amdgcn_raw_buffer_load_b128(
-                                                       rprev, (int)acc_off(i % MTT, i / MTT), 0, POL));
-                                });
-                                // keep them here: the scheduler would otherwise sink
-                                // every load below the contraction
-                                __builtin_amdgcn_sched_barrier(0);
+                        dq_tile(dq, [&](auto pc) {
+                            // (rank 0 does not use them: no branch for it)
+                            constexpr int step = decltype(pc)::value;
+                            static_for<0, PER>([&](auto jc) {
+                                constexpr int i = step * PER + decltype(jc)::value;
+                                if constexpr (i < NPREV)
+                                    prev[i / MTT][i % MTT] = __builtin_bit_cast(
+                                        f32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                                                   rprev, (int)acc_off(i % MTT, i / MTT), 0, POL));
                             });
+                            // keep them here: the scheduler would otherwise sink
+                            // every load below the contraction
+                            __builtin_amdgcn_sched_barrier(0);
                         });
                     };
                     if (same)
@@ -840,10 +861,10 @@ void bwd_main_kernel(KParams p) {
                         pend_val = (unsigned)(rank + 1) | (xcc << 24) | ((unsigned)queue << 28) | (wt ? kWroteThrough : 0u);
                     }
                 } else {
+                    f32x4 dq[NSUB][NDT][MT];
+                    dq_tile(dq, [](auto) {});
 #pragma unroll
-                    for (int part = 0; part < NSUB; ++part) {
-                        f32x4 dq[NDT][MT];
-                        dq_rows(dq, part * BQ, [](auto) {});
+                    for (int part = 0; part < NSUB; ++part)
 #pragma unroll
                         for (int dtw = 0; dtw < NDT; ++dtw)
 #pragma unroll
@@ -852,8 +873,7 @@ void bwd_main_kernel(KParams p) {
                                 for (int i = 0; i < 4; ++i)
                                     unsafeAtomicAdd(acc + (size_t)(qt * TILE + part * BQ + mt * 16 + 4 * g + i) * D + w * DW +
                                                         dtw * 16 + c16,
-                                                    dq[dtw][mt][i]);
-                    }
+                                                    dq[part][dtw][mt][i]);
                 }
                 ++t;
                 more = false;
@@ -1003,6 +1023,8 @@ static int launch_main_t(const KParams& kp, const BwdLaunch& L) {
         k.chunk_items = pl.chunk_items;
         k.groups = pl.groups;
         k.acc_slots = pl.slots;
+        k.chunk_shift = __builtin_ctz((unsigned)pl.chunks);
+        k.group_shift = __builtin_ctz((unsigned)pl.groups);
     }
     hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(nthreads), smem, (hipStream_t)L.stream, k);
     if (hipGetLastError() != hipSuccess) return fail(ATTN_ERR_HIP, "main kernel launch failed");
