@@ -350,20 +350,39 @@ void bwd_main_kernel(KParams p) {
         // output row past s is stored.)
         float s_init[NT];
 
+        // dK and dV of the run's KV tile to the outputs.  A lane's fragment
+        // holds four rows of one column, so the values go through LDS (this
+        // wave's rows of the K tile's region, free once every wave is done
+        // with the run's last task) and leave as 16-byte row chunks: 1 KiB per
+        // store instruction instead of four 32-byte row pieces.
         auto store_dkdv = [&](int kvt) {
+            using P = Pad<T, D>;
+            constexpr int CH = 16 / (int)sizeof(T);  // elements per 16-byte chunk
+            constexpr int CPR = D / CH;              // chunks per row
+            constexpr int RPI = 64 / CPR;            // rows per wave-wide instruction
+            static_assert(RW % RPI == 0, "a wave's rows as whole instructions");
+            using VC = T __attribute__((ext_vector_type(CH)));
+            __syncthreads();  // every wave is done with sK and sdS
+            unsigned char* stage = smem + L::OFF_K;
+            auto put = [&](const f32x4 (&acc)[NT][DT], float mul, T* out) {
 #pragma unroll
-            for (int nt = 0; nt < NT; ++nt)
+                for (int nt = 0; nt < NT; ++nt)
 #pragma unroll
-                for (int dt = 0; dt < DT; ++dt)
+                    for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
-                    for (int i = 0; i < 4; ++i) {
-                        const int row = kvt * TILE + w * RW + nt * 16 + 4 * g + i;
-                        if (row < s) {
-                            const size_t off = hoff + (size_t)row * D + dt * 16 + c16;
-                            gdV[off] = E::from_f(dV[nt][dt][i]);
-                            gdK[off] = E::from_f(p.scale * dK[nt][dt][i]);
-                        }
-                    }
+                        for (int i = 0; i < 4; ++i)
+                            *reinterpret_cast<T*>(stage + (w * RW + nt * 16 + 4 * g + i) * P::RS +
+                                                  (dt * 16 + c16) * (int)sizeof(T)) = E::from_f(mul * acc[nt][dt][i]);
+#pragma unroll
+                for (int j = 0; j < RW / RPI; ++j) {
+                    const int lr = w * RW + j * RPI + lane / CPR, chunk = lane % CPR;
+                    const VC v = *reinterpret_cast<const VC*>(stage + lr * P::RS + chunk * 16);
+                    const int row = kvt * TILE + lr;
+                    if (row < s) *reinterpret_cast<VC*>(out + hoff + (size_t)row * D + chunk * CH) = v;
+                }
+            };
+            put(dV, 1.f, gdV);
+            put(dK, p.scale, gdK);  // (this wave's rows only: no barrier between the two)
         };
 
         // The item's tasks, as runs of consecutive tasks on one KV tile: the
