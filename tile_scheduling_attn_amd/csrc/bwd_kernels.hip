@@ -94,7 +94,8 @@ struct KParams {
     int H, s, n, items_per_head, s_pad;
     // XCD placement (XcdPlan; chunks == 0: one global queue and one
     // accumulator, every hand-off through memory)
-    int chunks, chunk_items, groups;
+    int chunks, groups;
+    int bounds[kQueues + 1];  // chunk c of a head = items [bounds[c], bounds[c + 1])
     int chunk_shift, group_shift;  // log2 of chunks and of groups (both powers of two)
     long long acc_slots;  // heads of one XCD's accumulator copy
     long long total_items;
@@ -173,8 +174,8 @@ void bwd_main_kernel(KParams p) {
     xcc &= 0xfu;
     const int queue = (int)(xcc % kQueues);  // XCD placement: this XCD's queue
     // the items of a head that this queue serves: [chunk_lo(), chunk_hi())
-    auto chunk_lo = [&]() { return (queue & (p.chunks - 1)) * p.chunk_items; };
-    auto chunk_hi = [&]() { return min(chunk_lo() + p.chunk_items, p.items_per_head); };
+    auto chunk_lo = [&]() { return p.bounds[queue & (p.chunks - 1)]; };
+    auto chunk_hi = [&]() { return p.bounds[(queue & (p.chunks - 1)) + 1]; };
     if (DET && p.chunks && xcc >= (unsigned)kQueues && tid == 0) atomicOr(p.status, 2u);
 
     unsigned long long wait_cycles = 0, polls = 0, item_cycles = 0;
@@ -914,8 +915,7 @@ void bwd_main_kernel(KParams p) {
     // its items undone)
     if (DET && p.chunks && tid == 0 && atomicAdd(p.queues + kQueues, 1u) == gridDim.x - 1) {
         for (int q = 0; q < kQueues; ++q) {
-            const int grp = q / p.chunks, lo = (q % p.chunks) * p.chunk_items;
-            const int size = min(p.chunk_items, p.items_per_head - lo);
+            const int grp = q / p.chunks, size = p.bounds[q % p.chunks + 1] - p.bounds[q % p.chunks];
             const long long heads = grp < p.H ? (p.H - grp + p.groups - 1) / p.groups : 0;
             const unsigned handed = __hip_atomic_load(p.queues + q, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
             if (size > 0 && (long long)handed < heads * size) atomicOr(p.status, 2u);
@@ -1037,9 +1037,9 @@ static int launch_main_t(const KParams& kp, const BwdLaunch& L) {
     // larger grid (checked anyway; the accumulator always has room for the
     // global queue's one copy)
     const XcdPlan& pl = L.plan;
-    if (DET && pl.chunks && grid / kQueues >= 1 && (L.min_workers <= 1 || pl.chunk_items <= grid / kQueues)) {
+    if (DET && pl.chunks && grid / kQueues >= 1 && (L.min_workers <= 1 || pl.max_chunk <= grid / kQueues)) {
         k.chunks = pl.chunks;
-        k.chunk_items = pl.chunk_items;
+        for (int c = 0; c <= kQueues; ++c) k.bounds[c] = pl.bounds[c];
         k.groups = pl.groups;
         k.acc_slots = pl.slots;
         k.chunk_shift = __builtin_ctz((unsigned)pl.chunks);

@@ -50,11 +50,13 @@ struct BwdArgs {
 constexpr int kQueues = 8;
 
 // XCD placement of a deterministic launch: a head's items split into
-// `chunks` runs of `chunk_items`; queue q serves chunk q % chunks of the heads
-// g, g + groups, ... (g = q / chunks, groups = kQueues / chunks).  Each XCD
-// keeps its own dQ accumulator of `slots` heads (head h in slot h / groups).
+// `chunks` contiguous runs, chunk c = items [bounds[c], bounds[c + 1]); queue
+// q serves chunk q % chunks of the heads g, g + groups, ... (g = q / chunks,
+// groups = kQueues / chunks).  Each XCD keeps its own dQ accumulator of
+// `slots` heads (head h in slot h / groups).
 struct XcdPlan {
-    int chunks = 0, chunk_items = 0, groups = 0;
+    int chunks = 0, groups = 0, max_chunk = 0;
+    int bounds[kQueues + 1] = {};
     long long slots = 0;
 };
 // The plan for `grid` resident work groups, or chunks == 0 when the launch

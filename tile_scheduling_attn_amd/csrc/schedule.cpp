@@ -117,34 +117,52 @@ int build_schedule(int n, bool causal, int schedule, Schedule& out) {
     return ATTN_OK;
 }
 
-// The fewest chunks (1, 2, 4 or 8 per head) whose size fits the work groups
-// of one queue.  A schedule whose items must all be resident at once
-// (min_workers > 1) needs that fit; the others only ever wait on items of
-// the head taken earlier from the same or a lower queue of the group, so any
-// chunk size keeps them deadlock-free.  The XCDs of a group work on the same
-// heads in step, so the chunks must also carry about equal work (within
-// kChunkImbalance of the mean); a causal head's consecutive items do not.
+// The chunks of a head are contiguous runs of its items cut at about equal
+// work (the XCDs of a group work on the same heads in step); a plan is used
+// only if every chunk carries at most kChunkImbalance times the mean.
+// Schedules whose items must all be resident at once (min_workers > 1: the
+// Shift family) take the fewest chunks (1, 2, 4 or 8) that each fit the
+// ⌊grid/8⌋ work groups of a queue.  The others only ever wait on items of the
+// head taken earlier from the same or a lower queue of the group, so any
+// chunk size keeps them deadlock-free: they take the fewest chunks that
+// still give every queue a head (a whole head per XCD when there are eight
+// heads or more, so that no reduction chain leaves its XCD).
 constexpr double kChunkImbalance = 1.1;
 
 XcdPlan xcd_plan(const std::vector<int>& item_begin, int min_workers, long long grid, long long heads) {
-    XcdPlan p;
+    XcdPlan none;
     const int items_per_head = (int)item_begin.size() - 1;
     const long long per_queue = grid / kQueues;
-    if (per_queue < 1 || items_per_head < 1 || heads < 1) return p;
-    int g = 1;
-    while (g < kQueues && (items_per_head + g - 1) / g > per_queue) g *= 2;
-    const int c = (items_per_head + g - 1) / g;
-    if (min_workers > 1 && c > per_queue) return p;
-    const double mean = (double)(item_begin[items_per_head] - item_begin[0]) / g;
-    for (int k = 0; k < g; ++k) {
-        const int lo = std::min(k * c, items_per_head), hi = std::min((k + 1) * c, items_per_head);
-        if (item_begin[hi] - item_begin[lo] > kChunkImbalance * mean) return p;
+    if (per_queue < 1 || items_per_head < 1 || heads < 1) return none;
+    const long long total = item_begin[items_per_head] - item_begin[0];
+    for (int g = 1; g <= kQueues; g *= 2) {
+        if (min_workers <= 1 && g < kQueues && kQueues / g > heads) continue;
+        XcdPlan p;
+        p.bounds[0] = 0;
+        for (int k = 1; k < g; ++k) {  // the cut whose work before it is closest to k/g of the head's
+            const double target = (double)total * k / g;
+            int b = p.bounds[k - 1];
+            while (b < items_per_head && std::fabs((double)(item_begin[b + 1] - item_begin[0]) - target) <=
+                                             std::fabs((double)(item_begin[b] - item_begin[0]) - target))
+                ++b;
+            p.bounds[k] = b;
+        }
+        p.bounds[g] = items_per_head;
+        int max_chunk = 0;
+        long long max_work = 0;
+        for (int k = 0; k < g; ++k) {
+            max_chunk = std::max(max_chunk, p.bounds[k + 1] - p.bounds[k]);
+            max_work = std::max<long long>(max_work, item_begin[p.bounds[k + 1]] - item_begin[p.bounds[k]]);
+        }
+        if (min_workers > 1 && max_chunk > per_queue) continue;
+        if (max_work > kChunkImbalance * (double)total / g) continue;
+        p.chunks = g;
+        p.groups = kQueues / g;
+        p.max_chunk = max_chunk;
+        p.slots = (heads + p.groups - 1) / p.groups;
+        return p;
     }
-    p.chunks = g;
-    p.chunk_items = c;
-    p.groups = kQueues / g;
-    p.slots = (heads + p.groups - 1) / p.groups;
-    return p;
+    return none;
 }
 
 int min_workers(const Schedule& sc) {
