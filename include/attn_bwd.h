@@ -223,7 +223,10 @@ int attn_sched_min_workers(int n, int causal, int schedule);
  * page, "What carries the argument" and Axiom ledger).  `heads` copies of
  * the schedule run on `workers` workers; placement 0 deals items
  * round-robin in head-major order, placement 1 hands the next item to the
- * first worker that becomes free (the kernel's ticket queue).
+ * first worker that becomes free (the kernel's global ticket queue),
+ * placement 2 models the kernel's XCD placement (worker w serves the queue
+ * of XCD w % 8 with the chunks the kernel would use for this shape, and the
+ * global queue when the kernel would fall back to it).
  * Outputs (any may be NULL): makespan, the summed time workers spent
  * blocked on waits, and the summed busy time (compute + reduction).
  * Returns ATTN_OK, ATTN_ERR_DEADLOCK or an argument error.
@@ -233,9 +236,11 @@ int attn_dagsim(int n, int causal, int schedule, int heads, int workers, int pla
 
 /* Same, with an edge cost: a reduction that follows another contributor's
  * reduction of the same dQ tile starts no earlier than e after it ended (the
- * time a release takes to reach the next contributor).  The pages' model
- * has e = 0 (review page, "Load-bearing premise": zero-cost synchronisation
- * edges); attn_dagsim is this with e = 0. */
+ * time a release takes to reach the next contributor; under placement 2
+ * only between workers of different XCDs, a hand-off within an XCD costing
+ * nothing more).  The pages' model has e = 0 (review page, "Load-bearing
+ * premise": zero-cost synchronisation edges); attn_dagsim is this with
+ * e = 0. */
 int attn_dagsim_edge(int n, int causal, int schedule, int heads, int workers, int placement,
                      double c, double r, double e, double* makespan, double* wait_time,
                      double* busy_time);
@@ -245,16 +250,16 @@ int attn_dagsim_edge(int n, int causal, int schedule, int heads, int workers, in
  * schedules complementary and has an implementation pick one per
  * configuration; this picks, among NAIVE, DESCENDING, SHIFT and
  * SYMMETRIC_SHIFT, the one with the smallest simulated makespan
- * (attn_dagsim_edge, placement 1) for `heads` heads of n tiles on `workers`
- * resident work groups with task costs c, r and edge cost e.  Schedules that
+ * (attn_dagsim_edge with the given placement) for `heads` heads of n tiles
+ * on `workers` resident work groups with task costs c, r and edge cost e.  Schedules that
  * the shape does not admit (SYMMETRIC_SHIFT with odd n under the causal
  * mask) or that need more resident work groups than `workers` are skipped;
  * ties go to the lower schedule id.  Outputs (may be NULL): the schedule and
  * its makespan.  Returns ATTN_OK, ATTN_ERR_INVALID_ARG, or
  * ATTN_ERR_UNSUPPORTED when no schedule qualifies.
  * ------------------------------------------------------------------------ */
-int attn_sched_select(int n, int causal, int heads, int workers, double c, double r, double e,
-                      int* schedule, double* makespan);
+int attn_sched_select(int n, int causal, int heads, int workers, int placement, double c, double r,
+                      double e, int* schedule, double* makespan);
 
 /* ------------------------------------------------------------------------
  * Cost calibration of the DAG model (host).  The review page ("What would
@@ -264,16 +269,16 @@ int attn_sched_select(int n, int causal, int heads, int workers, double c, doubl
  * heads[k] heads of n[k] tiles with mask causal[k] and schedule schedule[k]
  * on workers[k] resident work groups that took measured[k] (> 0, any time
  * unit).  Returns c, r and e (per task or edge, same unit) minimising the
- * RMS relative error between the simulated makespans (attn_dagsim_edge,
- * placement 1) and the measurements, and that error.  r/c and e/c are
+ * RMS relative error between the simulated makespans (attn_dagsim_edge with
+ * the given placement) and the measurements, and that error.  r/c and e/c are
  * searched in [1e-4, 1e2] (e may also be 0): grids, then a pattern search.
  * Arrays are host memory of `count` elements, read only.  Returns ATTN_OK,
  * ATTN_ERR_INVALID_ARG, or ATTN_ERR_UNSUPPORTED when a sample cannot be
  * simulated (unsupported schedule, deadlock).
  * ------------------------------------------------------------------------ */
 int attn_sched_fit(int count, const int* n, const int* causal, const int* schedule, const int* heads,
-                   const int* workers, const double* measured, double* c, double* r, double* e,
-                   double* rms);
+                   const int* workers, int placement, const double* measured, double* c, double* r,
+                   double* e, double* rms);
 
 #ifdef __cplusplus
 }

@@ -57,7 +57,7 @@ def test_simulator_matches_oracle_critical_path(name, causal, n, heads, workers,
     assert busy == pytest.approx(ntasks * (c + r))
 
 
-@pytest.mark.parametrize("placement", [0, 1])
+@pytest.mark.parametrize("placement", [0, 1, 2])
 @pytest.mark.parametrize("m,n", [(1, 4), (2, 8), (3, 16), (4, 64)])
 def test_simulator_closed_form_full(placement, m, n):
     for c, r in ((1, 1), (3, 1), (0.5, 2)):
@@ -65,7 +65,7 @@ def test_simulator_closed_form_full(placement, m, n):
         assert got == m * n * (c + r)
 
 
-@pytest.mark.parametrize("placement", [0, 1])
+@pytest.mark.parametrize("placement", [0, 1, 2])
 @pytest.mark.parametrize("m,n", [(2, 2), (2, 8), (4, 16), (6, 64)])
 def test_simulator_closed_form_causal(placement, m, n):
     for c, r in ((1, 1), (3, 1), (0.5, 2)):
@@ -199,6 +199,42 @@ def test_edge_cost_delays_the_serial_chain_but_not_shift():
     assert tsa.attn_dagsim_edge(8, False, "naive", 1, 8, 1, c, r, 0.25)[0] > base
     assert tsa.attn_dagsim_edge(8, False, "shift", 1, 8, 1, c, r, 0.25)[0] == \
         float(dag.closed_form_full(1, 8, Fraction(c), Fraction(r)))
+
+
+def test_xcd_placement_keeps_whole_heads_on_one_xcd():
+    """Placement 2 models the kernel's per-XCD queues.  With at least eight
+    heads a naive or Descending head runs on one XCD, so no hand-off crosses
+    XCDs and the edge cost changes nothing; under one global queue it delays
+    the serial chains."""
+    c, r, e = 1.0, 0.5, 0.75
+    for name, causal in (("naive", False), ("descending", True)):
+        base = tsa.attn_dagsim_edge(16, causal, name, 16, 64, 2, c, r, 0.0)[0]
+        assert tsa.attn_dagsim_edge(16, causal, name, 16, 64, 2, c, r, e)[0] == base
+        assert tsa.attn_dagsim_edge(16, causal, name, 16, 64, 1, c, r, e)[0] > \
+            tsa.attn_dagsim_edge(16, causal, name, 16, 64, 1, c, r, 0.0)[0]
+
+
+def test_xcd_placement_charges_edges_only_between_xcds():
+    """Shift at n = 64 on 256 workers: a head's 64 items run as two chunks of
+    32 on two XCDs, so 2 of a tile's 63 hand-offs cross XCDs.  With an edge
+    longer than a task those crossings delay the launch, but by less than
+    when every hand-off pays it, and never below the edge-free makespan."""
+    c, r, e = 1.0, 1.0, 2.5
+    free = tsa.attn_dagsim_edge(64, False, "shift", 32, 256, 2, c, r, 0.0)[0]
+    xcd = tsa.attn_dagsim_edge(64, False, "shift", 32, 256, 2, c, r, e)[0]
+    every = tsa.attn_dagsim_edge(64, False, "shift", 32, 256, 1, c, r, e)[0]
+    # 32 heads on four groups of 64 workers: 8 heads per group
+    assert free == float(dag.closed_form_full(8, 64, Fraction(c), Fraction(r)))
+    assert free < xcd < every
+
+
+def test_placement_argument_is_checked():
+    with pytest.raises(tsa.AttnError):
+        tsa.attn_dagsim(8, False, "shift", 1, 8, 3, 1.0, 1.0)
+    with pytest.raises(tsa.AttnError):
+        tsa.attn_sched_select(8, False, 1, 8, 1.0, 1.0, 0.0, placement=-1)
+    with pytest.raises(tsa.AttnError):
+        tsa.attn_sched_fit([(8, False, "shift", 1, 8, 1.0)], placement=5)
 
 
 def test_fit_argument_errors():

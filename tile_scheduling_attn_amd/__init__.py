@@ -84,9 +84,9 @@ def _load():
     lib.attn_dagsim.restype = i
     lib.attn_dagsim_edge.argtypes = [i, i, i, i, i, i, d, d, d, dp, dp, dp]
     lib.attn_dagsim_edge.restype = i
-    lib.attn_sched_select.argtypes = [i, i, i, i, d, d, d, ip, dp]
+    lib.attn_sched_select.argtypes = [i, i, i, i, i, d, d, d, ip, dp]
     lib.attn_sched_select.restype = i
-    lib.attn_sched_fit.argtypes = [i, ip, ip, ip, ip, ip, dp, dp, dp, dp, dp]
+    lib.attn_sched_fit.argtypes = [i, ip, ip, ip, ip, ip, i, dp, dp, dp, dp, dp]
     lib.attn_sched_fit.restype = i
     return lib
 
@@ -232,18 +232,19 @@ def attn_dagsim_edge(n, causal, schedule, heads, workers, placement, c, r, e):
     return m.value, w.value, b_.value
 
 
-def attn_sched_select(n, causal, heads, workers, c, r, e=0.0):
-    """Returns (schedule name, simulated makespan)."""
+def attn_sched_select(n, causal, heads, workers, c, r, e=0.0, placement=1):
+    """Returns (schedule name, simulated makespan).  placement as in
+    attn_dagsim (1: one ticket queue, 2: the kernel's XCD placement)."""
     sch, ms = ctypes.c_int(), ctypes.c_double()
-    _check(lib.attn_sched_select(n, int(causal), heads, workers, float(c), float(r), float(e),
+    _check(lib.attn_sched_select(n, int(causal), heads, workers, int(placement), float(c), float(r), float(e),
                                  ctypes.byref(sch), ctypes.byref(ms)), "attn_sched_select")
     name = {v: k for k, v in SCHEDULES.items()}[sch.value]
     return name, ms.value
 
 
-def attn_sched_fit(samples):
+def attn_sched_fit(samples, placement=1):
     """samples: iterable of (n, causal, schedule, heads, workers, measured).
-    Returns (c, r, e, rms relative error)."""
+    Returns (c, r, e, rms relative error) of the model with `placement`."""
     samples = list(samples)
     k = len(samples)
     I = ctypes.c_int * k
@@ -252,8 +253,8 @@ def attn_sched_fit(samples):
             I(*[int(s[4]) for s in samples])]
     meas = (ctypes.c_double * k)(*[float(s[5]) for s in samples])
     c, r, e, rms = ctypes.c_double(), ctypes.c_double(), ctypes.c_double(), ctypes.c_double()
-    _check(lib.attn_sched_fit(k, *cols, meas, ctypes.byref(c), ctypes.byref(r), ctypes.byref(e),
-                              ctypes.byref(rms)), "attn_sched_fit")
+    _check(lib.attn_sched_fit(k, *cols, int(placement), meas, ctypes.byref(c), ctypes.byref(r),
+                              ctypes.byref(e), ctypes.byref(rms)), "attn_sched_fit")
     return c.value, r.value, e.value, rms.value
 
 

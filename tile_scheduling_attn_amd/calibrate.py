@@ -3,11 +3,12 @@
     python tile_scheduling_attn_amd/calibrate.py [--steps K] [--measure-only | --samples FILE]
 
 Times the main kernel of the backward for every (workload, mask, schedule)
-below with the library's own launch-stream events, fits the model's compute
-and reduction costs c and r and the edge cost e (a release reaching the next
-contributor) per head dimension with `attn_sched_fit` (the DAG of the review
-page's "What carries the argument", with the kernel's ticket queue as
-placement), fits the pages' model (e = 0) too, and prints one JSON document:
+below with the library's own launch-stream events (under the library's
+default XCD placement), fits the model's compute and reduction costs c and r
+and the edge cost e (a release reaching the next contributor on another XCD)
+per head dimension with `attn_sched_fit` (the DAG of the review page's "What
+carries the argument", with the kernel's XCD placement, simulator placement
+2), fits the pages' model (e = 0) too, and prints one JSON document:
 the fitted costs, measured against simulated makespan for every sample, and
 the schedule
 `attn_sched_select` picks for each shape.  `--measure-only` prints the
@@ -26,6 +27,9 @@ import sys
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, os.path.dirname(HERE))
+
+# the simulator's model of the kernel's default work placement (per-XCD queues)
+PLACEMENT = 2
 
 # (workload name, causal, schedules timed)
 PLAN = [
@@ -68,7 +72,8 @@ def zero_edge_fit(tsa, ss):
     best = None
     for i in range(121):
         rho = 10 ** (-4 + 6 * i / 120)
-        x = [tsa.attn_dagsim(n, causal, sched, heads, w, 1, 1.0, rho)[0] / ms for n, causal, sched, heads, w, ms, _ in ss]
+        x = [tsa.attn_dagsim(n, causal, sched, heads, w, PLACEMENT, 1.0, rho)[0] / ms
+             for n, causal, sched, heads, w, ms, _ in ss]
         c = sum(x) / sum(v * v for v in x)
         err = math.sqrt(sum((c * v - 1) ** 2 for v in x) / len(x))
         if best is None or err < best[3]:
@@ -104,19 +109,19 @@ def fit(samples):
     for d in sorted({s[7] for s in samples}):
         ss = [tuple(s[:7]) for s in samples if s[7] == d]
         print(f"fitting d={d} ({len(ss)} samples)", file=sys.stderr, flush=True)
-        c, r, e, rms = tsa.attn_sched_fit([s[:6] for s in ss])
+        c, r, e, rms = tsa.attn_sched_fit([s[:6] for s in ss], placement=PLACEMENT)
         c0, r0, _, rms0 = zero_edge_fit(tsa, ss)
         rows = []
         for n, causal, sched, heads, w, ms, name in ss:
-            pred = tsa.attn_dagsim_edge(n, causal, sched, heads, w, 1, c, r, e)[0]
-            pred0 = tsa.attn_dagsim(n, causal, sched, heads, w, 1, c0, r0)[0]
+            pred = tsa.attn_dagsim_edge(n, causal, sched, heads, w, PLACEMENT, c, r, e)[0]
+            pred0 = tsa.attn_dagsim(n, causal, sched, heads, w, PLACEMENT, c0, r0)[0]
             rows.append({"workload": name, "causal": causal, "schedule": sched, "measured_ms": round(ms, 4),
                          "model_ms": round(pred, 4), "model_e0_ms": round(pred0, 4)})
         picks = {}
         for n, causal, _, heads, w, _, name in ss:
             key = f"{name} {'causal' if causal else 'full'}"
             if key not in picks:
-                sel, t = tsa.attn_sched_select(n, causal, heads, w, c, r, e)
+                sel, t = tsa.attn_sched_select(n, causal, heads, w, c, r, e, placement=PLACEMENT)
                 picks[key] = {"schedule": sel, "model_ms": round(t, 4)}
         report["fits"][f"d{d}"] = {"c_us": round(c * 1e3, 4), "r_us": round(r * 1e3, 4), "e_us": round(e * 1e3, 4),
                                    "rms_rel_err": round(rms, 4),

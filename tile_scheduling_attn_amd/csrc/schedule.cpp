@@ -117,16 +117,17 @@ int build_schedule(int n, bool causal, int schedule, Schedule& out) {
     return ATTN_OK;
 }
 
-// The chunks of a head are contiguous runs of its items cut at about equal
-// work (the XCDs of a group work on the same heads in step); a plan is used
-// only if every chunk carries at most kChunkImbalance times the mean.
+// The chunks of a head are contiguous runs of its items, and a plan is used
+// only if every chunk carries at most kChunkImbalance times the mean work.
 // Schedules whose items must all be resident at once (min_workers > 1: the
-// Shift family) take the fewest chunks (1, 2, 4 or 8) that each fit the
-// ⌊grid/8⌋ work groups of a queue.  The others only ever wait on items of the
-// head taken earlier from the same or a lower queue of the group, so any
-// chunk size keeps them deadlock-free: they take the fewest chunks that
-// still give every queue a head (a whole head per XCD when there are eight
-// heads or more, so that no reduction chain leaves its XCD).
+// Shift family) take the fewest chunks (1, 2, 4 or 8) of equal item count
+// that each fit the ⌊grid/8⌋ work groups of a queue: the queues of a group
+// then move through their heads at one rate.  The others only ever wait on
+// items of the head taken earlier from the same or a lower queue of the
+// group, so any chunk size keeps them deadlock-free: they take the fewest
+// chunks that still give every queue a head (a whole head per XCD when there
+// are eight heads or more, so that no reduction chain leaves its XCD), cut
+// at about equal work.
 constexpr double kChunkImbalance = 1.1;
 
 XcdPlan xcd_plan(const std::vector<int>& item_begin, int min_workers, long long grid, long long heads) {
@@ -139,7 +140,12 @@ XcdPlan xcd_plan(const std::vector<int>& item_begin, int min_workers, long long 
         if (min_workers <= 1 && g < kQueues && kQueues / g > heads) continue;
         XcdPlan p;
         p.bounds[0] = 0;
-        for (int k = 1; k < g; ++k) {  // the cut whose work before it is closest to k/g of the head's
+        for (int k = 1; k < g; ++k) {
+            if (min_workers > 1) {  // equal item counts
+                p.bounds[k] = std::min(k * ((items_per_head + g - 1) / g), items_per_head);
+                continue;
+            }
+            // the cut whose work before it is closest to k/g of the head's
             const double target = (double)total * k / g;
             int b = p.bounds[k - 1];
             while (b < items_per_head && std::fabs((double)(item_begin[b + 1] - item_begin[0]) - target) <=
@@ -173,10 +179,14 @@ int min_workers(const Schedule& sc) {
 }
 
 // Discrete-event simulation of `heads` copies of the schedule on `workers`
-// workers.  Events are processed in (time, worker) order.
+// workers.  Events are processed in (time, worker) order.  Placement 0:
+// item g on worker g % workers; 1: one ticket queue in item order; 2: the
+// kernel's XCD placement (worker w serves queue w % kQueues with the chunks
+// of xcd_plan, else as 1), where the edge cost e applies only to a hand-off
+// between workers of different queues (XCDs); under 0 and 1 to every one.
 int simulate(const Schedule& sc, int heads, int workers, int placement, double c, double r, double e,
              double* makespan, double* wait_time, double* busy_time) {
-    if (heads < 0 || workers <= 0 || c < 0 || r < 0 || e < 0 || (placement != 0 && placement != 1))
+    if (heads < 0 || workers <= 0 || c < 0 || r < 0 || e < 0 || placement < 0 || placement > 2)
         return ATTN_ERR_INVALID_ARG;
     const int n = sc.n, items_per_head = sc.num_items();
     const long long total_items = (long long)heads * items_per_head;
@@ -202,6 +212,15 @@ int simulate(const Schedule& sc, int heads, int workers, int placement, double c
         for (long long g = 0; g < total_items; ++g) static_lists[g % workers].push_back(g);
     }
     long long next_ticket = 0;
+    // XCD placement: per-queue ticket counters and the queue of each (head,
+    // q)'s last contributor
+    XcdPlan plan;
+    if (placement == 2) plan = xcd_plan(sc.item_begin, min_workers(sc), workers, heads);
+    const bool xcd = placement == 2 && plan.chunks > 0;
+    std::vector<long long> queue_ticket(kQueues, 0);
+    std::vector<int> last_queue((size_t)heads * n, -1);
+    // edge cost of a hand-off from queue qa to worker w
+    auto edge = [&](int qa, int w) { return !xcd || qa != w % kQueues ? e : 0.0; };
     // waiters per (head, q): at most one worker can wait for a given rank;
     // keep a list and scan it (lists stay short).
     std::vector<std::vector<int>> waiters((size_t)heads * n);
@@ -228,6 +247,7 @@ int simulate(const Schedule& sc, int heads, int workers, int placement, double c
         busy += r;
         next_rank[key]++;
         last_finish[key] = fin;
+        last_queue[key] = w % kQueues;
         if (fin > t_end) t_end = fin;
         tasks_done++;
         // wake the worker waiting for the next rank of this tile
@@ -238,9 +258,10 @@ int simulate(const Schedule& sc, int heads, int workers, int placement, double c
             int kv2 = sc.task_kv[s2.task];
             if (sc.rank[(size_t)kv2 * n + q] == next_rank[key]) {
                 lst.erase(lst.begin() + x);
-                waited += fin + e - s2.wait_since;
+                const double ed = edge(w % kQueues, w2);
+                waited += fin + ed - s2.wait_since;
                 s2.waiting_key = -1;
-                self_pq.push({fin + e, w2 + workers});  // +workers: "reduction may start"
+                self_pq.push({fin + ed, w2 + workers});  // +workers: "reduction may start"
                 break;
             }
         }
@@ -266,6 +287,14 @@ int simulate(const Schedule& sc, int heads, int workers, int placement, double c
                 long long g = -1;
                 if (placement == 0) {
                     if (static_pos[w] < static_lists[w].size()) g = static_lists[w][static_pos[w]++];
+                } else if (xcd) {
+                    const int qq = w % kQueues, grp = qq / plan.chunks, chunk = qq % plan.chunks;
+                    const int lo = plan.bounds[chunk], size = plan.bounds[chunk + 1] - lo;
+                    if (size > 0) {
+                        const long long k = queue_ticket[qq]++;
+                        const long long head = grp + (long long)plan.groups * (k / size);
+                        if (head < heads) g = head * items_per_head + lo + k % size;
+                    }
                 } else if (next_ticket < total_items) {
                     g = next_ticket++;
                 }
@@ -289,7 +318,7 @@ int simulate(const Schedule& sc, int heads, int workers, int placement, double c
             // a contributor after the first starts once the previous one's
             // release has reached it (edge cost e)
             double st = t;
-            if (ordered && next_rank[key] > 0) st = std::max(t, last_finish[key] + e);
+            if (ordered && next_rank[key] > 0) st = std::max(t, last_finish[key] + edge(last_queue[key], w));
             if (st > t) waited += st - t;
             start_reduction(w, st, pq);
         } else {
@@ -358,9 +387,10 @@ extern "C" int attn_dagsim_edge(int n, int causal, int schedule, int heads, int 
 // ---------------------------------------------------------------------------
 // Schedule selection and cost calibration on the DAG model
 // ---------------------------------------------------------------------------
-extern "C" int attn_sched_select(int n, int causal, int heads, int workers, double c, double r, double e,
-                                 int* schedule, double* makespan) {
-    if (n <= 0 || heads <= 0 || workers <= 0 || !(c >= 0) || !(r >= 0) || !(e >= 0))
+extern "C" int attn_sched_select(int n, int causal, int heads, int workers, int placement, double c, double r,
+                                 double e, int* schedule, double* makespan) {
+    if (n <= 0 || heads <= 0 || workers <= 0 || placement < 0 || placement > 2 || !(c >= 0) || !(r >= 0) ||
+        !(e >= 0))
         return attn::fail(ATTN_ERR_INVALID_ARG, "attn_sched_select: invalid arguments");
     int best = -1;
     double best_t = 0;
@@ -369,7 +399,7 @@ extern "C" int attn_sched_select(int n, int causal, int heads, int workers, doub
         if (attn::build_schedule(n, causal != 0, s, sc) != ATTN_OK) continue;  // e.g. odd n, fold
         if (attn::min_workers(sc) > workers) continue;                          // cannot be co-scheduled
         double t = 0;
-        if (attn::simulate(sc, heads, workers, 1, c, r, e, &t, nullptr, nullptr) != ATTN_OK) continue;
+        if (attn::simulate(sc, heads, workers, placement, c, r, e, &t, nullptr, nullptr) != ATTN_OK) continue;
         if (best < 0 || t < best_t * (1 - 1e-12)) {
             best = s;
             best_t = t;
@@ -383,7 +413,7 @@ extern "C" int attn_sched_select(int n, int causal, int heads, int workers, doub
 
 namespace {
 struct FitData {
-    int count;
+    int count, placement;
     const int *n, *causal, *schedule, *heads, *workers;
     const double* measured;
 };
@@ -399,7 +429,7 @@ double fit_error(const FitData& f, double rho, double eps, double* c_out) {
         attn::Schedule sc;
         double m = 0;
         if (attn::build_schedule(f.n[k], f.causal[k] != 0, f.schedule[k], sc) != ATTN_OK) return -1;
-        if (attn::simulate(sc, f.heads[k], f.workers[k], 1, 1.0, rho, eps, &m, nullptr, nullptr) != ATTN_OK)
+        if (attn::simulate(sc, f.heads[k], f.workers[k], f.placement, 1.0, rho, eps, &m, nullptr, nullptr) != ATTN_OK)
             return -1;
         x[k] = m / f.measured[k];
         sx += x[k];
@@ -414,14 +444,15 @@ double fit_error(const FitData& f, double rho, double eps, double* c_out) {
 }  // namespace
 
 extern "C" int attn_sched_fit(int count, const int* n, const int* causal, const int* schedule, const int* heads,
-                              const int* workers, const double* measured, double* c, double* r, double* e,
-                              double* rms) {
-    if (count <= 0 || !n || !causal || !schedule || !heads || !workers || !measured)
+                              const int* workers, int placement, const double* measured, double* c, double* r,
+                              double* e, double* rms) {
+    if (count <= 0 || !n || !causal || !schedule || !heads || !workers || !measured || placement < 0 ||
+        placement > 2)
         return attn::fail(ATTN_ERR_INVALID_ARG, "attn_sched_fit: invalid arguments");
     for (int k = 0; k < count; ++k)
         if (!(measured[k] > 0) || n[k] <= 0 || heads[k] <= 0 || workers[k] <= 0)
             return attn::fail(ATTN_ERR_INVALID_ARG, "attn_sched_fit: invalid sample");
-    const FitData f{count, n, causal, schedule, heads, workers, measured};
+    const FitData f{count, placement, n, causal, schedule, heads, workers, measured};
     // search in u = log(r/c) in [log 1e-4, log 1e2] and v = log(e/c) in
     // [log 1e-4, log 1e2], with v at its lower end standing for e = 0
     const double ulo = std::log(1e-4), uhi = std::log(1e2), vlo = std::log(1e-4), vhi = std::log(1e2);
