@@ -230,6 +230,37 @@ def test_xcd_and_global_placement_give_the_same_bits(shape):
         _check_parity(pb, outs["xcd"], [0, b * h - 1], f"placement {shape}")
 
 
+@pytest.mark.parametrize("shape", [PLACEMENT_SHAPES[0], PLACEMENT_SHAPES[2], PLACEMENT_SHAPES[3]],
+                         ids=lambda x: "-".join(map(str, x)))
+def test_atomic_variant_matches_ordered_sum_within_one_rounding(shape):
+    """The atomic variant adds the same fp32 partials as the naive order,
+    only in an unordered sequence, so its dQ may differ from the naive
+    schedule's by the reassociation error of the fp32 sum (tiny) plus one
+    bf16 rounding step of the element: |a - n| <= 2^-7 max(|a|, |n|) +
+    1e-5 max|n|.  A lost or doubled partial (an atomic that did not see
+    another's update) moves an element by a whole partial, far beyond that.
+    Its dK and dV come from the same per-tile accumulation in the same order
+    as the naive schedule's: bitwise equal.  The placement switch only
+    changes the deterministic schedules' queues; both settings are run."""
+    b, h, s, d, causal = shape
+    pb = Problem(b, h, s, d, "bf16", 5151, causal)
+    ref = [t.clone() for t in pb.run("naive")]
+    for place in ("xcd", "global"):
+        _say(f"atomic vs naive {shape} placement {place}")
+        tsa.attn_bwd_set_placement(place)
+        try:
+            out = [t.clone() for t in pb.run("atomic")]
+        finally:
+            tsa.attn_bwd_set_placement("xcd")
+        assert tsa.attn_bwd_query_status() == 0, tsa.last_error()
+        a, n_ = out[0].float(), ref[0].float()
+        bound = 2.0 ** -7 * torch.maximum(a.abs(), n_.abs()) + 1e-5 * float(n_.abs().max())
+        excess = float(((a - n_).abs() - bound).max())
+        assert excess <= 0, f"{shape} {place}: atomic dQ off by more than one rounding ({excess})"
+        for x, y in zip(out[1:], ref[1:]):
+            assert torch.equal(x.view(torch.int16), y.view(torch.int16)), f"{shape} {place}"
+
+
 def test_default_entry_point_bf16():
     pb = Problem(1, 2, 256, 64, "bf16", 91, False)
     dq, dk, dv = (torch.empty_like(pb.q) for _ in range(3))
