@@ -51,7 +51,8 @@ static bool ws_layout(long long H, long long s, int d, long long acc_heads, WsLa
     w.nflags = (int)(H * nmax);
     w.acc = 0;
     w.delta = align_up(w.acc + (size_t)acc_heads * w.s_pad * d * sizeof(float));
-    w.flags = align_up(w.delta + (size_t)H * w.s_pad * sizeof(float));
+    // D, then lse * log2(e), [H][s_pad] each
+    w.flags = align_up(w.delta + 2 * (size_t)H * w.s_pad * sizeof(float));
     w.counters = align_up(w.flags + (size_t)w.nflags * sizeof(unsigned));
     w.total = align_up(w.counters + kCounterWords * sizeof(unsigned));
     return true;

@@ -79,7 +79,7 @@ constexpr unsigned kRankMask = 0xffffffu, kWroteThrough = 1u << 31;
 
 struct KParams {
     const void *q, *k, *v, *dO;
-    const float* lse;
+    const float* lse2;   // lse * log2(e) [H][s_pad] (workspace; zero past s)
     const float* delta;
     void *dq, *dk, *dv;
     float* dq_acc;
@@ -106,7 +106,7 @@ struct KParams {
 //   sQ[2], sdO[2]  padded [BQ][D]   query rows of a sub-step (double buffer)
 //   sK             padded [TILE][D] keys of the current KV tile (dQ operand)
 //   sdS            [TILE][TILE] (+pad) dS of the current task as [query][key]
-//   slse[2], sdelta[2] [BQ]
+//   slse[2] (lse * log2 e), sdelta[2] [BQ]
 //   the current item's task records, MAXT at a time (plus the next one)
 //   a 1 KiB sink for copy slots with nothing to copy
 template <typename T, int D, int TILE>
@@ -163,6 +163,9 @@ void bwd_main_kernel(KParams p) {
 
     const int tid = threadIdx.x, lane = tid & 63, g = lane >> 4, c16 = lane & 15;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave index, in an SGPR
+    // (kThreads per work group: lets the compiler drop the sink selection of
+    // copy slots that never reach past a tile)
+    __builtin_assume(w >= 0 && w < NW);
     const T* gK = static_cast<const T*>(p.k);
     const T* gV = static_cast<const T*>(p.v);
     T* gdQ = static_cast<T*>(p.dq);
@@ -311,7 +314,7 @@ void bwd_main_kernel(KParams p) {
         const u32x4 rq = rsrc_words(static_cast<const T*>(p.q) + hoff, head_bytes);
         const u32x4 rdo = rsrc_words(static_cast<const T*>(p.dO) + hoff, head_bytes);
         const u32x4 rk = rsrc_words(gK + hoff, head_bytes);
-        const u32x4 rlse = rsrc_words(p.lse + (size_t)head * s, (unsigned)(s * 4));
+        const u32x4 rlse = rsrc_words(p.lse2 + (size_t)head * p.s_pad, (unsigned)(p.s_pad * 4));
         const u32x4 rdel = rsrc_words(p.delta + (size_t)head * p.s_pad, (unsigned)(p.s_pad * 4));
         // The copies of one sub-step's rows, as NSLOT issue slots per wave: the
         // wave's blocks of the Q tile, of the dO tile, then one slot for the
@@ -526,7 +529,7 @@ void bwd_main_kernel(KParams p) {
 #pragma unroll
                             for (int i = 0; i < 4; ++i) {
                                 const int ql = (2 * GQ + m) * 16 + 4 * g + i;
-                                const float l2 = slse[ql] * kLog2e, dl = sdelta[ql];
+                                const float l2 = slse[ql], dl = sdelta[ql];
 #pragma unroll
                                 for (int nt = 0; nt < NT; ++nt) {
                                     float pv = __builtin_amdgcn_exp2f(S[GQ][m][nt][i] * p.scale_log2 - l2);
@@ -618,7 +621,7 @@ void bwd_main_kernel(KParams p) {
                         // several steps in flight.
                         constexpr int PF2 = 4, R2 = PF2 + 1;
                         s16x4 t2[R2][2][2];
-                        f32x4 lsev[2][2], delv[2][2];  // [group][m]: lse and D of rows 4g..4g+3
+                        f32x4 lsev[2][2], delv[2][2];  // [group][m]: lse * log2 e and D of rows 4g..4g+3
                         const lds_u8* tq = (const lds_u8*)sQ + (4 * g + (c16 >> 2)) * P::RS + 8 * (c16 & 3);
                         // read k (0..3) of phase-1 step j = (group, 32-wide d step)
                         auto rd1 = [&](auto jc, auto kc) {
@@ -653,16 +656,28 @@ void bwd_main_kernel(KParams p) {
                             constexpr int m = k / 4, nt = (k / 2) % 2, ip = k % 2;
 #pragma unroll
                             for (int i = 2 * ip; i < 2 * ip + 2; ++i) {
-                                const float pv = __builtin_amdgcn_exp2f(S[G][m][nt][i] * p.scale_log2 - lsev[G][m][i] * kLog2e);
+                                const float pv = __builtin_amdgcn_exp2f(S[G][m][nt][i] * p.scale_log2 - lsev[G][m][i]);
                                 aP[G][nt][4 * m + i] = E::from_f(pv);
                                 aS[G][nt][4 * m + i] = E::from_f(pv * (dP[G][m][nt][i] - delv[G][m][i]));
                             }
                         };
-                        // dS store k (0..31): group, m, key tile, row
+                        // dS store k (0..31): group, m, key tile, row.  The value is
+                        // taken from its half of the packed bf16 pair that the
+                        // softmax made for phase 2 (no second conversion): the
+                        // store of the low half reads the pair once, through an
+                        // empty asm that hides it from the optimiser (which would
+                        // otherwise convert the fp32 value again for each 16-bit
+                        // store), and the store of the high half reuses it
+                        unsigned ds_pair = 0;
                         auto st_ds = [&](auto kc) {
                             constexpr int k = decltype(kc)::value, G = k / 16, m = (k / 8) % 2, nt = (k / 4) % 2, i = k % 4;
+                            constexpr int e = 4 * m + i;
+                            if constexpr (e % 2 == 0) {
+                                ds_pair = __builtin_bit_cast(u32x4, aS[G][nt])[e / 2];
+                                asm volatile("" : "+v"(ds_pair));
+                            }
                             sdS[(sub * BQ + (2 * G + m) * 16 + 4 * g + i) * LDSS + w * RW + nt * 16 + c16] =
-                                aS[G][nt][4 * m + i];
+                                __builtin_bit_cast(T, (unsigned short)(e % 2 ? ds_pair >> 16 : ds_pair));
                         };
                         auto mfma = [&](auto ic) {
                             constexpr int i = decltype(ic)::value;
@@ -928,12 +943,14 @@ void bwd_main_kernel(KParams p) {
     }
 }
 
-// D[head][row] = <dO_row, O_row> in fp32 (zero for padded rows); clears the
-// flags and counters of the call and, for the atomic variant, the dQ
-// accumulator.  16 lanes per row.
+// D[head][row] = <dO_row, O_row> in fp32 and lse2[head][row] = lse * log2(e)
+// (both zero for padded rows, the softmax's exp2 argument then needs no
+// multiply per use); clears the flags and counters of the call and, for the
+// atomic variant, the dQ accumulator.  16 lanes per row.
 template <typename T, int D>
 __global__ __launch_bounds__(256) void bwd_preprocess_kernel(const T* __restrict__ o, const T* __restrict__ dO,
-                                                              float* __restrict__ delta, int H, int s, int s_pad,
+                                                              const float* __restrict__ lse, float* __restrict__ delta,
+                                                              float* __restrict__ lse2, int H, int s, int s_pad,
                                                               unsigned* __restrict__ clear32, int nclear32,
                                                               float* __restrict__ zero_acc, size_t nzero4) {
     constexpr int PER = D / 16;
@@ -951,7 +968,10 @@ __global__ __launch_bounds__(256) void bwd_preprocess_kernel(const T* __restrict
         }
 #pragma unroll
         for (int m = 8; m >= 1; m >>= 1) acc += __shfl_xor(acc, m, 16);
-        if (part == 0) delta[row] = acc;
+        if (part == 0) {
+            delta[row] = acc;
+            lse2[row] = r < s ? lse[(size_t)hh * s + r] * kLog2e : 0.f;
+        }
     }
     const size_t nthreads = (size_t)gridDim.x * blockDim.x;
     for (size_t i = gtid; i < (size_t)nclear32; i += nthreads) clear32[i] = 0u;
@@ -1071,11 +1091,12 @@ static int launch_all(const BwdArgs& a, const BwdLaunch& L, KParams& kp) {
         const size_t threads = rows * 16;
         const unsigned blocks = (unsigned)((threads + 255) / 256);
         const size_t nzero4 = det ? 0 : (size_t)a.H * a.s_pad * a.d / 4;
+        float* lse2 = a.delta + (size_t)a.H * a.s_pad;
         if (a.d == 64)
-            hipLaunchKernelGGL((bwd_preprocess_kernel<T, 64>), dim3(blocks), dim3(256), 0, st, o, dO, a.delta, a.H,
+            hipLaunchKernelGGL((bwd_preprocess_kernel<T, 64>), dim3(blocks), dim3(256), 0, st, o, dO, a.lse, a.delta, lse2, a.H,
                                a.s, (int)a.s_pad, a.flags, L.nclear32, det ? nullptr : a.dq_acc, nzero4);
         else
-            hipLaunchKernelGGL((bwd_preprocess_kernel<T, 128>), dim3(blocks), dim3(256), 0, st, o, dO, a.delta, a.H,
+            hipLaunchKernelGGL((bwd_preprocess_kernel<T, 128>), dim3(blocks), dim3(256), 0, st, o, dO, a.lse, a.delta, lse2, a.H,
                                a.s, (int)a.s_pad, a.flags, L.nclear32, det ? nullptr : a.dq_acc, nzero4);
         if (hipGetLastError() != hipSuccess) return fail(ATTN_ERR_HIP, "preprocess kernel launch failed");
     }
@@ -1102,7 +1123,7 @@ static int launch_all(const BwdArgs& a, const BwdLaunch& L, KParams& kp) {
 int launch_backward(const BwdArgs& a, const BwdLaunch& L) {
     KParams kp{};
     kp.q = a.q; kp.k = a.k; kp.v = a.v; kp.dO = a.dO;
-    kp.lse = a.lse;
+    kp.lse2 = a.delta + (size_t)a.H * a.s_pad;
     kp.delta = a.delta;
     kp.dq = a.dq; kp.dk = a.dk; kp.dv = a.dv;
     kp.dq_acc = a.dq_acc;

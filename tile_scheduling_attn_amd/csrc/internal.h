@@ -39,7 +39,7 @@ struct BwdArgs {
     void* stream;
     // workspace carve-out
     float* dq_acc;
-    float* delta;
+    float* delta;         // D [H][s_pad], then lse * log2(e) [H][s_pad]
     unsigned* flags;
     unsigned* counters;   // [0] ticket, [1] abort, [2..] wait statistics, [kQueueWord..] XCD queues
     long long acc_slots;  // heads of dq_acc: H, or kQueues copies of XcdPlan::slots
