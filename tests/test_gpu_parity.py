@@ -29,7 +29,12 @@ def _say(msg):
 
 
 def _check_parity(pb, grads, heads, tag):
-    ref = pb.oracle(heads)
+    # the oracle of one problem is the same for every schedule: computed once
+    cache = pb.__dict__.setdefault("_oracle_cache", {})
+    key = tuple(heads)
+    if key not in cache:
+        cache[key] = pb.oracle(heads)
+    ref = cache[key]
     tol = TOL[pb.dtype]
     errs = {}
     for name, g in zip(("dq", "dk", "dv"), grads):
@@ -130,7 +135,7 @@ def test_config_s8k_d128_causal():
 @pytest.mark.parametrize("causal", [False, True])
 def test_config_s16k_d128(causal):
     scheds = ("shift", "naive", "atomic") if not causal else ("descending", "symmetric_shift", "shift")
-    _run_config("s16k_d128", causal, scheds, heads=[0, 31])
+    _run_config("s16k_d128", causal, scheds, heads="sample")
 
 
 # ---------------------------------------------------------------- determinism

@@ -20,6 +20,8 @@ constexpr float kLog2e = 1.4426950408889634f;
 
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
+typedef __attribute__((address_space(3))) u32x2 lds_u32x2;
 
 template <typename T> struct Elem;
 

@@ -105,7 +105,9 @@ struct KParams {
 // LDS of one work group:
 //   sQ[2], sdO[2]  padded [BQ][D]   query rows of a sub-step (double buffer)
 //   sK             padded [TILE][D] keys of the current KV tile (dQ operand)
-//   sdS            [TILE][TILE] (+pad) dS of the current task as [query][key]
+//   sdS            [TILE][TILE] (+pad) dS of the current task as [query][key], or
+//                  (DST, bf16 only) as [key][query]: a lane's four query rows of
+//                  one key are then 8 contiguous bytes, one 64-bit store
 //   slse[2] (lse * log2 e), sdelta[2] [BQ]
 //   the current item's task records, MAXT at a time (plus the next one)
 //   a 1 KiB sink for copy slots with nothing to copy
@@ -137,9 +139,16 @@ struct Layout {
 // registers left over hold several operand fetches in flight.
 constexpr int kWaves = 4, kThreads = 64 * kWaves;
 
-template <typename T, int D, int TILE, bool CAUSAL, bool DET>
+// DST: dS in LDS as [key][query] (bf16 only).  Its stores take a quarter of
+// the instructions of the sub-step's [query][key] ones, and the dQ contraction
+// reads it through transposing reads (twice the instructions there); the two
+// layouts give the same operands, so the same bits.  Measured, the balance
+// favours it under Symmetric Shift at d = 128 (whose one-step reduction
+// chains carry every sub-step's length) and not under the other schedules.
+template <typename T, int D, int TILE, bool CAUSAL, bool DET, bool DST>
 __global__ __launch_bounds__(kThreads, 1) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void bwd_main_kernel(KParams p) {
+    static_assert(!DST || sizeof(T) == 2, "the [key][query] dS layout is a bf16 layout");
     using E = Elem<T>;
     using V8 = typename E::vec8;
     using V4 = typename E::vec4;
@@ -205,9 +214,20 @@ void bwd_main_kernel(KParams p) {
         constexpr int NP = KSKV * NSUB;
         auto load_b = [&](auto pc, V8 (&b)[MT]) {
             constexpr int pi = decltype(pc)::value, ks = pi / NSUB, part = pi % NSUB;
+            if constexpr (DST) {
+                // keys 32ks + 8g .. +7 of query row part*BQ + 16mt + c16, down a
+                // column of the [key][query] tile: two transposing reads
+                constexpr int SRS = LDSS * 2;  // bytes per key row
+                const lds_u8* ts = lsm + L::OFF_S + (8 * g + (c16 >> 2)) * SRS + 8 * (c16 & 3);
+                static_for<0, MT>([&](auto mc) {
+                    constexpr int o = ks * 32 * SRS + (part * BQ + decltype(mc)::value * 16) * 2;
+                    b[decltype(mc)::value] = tr_frag<o, o + 4 * SRS>(ts);
+                });
+            } else {
 #pragma unroll
-            for (int mt = 0; mt < MT; ++mt)
-                b[mt] = *reinterpret_cast<const V8*>(sdS + (part * BQ + mt * 16 + c16) * LDSS + ks * 32 + 8 * g);
+                for (int mt = 0; mt < MT; ++mt)
+                    b[mt] = *reinterpret_cast<const V8*>(sdS + (part * BQ + mt * 16 + c16) * LDSS + ks * 32 + 8 * g);
+            }
         };
         auto mm = [&](int part, const V8 (&a)[NDT], const V8 (&b)[MT]) {
 #pragma unroll
@@ -592,9 +612,10 @@ void bwd_main_kernel(KParams p) {
 #pragma unroll
                             for (int nt = 0; nt < NT; ++nt)
 #pragma unroll
-                                for (int i = 0; i < 4; ++i)
-                                    sdS[(sub * BQ + (2 * GQ + m) * 16 + 4 * g + i) * LDSS + w * RW + nt * 16 + c16] =
-                                        aS[GQ][nt][4 * m + i];
+                                for (int i = 0; i < 4; ++i) {
+                                    const int q = sub * BQ + (2 * GQ + m) * 16 + 4 * g + i, key = w * RW + nt * 16 + c16;
+                                    sdS[DST ? key * LDSS + q : q * LDSS + key] = aS[GQ][nt][4 * m + i];
+                                }
                     };
                     if constexpr (sizeof(T) == 2 && NT == 2 && KSQ == 2) {
                         // The bf16 sub-step as an explicit instruction schedule.  The
@@ -661,23 +682,36 @@ void bwd_main_kernel(KParams p) {
                                 aS[G][nt][4 * m + i] = E::from_f(pv * (dP[G][m][nt][i] - delv[G][m][i]));
                             }
                         };
-                        // dS store k (0..31): group, m, key tile, row.  The value is
-                        // taken from its half of the packed bf16 pair that the
-                        // softmax made for phase 2 (no second conversion): the
-                        // store of the low half reads the pair once, through an
-                        // empty asm that hides it from the optimiser (which would
-                        // otherwise convert the fp32 value again for each 16-bit
-                        // store), and the store of the high half reuses it
+                        // dS stores.  DST ([key][query]): store k (0..7) = group, m, key
+                        // tile; the lane's four query rows 4g..4g+3 of its key are two
+                        // packed bf16 pairs of the phase-2 operand and 8 contiguous
+                        // bytes: one 64-bit store.  Otherwise ([query][key]): store k
+                        // (0..31) = group, m, key tile, row, each value taken from its
+                        // half of the packed pair (no second conversion): the store of
+                        // the low half reads the pair once, through an empty asm that
+                        // hides it from the optimiser (which would otherwise convert
+                        // the fp32 value again for each 16-bit store), and the store
+                        // of the high half reuses it.
+                        constexpr int NDS = DST ? 8 : 32;
                         unsigned ds_pair = 0;
                         auto st_ds = [&](auto kc) {
-                            constexpr int k = decltype(kc)::value, G = k / 16, m = (k / 8) % 2, nt = (k / 4) % 2, i = k % 4;
-                            constexpr int e = 4 * m + i;
-                            if constexpr (e % 2 == 0) {
-                                ds_pair = __builtin_bit_cast(u32x4, aS[G][nt])[e / 2];
-                                asm volatile("" : "+v"(ds_pair));
+                            constexpr int k = decltype(kc)::value;
+                            if constexpr (DST) {
+                                constexpr int G = k / 4, m = (k / 2) % 2, nt = k % 2;
+                                const u32x4 words = __builtin_bit_cast(u32x4, aS[G][nt]);
+                                const u32x2 pr = {words[2 * m], words[2 * m + 1]};
+                                *reinterpret_cast<lds_u32x2*>(
+                                    lsm + L::OFF_S + ((w * RW + nt * 16 + c16) * LDSS + sub * BQ + (2 * G + m) * 16 + 4 * g) * 2) = pr;
+                            } else {
+                                constexpr int G = k / 16, m = (k / 8) % 2, nt = (k / 4) % 2, i = k % 4;
+                                constexpr int e = 4 * m + i;
+                                if constexpr (e % 2 == 0) {
+                                    ds_pair = __builtin_bit_cast(u32x4, aS[G][nt])[e / 2];
+                                    asm volatile("" : "+v"(ds_pair));
+                                }
+                                sdS[(sub * BQ + (2 * G + m) * 16 + 4 * g + i) * LDSS + w * RW + nt * 16 + c16] =
+                                    __builtin_bit_cast(T, (unsigned short)(e % 2 ? ds_pair >> 16 : ds_pair));
                             }
-                            sdS[(sub * BQ + (2 * G + m) * 16 + 4 * g + i) * LDSS + w * RW + nt * 16 + c16] =
-                                __builtin_bit_cast(T, (unsigned short)(e % 2 ? ds_pair >> 16 : ds_pair));
                         };
                         auto mfma = [&](auto ic) {
                             constexpr int i = decltype(ic)::value;
@@ -755,12 +789,16 @@ void bwd_main_kernel(KParams p) {
                                 sm_pair(I0{}, std::integral_constant<int, (i - A) / (A / 8)>{});
                             if constexpr (i >= 2 * A && i < 2 * A + B && (i - 2 * A) % (B / 8) == 0)
                                 sm_pair(I1{}, std::integral_constant<int, (i - 2 * A) / (B / 8)>{});
-                            // dS stores beside phase 2 of group 1
+                            // dS stores spread over phase 2 of group 1
                             if constexpr (i >= 2 * A + B) {
-                                constexpr int per = 32 / B;
-                                static_for<0, per>([&](auto jc) {
-                                    st_ds(std::integral_constant<int, (i - 2 * A - B) * per + decltype(jc)::value>{});
-                                });
+                                constexpr int r = i - 2 * A - B;
+                                if constexpr (NDS >= B) {
+                                    static_for<0, NDS / B>([&](auto jc) {
+                                        st_ds(std::integral_constant<int, r * (NDS / B) + decltype(jc)::value>{});
+                                    });
+                                } else if constexpr (r % (B / NDS) == 0) {
+                                    st_ds(std::integral_constant<int, r / (B / NDS)>{});
+                                }
                             }
                             __builtin_amdgcn_sched_barrier(0);
                         });
@@ -1031,9 +1069,9 @@ int probe_xcd_dispatch(int num_cus, bool* ok) {
     return ATTN_OK;
 }
 
-template <typename T, int D, int TILE, bool CAUSAL, bool DET>
+template <typename T, int D, int TILE, bool CAUSAL, bool DET, bool DST = false>
 static int launch_main_t(const KParams& kp, const BwdLaunch& L) {
-    auto kern = bwd_main_kernel<T, D, TILE, CAUSAL, DET>;
+    auto kern = bwd_main_kernel<T, D, TILE, CAUSAL, DET, DST>;
     const size_t smem = Layout<T, D, TILE>::bytes;
     static bool attr_set = false;  // per instantiation; attribute is per device-function
     if (!attr_set) {
@@ -1071,7 +1109,10 @@ static int launch_main_t(const KParams& kp, const BwdLaunch& L) {
 }
 
 template <typename T, int D, int TILE>
-static int launch_main_d(const KParams& kp, const BwdLaunch& L, bool causal, bool det) {
+static int launch_main_d(const KParams& kp, const BwdLaunch& L, bool causal, bool det, bool dst) {
+    if constexpr (sizeof(T) == 2 && D == 128) {
+        if (causal && det && dst) return launch_main_t<T, D, TILE, true, true, true>(kp, L);
+    }
     if (causal)
         return det ? launch_main_t<T, D, TILE, true, true>(kp, L) : launch_main_t<T, D, TILE, true, false>(kp, L);
     return det ? launch_main_t<T, D, TILE, false, true>(kp, L) : launch_main_t<T, D, TILE, false, false>(kp, L);
@@ -1101,8 +1142,12 @@ static int launch_all(const BwdArgs& a, const BwdLaunch& L, KParams& kp) {
         if (hipGetLastError() != hipSuccess) return fail(ATTN_ERR_HIP, "preprocess kernel launch failed");
     }
     if (L.ev && hipEventRecord((hipEvent_t)L.ev[1], st) != hipSuccess) return fail(ATTN_ERR_HIP, "hipEventRecord failed");
-    int rc = (a.d == 64) ? launch_main_d<T, 64, TILE>(kp, L, a.causal, det)
-                         : launch_main_d<T, 128, TILE>(kp, L, a.causal, det);
+    // Symmetric Shift (causal; under the full mask it runs Shift) with dS as
+    // [key][query] at d = 128 (measured: 8% faster at s = 8192; at d = 64,
+    // s = 2048 the row layout is 3% faster)
+    const bool dst = a.schedule == ATTN_SCHED_SYMMETRIC_SHIFT;
+    int rc = (a.d == 64) ? launch_main_d<T, 64, TILE>(kp, L, a.causal, det, dst)
+                         : launch_main_d<T, 128, TILE>(kp, L, a.causal, det, dst);
     if (rc != ATTN_OK) return rc;
     if (L.ev && hipEventRecord((hipEvent_t)L.ev[2], st) != hipSuccess) return fail(ATTN_ERR_HIP, "hipEventRecord failed");
     if (!det) {
