@@ -109,7 +109,8 @@ int attn_bwd_deterministic_ex(const void* q, const void* k, const void* v, const
 /* Bytes of workspace a call with these sizes needs on the current device:
  * fp32 dQ accumulator (b*h*s_pad*d*4, or the per-XCD copies of XCD
  * placement, for either element type), per-(head, Q tile) flags,
- * D = rowsum(dO*O), counters.  s_pad is s rounded up to 128.  Without a
+ * D = rowsum(dO*O) and lse*log2(e) (b*h*s_pad*4 each), counters.  s_pad is
+ * s rounded up to 128.  Without a
  * usable device, or under ATTN_PLACE_GLOBAL, the size for the single global
  * queue, which is also the smallest workspace a call accepts.  Returns 0
  * for invalid sizes. */
