@@ -75,6 +75,7 @@ SMALL = [
     (2, 1, 384, 128, "bf16"),
     (1, 3, 200, 64, "bf16"),      # ragged: 200 = 128 + 72
     (1, 2, 300, 128, "bf16"),     # ragged: 3 tiles, last one 44 rows
+    (1, 2, 500, 128, "bf16"),     # ragged, even tile count (causal Symmetric Shift at d=128)
     (1, 2, 130, 64, "fp32"),      # ragged fp32: 64 + 64 + 2
     (2, 2, 256, 128, "fp32"),
     (1, 1, 1, 64, "bf16"),        # a single row
