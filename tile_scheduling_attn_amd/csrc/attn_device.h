@@ -132,6 +132,15 @@ __device__ inline void copy16_to_lds(u32x4 rsrc, unsigned voff, unsigned lds) {
                  : "v"(voff), "s"(rsrc), "s"(__builtin_amdgcn_readfirstlane(lds))
                  : "memory", "m0");
 }
+// As copy16_to_lds, to LDS byte address base + OFF: the add is the m0 write
+// itself (one scalar instruction instead of an add and a move).
+template <unsigned OFF>
+__device__ inline void copy16_to_lds_at(u32x4 rsrc, unsigned voff, unsigned base) {
+    asm volatile("s_add_u32 m0, %2, %3\n\ts_nop 0\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds"
+                 :
+                 : "v"(voff), "s"(rsrc), "s"(__builtin_amdgcn_readfirstlane(base)), "i"(OFF)
+                 : "memory", "m0", "scc");
+}
 __device__ inline void copy4_to_lds(u32x4 rsrc, unsigned voff, unsigned lds) {
     asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tbuffer_load_dword %0, %1, 0 offen lds"
                  :
@@ -183,6 +192,26 @@ __device__ inline void load_tile_block(unsigned tile, unsigned sink, u32x4 rsrc,
     const int row = byte / P::RS, inrow = byte % P::RS;
     const unsigned voff = (byte < TOTAL && inrow < P::RB) ? (unsigned)((row0 + row) * P::RB + inrow) : kOutOfRange;
     copy16_to_lds(rsrc, voff, blk < BLOCKS ? tile + blk * 1024 : sink);
+}
+
+// load_tile_block for a block index IT known at compile time, from
+// tile_w = tile + w * 1024 (this wave's first block): where no wave's block
+// IT reaches past the tile, no sink selection and one scalar instruction for
+// the destination.
+template <typename T, int D, int ROWS, int NW, int IT>
+__device__ inline void load_tile_block_c(unsigned tile, unsigned tile_w, unsigned sink, u32x4 rsrc, int row0, int w,
+                                         int lane) {
+    using P = Pad<T, D>;
+    constexpr int TOTAL = ROWS * P::RS;
+    constexpr int BLOCKS = (TOTAL + 1023) / 1024;
+    if constexpr (NW - 1 + NW * IT < BLOCKS) {
+        const int byte = (w + NW * IT) * 1024 + lane * 16;
+        const int row = byte / P::RS, inrow = byte % P::RS;
+        const unsigned voff = (byte < TOTAL && inrow < P::RB) ? (unsigned)((row0 + row) * P::RB + inrow) : kOutOfRange;
+        copy16_to_lds_at<(unsigned)(NW * IT * 1024)>(rsrc, voff, tile_w);
+    } else {
+        load_tile_block<T, D, ROWS, NW>(tile, sink, rsrc, row0, w, lane, IT);
+    }
 }
 
 // n consecutive fp32 values of a per-row vector (rows [row0, row0 + n),

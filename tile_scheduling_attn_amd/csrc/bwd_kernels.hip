@@ -345,10 +345,20 @@ void bwd_main_kernel(KParams p) {
         const unsigned sink = lds_base + L::OFF_SINK;
         auto issue_slot = [&](auto slotc, int b, int q0) {
             constexpr int slot = decltype(slotc)::value;
+            // (d = 128: the destination add folded into the m0 write, measured
+            // 2.7% faster under the causal mask; at d = 64 1% slower)
             if constexpr (slot < QITS) {
-                load_tile_block<T, D, BQ, NW>(lds_base + L::OFF_Q + b * L::QB, sink, rq, q0, w, lane, slot);
+                const unsigned tile = lds_base + L::OFF_Q + b * L::QB;
+                if constexpr (D == 128)
+                    load_tile_block_c<T, D, BQ, NW, slot>(tile, tile + w * 1024, sink, rq, q0, w, lane);
+                else
+                    load_tile_block<T, D, BQ, NW>(tile, sink, rq, q0, w, lane, slot);
             } else if constexpr (slot < 2 * QITS) {
-                load_tile_block<T, D, BQ, NW>(lds_base + L::OFF_DO + b * L::QB, sink, rdo, q0, w, lane, slot - QITS);
+                const unsigned tile = lds_base + L::OFF_DO + b * L::QB;
+                if constexpr (D == 128)
+                    load_tile_block_c<T, D, BQ, NW, slot - QITS>(tile, tile + w * 1024, sink, rdo, q0, w, lane);
+                else
+                    load_tile_block<T, D, BQ, NW>(tile, sink, rdo, q0, w, lane, slot - QITS);
             } else if constexpr (BQ == 64) {
                 const bool lw = w == 0, dw = w == 1;
                 copy4_to_lds(lw ? rlse : rdel, lw || dw ? (unsigned)((q0 + lane) * 4) : kOutOfRange,
