@@ -195,7 +195,8 @@ void bwd_main_kernel(KParams p) {
     // dQ^T (deterministic) or dQ (atomic) of the task's whole Q tile, as
     // NSUB parts of BQ query rows, for this wave's DW columns, contracted
     // over the whole KV tile: A = K^T from sK (transposed reads), B = dS rows
-    // from sdS.  Deterministic: C[d][q], a lane holds 4 consecutive d of one
+    // from sdS (b128 reads of [query][key], or transposed reads of [key][query]
+    // under DST).  Deterministic: C[d][q], a lane holds 4 consecutive d of one
     // query row (16-byte accumulator accesses).  Atomic: C[q][d], 16 lanes
     // hold 16 consecutive d of one row (64 contiguous bytes per atomic
     // instruction).  The loop runs over (32-key step, part) pairs, part
@@ -614,7 +615,7 @@ void bwd_main_kernel(KParams p) {
                             }
                         }
                     };
-                    // dS to LDS as [query][key] for the dQ contraction
+                    // dS to LDS for the dQ contraction, in the layout DST selects
                     auto store_ds = [&](auto gqc) {
                         constexpr int GQ = decltype(gqc)::value;
 #pragma unroll
