@@ -143,6 +143,7 @@ def test_config_s16k_d128(causal):
 @pytest.mark.parametrize("name,causal,scheds", [
     ("s2k_d64_causal", True, ("descending", "symmetric_shift", "naive", "shift")),
     ("s8k_d128_full", False, ("shift", "naive")),
+    ("s8k_d128_causal", True, ("symmetric_shift", "descending")),
 ])
 def test_bitwise_determinism_20_runs(name, causal, scheds):
     wl = workloads.WORKLOADS[name]
