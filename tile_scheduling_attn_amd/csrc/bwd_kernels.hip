@@ -697,14 +697,9 @@ void bwd_main_kernel(KParams p) {
                         // tile; the lane's four query rows 4g..4g+3 of its key are two
                         // packed bf16 pairs of the phase-2 operand and 8 contiguous
                         // bytes: one 64-bit store.  Otherwise ([query][key]): store k
-                        // (0..31) = group, m, key tile, row, each value taken from its
-                        // half of the packed pair (no second conversion): the store of
-                        // the low half reads the pair once, through an empty asm that
-                        // hides it from the optimiser (which would otherwise convert
-                        // the fp32 value again for each 16-bit store), and the store
-                        // of the high half reuses it.
+                        // (0..31) = group, m, key tile, row, each value its half of the
+                        // packed pair (no second conversion; see the empty asm below).
                         constexpr int NDS = DST ? 8 : 32;
-                        unsigned ds_pair = 0;
                         auto st_ds = [&](auto kc) {
                             constexpr int k = decltype(kc)::value;
                             if constexpr (DST) {
@@ -716,12 +711,9 @@ void bwd_main_kernel(KParams p) {
                             } else {
                                 constexpr int G = k / 16, m = (k / 8) % 2, nt = (k / 4) % 2, i = k % 4;
                                 constexpr int e = 4 * m + i;
-                                if constexpr (e % 2 == 0) {
-                                    ds_pair = __builtin_bit_cast(u32x4, aS[G][nt])[e / 2];
-                                    asm volatile("" : "+v"(ds_pair));
-                                }
+                                const unsigned pair = __builtin_bit_cast(u32x4, aS[G][nt])[e / 2];
                                 sdS[(sub * BQ + (2 * G + m) * 16 + 4 * g + i) * LDSS + w * RW + nt * 16 + c16] =
-                                    __builtin_bit_cast(T, (unsigned short)(e % 2 ? ds_pair >> 16 : ds_pair));
+                                    __builtin_bit_cast(T, (unsigned short)(e % 2 ? pair >> 16 : pair));
                             }
                         };
                         auto mfma = [&](auto ic) {
@@ -775,6 +767,16 @@ void bwd_main_kernel(KParams p) {
                         });
                         static_for<0, NMF>([&](auto ic) {
                             constexpr int i = decltype(ic)::value;
+                            // a group's packed dS, once its softmax is complete and before
+                            // phase 2 reads it, passes an empty asm that hides its origin
+                            // from the optimiser: the dS stores then take their halves from
+                            // these registers instead of converting the fp32 values again
+                            // (emits no instruction, and no copy: nothing reads it earlier)
+                            if constexpr (i == 2 * A || i == 2 * A + B) {
+                                constexpr int G = i == 2 * A ? 0 : 1;
+                                asm volatile("" : "+v"(aS[G][0]));  // (NT == 2 on this path)
+                                asm volatile("" : "+v"(aS[G][1]));
+                            }
                             mfma(ic);
                             // the next sub-step's copies, one every DSTEP slots of phase 1
                             constexpr int DSTEP = (2 * A - 8) / NSLOT;
