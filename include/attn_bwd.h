@@ -29,8 +29,14 @@
  *  - Calls are asynchronous on the stream; device-side failures (a bounded
  *    flag wait that expired) are reported by attn_bwd_query_status().
  *  - Return value: ATTN_OK (0) or a negative attn_status_t.  No C++
- *    exception crosses the ABI.  attn_bwd_last_error() gives a message for
- *    the last failure on the calling thread.
+ *    exception crosses the ABI (every entry point catches them and returns
+ *    ATTN_ERR_INTERNAL).  attn_bwd_last_error() gives a message for the last
+ *    failure on the calling thread.
+ *  - Accepted sizes: s <= 262144 (at most 2048 tiles of 128 rows), b*h below
+ *    2^31 and b*h*s*d below 2^40; larger problems return
+ *    ATTN_ERR_UNSUPPORTED (s) or ATTN_ERR_INVALID_ARG (the others).
+ *  - scale must be a positive finite number (ATTN_ERR_INVALID_ARG
+ *    otherwise): masked logits are -inf before scaling.
  */
 #ifndef ATTN_BWD_H
 #define ATTN_BWD_H
@@ -70,10 +76,12 @@ typedef enum {
     ATTN_ERR_TIMEOUT = -5,      /* a device-side flag wait expired          */
     ATTN_ERR_WORKSPACE = -6,    /* caller workspace too small               */
     ATTN_ERR_DEADLOCK = -7,     /* simulator: the schedule cannot finish    */
-    ATTN_ERR_PLACEMENT = -8     /* XCD placement found work groups it could
+    ATTN_ERR_PLACEMENT = -8,    /* XCD placement found work groups it could
                                    not use as planned: an XCD without work
                                    groups or an unknown XCD id (results of
                                    that call invalid)                       */
+    ATTN_ERR_INTERNAL = -9      /* host memory exhausted, or another host-side
+                                   failure caught at the ABI boundary        */
 } attn_status_t;
 
 /* ------------------------------------------------------------------------
@@ -82,7 +90,9 @@ typedef enum {
 
 /* attn_bwd_deterministic - bf16 backward with scale = 1/sqrt(d), on the null
  * stream, with a library-owned workspace (allocated on first use and grown
- * as needed; one per device; calls must not overlap on one device).
+ * as needed; one per device).  Every call that uses the library workspace is
+ * ordered after the previous such call on the device: a call on another
+ * stream first waits (hipStreamWaitEvent) for the previous one to finish.
  *   q, k, v, o, dO : const bf16 [b][h][s][d]
  *   lse            : const float [b][h][s]
  *   dq, dk, dv     : bf16 [b][h][s][d], written
@@ -96,10 +106,11 @@ int attn_bwd_deterministic(const void* q, const void* k, const void* v, const vo
 /* attn_bwd_deterministic_ex - as above with explicit element type (tensors
  * q..dv are bf16 or fp32 per `dtype`; lse is always fp32), softmax scale,
  * stream (a hipStream_t, NULL for the null stream) and an optional caller
- * workspace.  workspace == NULL uses the library-owned one; otherwise it
- * must be device memory of at least attn_bwd_workspace_bytes(...) bytes
- * (ATTN_ERR_WORKSPACE if smaller), 256-byte aligned, owned by the caller
- * and not used concurrently by another call. */
+ * workspace.  workspace == NULL uses the library-owned one (ordered across
+ * streams as above); otherwise it must be device memory of at least
+ * attn_bwd_workspace_bytes(...) bytes (ATTN_ERR_WORKSPACE if smaller),
+ * 256-byte aligned, owned by the caller and not used concurrently by another
+ * call (the library does not order calls that share a caller workspace). */
 int attn_bwd_deterministic_ex(const void* q, const void* k, const void* v, const void* o,
                               const void* dO, const float* lse, void* dq, void* dk, void* dv,
                               int b, int h, int s, int d, int causal, int schedule,
@@ -181,8 +192,9 @@ int attn_bwd_get_wait_stats(unsigned long long* wait_cycles, unsigned long long*
  * independent of how work groups are scheduled.  Asynchronous on `stream`
  * (hipStream_t; NULL = default stream).  Returns ATTN_OK,
  * ATTN_ERR_INVALID_ARG (negative sizes, null or misaligned pointers, bad
- * causal or dtype, non-finite scale), ATTN_ERR_UNSUPPORTED (d not 64 or 128)
- * or ATTN_ERR_HIP (launch failure).  b*h == 0 or s == 0 is a no-op.
+ * causal or dtype, scale not positive and finite), ATTN_ERR_UNSUPPORTED (d
+ * not 64 or 128, s > 262144) or ATTN_ERR_HIP (launch failure).  b*h == 0 or
+ * s == 0 is a no-op.
  * ------------------------------------------------------------------------ */
 int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int b, int h, int s, int d,
              int causal, int dtype, float scale, void* stream);

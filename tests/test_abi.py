@@ -90,3 +90,123 @@ def test_forward_argument_errors_need_no_gpu():
     assert "aligned" in tsa.last_error()
     assert _fwd(q=16, k=16, v=16, o=16, lse=2) == -1
     assert _fwd(b=0) == 0 and _fwd(s=0) == 0
+
+
+def test_scale_must_be_positive():
+    """Masked logits start at -inf before the scale multiplies them: a zero
+    scale would turn them into NaN and a negative one into +inf, so both
+    entry points reject scale <= 0 before touching the GPU."""
+    ptrs = dict(q=16, k=16, v=16, o=16, dO=16, lse=16, dq=16, dk=16, dv=16)
+    for bad in (0.0, -0.0, -0.125, float("-inf")):
+        assert _call(scale=bad, **ptrs) == -1, bad
+        assert "positive" in tsa.last_error()
+        assert _fwd(scale=bad, q=16, k=16, v=16, o=16, lse=16) == -1, bad
+        assert "positive" in tsa.last_error()
+
+
+def test_size_limits_return_status_codes():
+    """Sizes past the library's limits come back as status codes instead of
+    overflowing 32-bit offsets or exhausting host memory."""
+    ptrs = dict(q=16, k=16, v=16, o=16, dO=16, lse=16, dq=16, dk=16, dv=16)
+    assert _call(s=262145, **ptrs) == -2
+    assert "262144" in tsa.last_error()
+    assert _fwd(s=262145, q=16, k=16, v=16, o=16, lse=16) == -2
+    assert _call(b=65536, h=65536, **ptrs) == -1            # b*h beyond an int
+    assert _call(b=1 << 14, h=1 << 10, s=262144, d=128, **ptrs) == -1  # b*h*s*d >= 2^40
+    assert tsa.attn_bwd_workspace_bytes(1, 1, 262145, 128, 0, 0) == 0
+    assert tsa.attn_bwd_workspace_bytes(65536, 65536, 128, 64, 0, 0) == 0
+    # the host-side schedule tools bound n and the simulated problem
+    for fn in (lambda: tsa.attn_sched_size(2049, 0, "shift"),
+               lambda: tsa.attn_sched_min_workers(2049, 1, "naive"),
+               lambda: tsa.attn_dagsim(2049, 0, "shift", 1, 8, 1, 1.0, 1.0),
+               lambda: tsa.attn_dagsim(2048, 0, "naive", 64, 8, 1, 1.0, 1.0),      # 2^28 tasks
+               lambda: tsa.attn_dagsim(8, 0, "naive", 1, (1 << 20) + 1, 1, 1.0, 1.0)):
+        with pytest.raises(tsa.AttnError) as e:
+            fn()
+        assert e.value.code == -2
+    assert tsa.attn_sched_size(2048, 1, "symmetric_shift")[0] == 1024
+
+
+def test_status_codes_are_named():
+    for code in (-1, -2, -3, -4, -5, -6, -7, -8, -9):
+        assert code in tsa.STATUS
+    header = open(HEADER).read()
+    for code, name in tsa.STATUS.items():
+        assert re.search(rf"\b{name}\s*=\s*{code}\b", header), name
+
+
+# ------------------------------------------------------------ binding checks
+torch = pytest.importorskip("torch")
+
+
+@pytest.fixture
+def host_as_device(monkeypatch):
+    """Let host tensors stand in for device tensors so that the binding's
+    shape, type, layout and placement checks can be exercised without a GPU;
+    every case below must be rejected before the C ABI is called."""
+    monkeypatch.setattr(tsa, "_on_device", lambda t: True)
+
+
+def _inputs(dtype=None, b=1, h=2, s=16, d=64):
+    dtype = dtype or torch.bfloat16
+    q, k, v, o, do = (torch.zeros(b, h, s, d, dtype=dtype) for _ in range(5))
+    lse = torch.zeros(b, h, s, dtype=torch.float32)
+    return q, k, v, o, do, lse
+
+
+def test_backward_rejects_host_tensors():
+    q, k, v, o, do, lse = _inputs()
+    with pytest.raises(ValueError, match="device tensor"):
+        tsa.backward(q, k, v, o, do, lse, False)
+
+
+@pytest.mark.parametrize("case", ["lse_dtype", "lse_shape", "lse_layout", "k_shape", "v_dtype",
+                                  "dq_dtype", "dk_shape", "dv_layout", "out_device", "ws_layout",
+                                  "ws_device", "q_rank", "q_dtype"])
+def test_backward_rejects_bad_tensors(host_as_device, case):
+    q, k, v, o, do, lse = _inputs()
+    out = [torch.zeros_like(q) for _ in range(3)]
+    ws = None
+    if case == "lse_dtype":
+        lse = lse.double()
+    elif case == "lse_shape":
+        lse = torch.zeros(1, 2, 15)
+    elif case == "lse_layout":
+        lse = torch.zeros(1, 2, 32)[:, :, ::2]
+    elif case == "k_shape":
+        k = torch.zeros(1, 2, 16, 128, dtype=torch.bfloat16)
+    elif case == "v_dtype":
+        v = v.float()
+    elif case == "dq_dtype":
+        out[0] = out[0].float()
+    elif case == "dk_shape":
+        out[1] = torch.zeros(1, 2, 8, 64, dtype=torch.bfloat16)
+    elif case == "dv_layout":
+        out[2] = torch.zeros(1, 2, 64, 16, dtype=torch.bfloat16).transpose(2, 3)
+    elif case == "out_device":
+        out[0] = torch.empty_like(q, device="meta")
+    elif case == "ws_layout":
+        ws = torch.zeros(64, 64, dtype=torch.uint8)[:, ::2]
+    elif case == "ws_device":
+        ws = torch.empty(4096, dtype=torch.uint8, device="meta")
+    elif case == "q_rank":
+        q = q[0]
+    elif case == "q_dtype":
+        q, k, v, o, do = (t.half() for t in (q, k, v, o, do))
+    with pytest.raises(ValueError):
+        tsa.backward(q, k, v, o, do, lse, False, out=out, workspace=ws, stream=0)
+
+
+@pytest.mark.parametrize("case", ["o_dtype", "lse_shape", "lse_dtype", "o_device"])
+def test_forward_rejects_bad_outputs(host_as_device, case):
+    q, k, v, o, _, lse = _inputs()
+    if case == "o_dtype":
+        o = o.float()
+    elif case == "lse_shape":
+        lse = torch.zeros(1, 2, 16, 1)
+    elif case == "lse_dtype":
+        lse = lse.half()
+    elif case == "o_device":
+        o = torch.empty_like(q, device="meta")
+    with pytest.raises(ValueError):
+        tsa.forward(q, k, v, False, out=(o, lse), stream=0)

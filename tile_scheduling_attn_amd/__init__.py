@@ -20,7 +20,8 @@ SCHEDULES = {"naive": 0, "descending": 1, "shift": 2, "symmetric_shift": 3, "ato
 DTYPES = {"bf16": 0, "fp32": 1}
 STATUS = {0: "ATTN_OK", -1: "ATTN_ERR_INVALID_ARG", -2: "ATTN_ERR_UNSUPPORTED",
           -3: "ATTN_ERR_COSCHEDULE", -4: "ATTN_ERR_HIP", -5: "ATTN_ERR_TIMEOUT",
-          -6: "ATTN_ERR_WORKSPACE", -7: "ATTN_ERR_DEADLOCK", -8: "ATTN_ERR_PLACEMENT"}
+          -6: "ATTN_ERR_WORKSPACE", -7: "ATTN_ERR_DEADLOCK", -8: "ATTN_ERR_PLACEMENT",
+          -9: "ATTN_ERR_INTERNAL"}
 
 # every function declared in include/attn_bwd.h
 EXPORTS = ("attn_fwd", "attn_bwd_deterministic", "attn_bwd_deterministic_ex", "attn_bwd_workspace_bytes",
@@ -261,23 +262,66 @@ def attn_sched_fit(samples, placement=1):
 # ---------------------------------------------------------------------------
 # Torch convenience wrapper (allocation and stream only)
 # ---------------------------------------------------------------------------
+def _on_device(t) -> bool:
+    """Whether a tensor lives in device memory (the kernels dereference every
+    pointer on the GPU)."""
+    return bool(t.is_cuda)
+
+
+def _require(t, name, shape, dtype, device):
+    """Raise ValueError unless `t` is a contiguous device tensor of `shape`
+    and `dtype` on `device`: a wrong size, type or placement would make the
+    kernels read or write outside the tensor."""
+    if t is None:
+        raise ValueError(f"{name} is missing")
+    if not _on_device(t) or t.device != device:
+        raise ValueError(f"{name} must be a device tensor on {device}, got {t.device}")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+    if t.dtype != dtype:
+        raise ValueError(f"{name} must have dtype {dtype}, got {t.dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def _require_inputs(q, names_tensors):
+    import torch
+    if q.dim() != 4:
+        raise ValueError(f"q must be [b, h, s, d], got shape {tuple(q.shape)}")
+    if q.dtype not in (torch.bfloat16, torch.float32):
+        raise ValueError("q must be bfloat16 or float32")
+    if not _on_device(q):
+        raise ValueError("q must be a device tensor")
+    for name, t in names_tensors:
+        _require(t, name, q.shape, q.dtype, q.device)
+
+
+def _require_workspace(workspace, device):
+    """A caller workspace: contiguous device memory on `device`; returns
+    (pointer, bytes)."""
+    if workspace is None:
+        return 0, 0
+    if not _on_device(workspace) or workspace.device != device:
+        raise ValueError(f"workspace must be a device tensor on {device}")
+    if not workspace.is_contiguous():
+        raise ValueError("workspace must be contiguous")
+    return workspace.data_ptr(), workspace.numel() * workspace.element_size()
+
+
 def forward(q, k, v, causal: bool, scale=None, out=None, stream=None):
     """Attention forward on torch tensors [b, h, s, d] (bf16 or fp32,
     contiguous, on the current HIP device).  Returns (o, lse) with lse
     [b, h, s] fp32, allocated unless `out` gives them.  Asynchronous on
     `stream` (default: torch's current stream)."""
     import torch
+    _require_inputs(q, (("q", q), ("k", k), ("v", v)))
     b, h, s, d = q.shape
-    for name, t in (("q", q), ("k", k), ("v", v)):
-        if tuple(t.shape) != (b, h, s, d) or t.dtype != q.dtype or not t.is_contiguous() or not t.is_cuda:
-            raise ValueError(f"{name} must be a contiguous device tensor of shape {(b, h, s, d)} "
-                             f"and dtype {q.dtype}")
-    dtype = {torch.bfloat16: "bf16", torch.float32: "fp32"}.get(q.dtype)
-    if dtype is None:
-        raise ValueError("q must be bfloat16 or float32")
+    dtype = {torch.bfloat16: "bf16", torch.float32: "fp32"}[q.dtype]
     if out is None:
         out = (torch.empty_like(q), torch.empty((b, h, s), dtype=torch.float32, device=q.device))
     o, lse = out
+    _require(o, "out[0] (o)", q.shape, q.dtype, q.device)
+    _require(lse, "out[1] (lse)", (b, h, s), torch.float32, q.device)
     if scale is None:
         scale = 1.0 / math.sqrt(d)
     if stream is None:
@@ -293,26 +337,20 @@ def backward(q, k, v, o, do, lse, causal: bool, schedule="shift", scale=None, ou
     allocated unless `out` gives them.  The call is asynchronous on `stream`
     (default: torch's current stream)."""
     import torch
+    _require_inputs(q, (("q", q), ("k", k), ("v", v), ("o", o), ("do", do)))
     b, h, s, d = q.shape
-    for name, t in (("q", q), ("k", k), ("v", v), ("o", o), ("do", do)):
-        if tuple(t.shape) != (b, h, s, d) or t.dtype != q.dtype or not t.is_contiguous() \
-                or not t.is_cuda:
-            raise ValueError(f"{name} must be a contiguous device tensor of shape {(b, h, s, d)} "
-                             f"and dtype {q.dtype}")
-    if tuple(lse.shape) != (b, h, s) or lse.dtype != torch.float32 or not lse.is_contiguous():
-        raise ValueError("lse must be a contiguous float32 tensor [b, h, s]")
-    dtype = {torch.bfloat16: "bf16", torch.float32: "fp32"}.get(q.dtype)
-    if dtype is None:
-        raise ValueError("q must be bfloat16 or float32")
+    _require(lse, "lse", (b, h, s), torch.float32, q.device)
+    dtype = {torch.bfloat16: "bf16", torch.float32: "fp32"}[q.dtype]
     if out is None:
         out = (torch.empty_like(q), torch.empty_like(q), torch.empty_like(q))
     dq, dk, dv = out
+    for name, t in (("out[0] (dq)", dq), ("out[1] (dk)", dk), ("out[2] (dv)", dv)):
+        _require(t, name, q.shape, q.dtype, q.device)
+    ws_ptr, ws_bytes = _require_workspace(workspace, q.device)
     if scale is None:
         scale = 1.0 / math.sqrt(d)
     if stream is None:
         stream = torch.cuda.current_stream().cuda_stream
-    ws_ptr, ws_bytes = (0, 0) if workspace is None else (workspace.data_ptr(), workspace.numel() *
-                                                         workspace.element_size())
     rc = attn_bwd_deterministic_ex(q, k, v, o, do, lse, dq, dk, dv, b, h, s, d, causal, schedule,
                                    dtype, scale, ws_ptr, ws_bytes, stream)
     _check(rc, "attn_bwd_deterministic_ex")

@@ -25,6 +25,15 @@ int fail(int code, const char* msg) {
     return code;
 }
 
+int fail_internal(const char* msg) noexcept {
+    try {
+        g_last_error = msg;
+    } catch (...) {
+        g_last_error.clear();
+    }
+    return ATTN_ERR_INTERNAL;
+}
+
 static int fail_hip(hipError_t e, const char* what) {
     g_last_error = std::string(what) + ": " + hipGetErrorString(e);
     return ATTN_ERR_HIP;
@@ -34,6 +43,10 @@ constexpr size_t kAlign = 256;
 constexpr int kPadRows = 128;     // s is padded to a multiple of this
 constexpr int kMinTile = 64;      // smallest tile: bounds the flag count
 constexpr int kCounterWords = 64; // ticket + wait statistics
+// Accepted sizes: s up to kMaxTiles tiles of the largest tile edge (128), and
+// b*h within an int (the kernels index heads with ints).
+constexpr int kMaxSeq = kMaxTiles * 128;
+constexpr long long kMaxHeads = (1LL << 31) - 1;
 
 static size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 
@@ -73,6 +86,11 @@ struct DevState {
     bool xcd_ok = false;  // work group b runs on XCD b % kQueues
     void* ws = nullptr;
     size_t ws_bytes = 0;
+    // the library workspace is shared by every call on the device: a call on
+    // another stream than the previous user first waits for its completion
+    hipEvent_t ws_done = nullptr;
+    void* ws_stream = nullptr;
+    bool ws_used = false;
     unsigned* status = nullptr;
     std::map<std::tuple<int, int, int>, DevSchedule> schedules;
     // kernel timing: 4 events per recorded call (before preprocess, before
@@ -143,7 +161,7 @@ static int get_schedule(DevState& ds, int n, bool causal, int schedule, DevSched
     if (e != hipSuccess) return fail_hip(e, "hipMalloc(schedule)");
     e = hipMemcpy(d.buf, host.data(), host.size() * sizeof(int), hipMemcpyHostToDevice);
     if (e != hipSuccess) {
-        hipFree(d.buf);
+        (void)hipFree(d.buf);
         return fail_hip(e, "hipMemcpy(schedule)");
     }
     d.items = sc.num_items();
@@ -176,11 +194,14 @@ static int backward(const void* q, const void* k, const void* v, const void* o, 
     if (schedule < ATTN_SCHED_NAIVE || schedule > ATTN_SCHED_ATOMIC)
         return fail(ATTN_ERR_INVALID_ARG, "unknown schedule");
     if (dtype != ATTN_BF16 && dtype != ATTN_FP32) return fail(ATTN_ERR_INVALID_ARG, "unknown dtype");
-    if (!std::isfinite(scale)) return fail(ATTN_ERR_INVALID_ARG, "scale must be finite");
+    if (!std::isfinite(scale) || !(scale > 0))
+        return fail(ATTN_ERR_INVALID_ARG, "scale must be a positive finite number");
     if (d != 64 && d != 128) return fail(ATTN_ERR_UNSUPPORTED, "head dimension must be 64 or 128");
     const long long H = (long long)b * h;
     if (H == 0 || s == 0) return ATTN_OK;
-    if (H * (long long)s * d >= (1LL << 40)) return fail(ATTN_ERR_INVALID_ARG, "problem too large");
+    if (s > kMaxSeq) return fail(ATTN_ERR_UNSUPPORTED, "sequence length above 262144 is not supported");
+    if (H > kMaxHeads || H * (long long)s * d >= (1LL << 40))
+        return fail(ATTN_ERR_INVALID_ARG, "problem too large");
     if (!q || !k || !v || !o || !dO || !lse || !dq || !dk || !dv)
         return fail(ATTN_ERR_INVALID_ARG, "null tensor pointer");
     const uintptr_t mis = (uintptr_t)q | (uintptr_t)k | (uintptr_t)v | (uintptr_t)o | (uintptr_t)dO |
@@ -190,8 +211,7 @@ static int backward(const void* q, const void* k, const void* v, const void* o, 
         return fail(ATTN_ERR_INVALID_ARG, "workspace must be 256-byte aligned");
 
     const int tile = tile_for(dtype);
-    const int n = (s + tile - 1) / tile;
-    if (n >= (1 << 24)) return fail(ATTN_ERR_UNSUPPORTED, "sequence too long: more than 2^24 - 1 tiles");
+    const int n = (s + tile - 1) / tile;  // <= kMaxTiles since s <= kMaxSeq
 
     std::lock_guard<std::mutex> lock(g_mutex);
     int dev = 0;
@@ -218,12 +238,22 @@ static int backward(const void* q, const void* k, const void* v, const void* o, 
         use_xcd = use_xcd && workspace_bytes >= wl_xcd.total;
     }
     if (use_xcd) wl = wl_xcd;
-    if (!ws) {
+    const bool lib_ws = ws == nullptr;
+    if (lib_ws) {
+        if (!ds.ws_done) {
+            e = hipEventCreateWithFlags(&ds.ws_done, hipEventDisableTiming);
+            if (e != hipSuccess) return fail_hip(e, "hipEventCreateWithFlags");
+        }
+        // order this call after the previous user of the library workspace
+        if (ds.ws_used && ds.ws_stream != stream) {
+            e = hipStreamWaitEvent((hipStream_t)stream, ds.ws_done, 0);
+            if (e != hipSuccess) return fail_hip(e, "hipStreamWaitEvent");
+        }
         if (ds.ws_bytes < wl.total) {
             if (ds.ws) {
                 e = hipDeviceSynchronize();
                 if (e != hipSuccess) return fail_hip(e, "hipDeviceSynchronize");
-                hipFree(ds.ws);
+                (void)hipFree(ds.ws);
                 ds.ws = nullptr;
                 ds.ws_bytes = 0;
             }
@@ -277,6 +307,12 @@ static int backward(const void* q, const void* k, const void* v, const void* o, 
 
     rc = launch_backward(a, L);
     if (rc != ATTN_OK) return rc;
+    if (lib_ws) {
+        e = hipEventRecord(ds.ws_done, (hipStream_t)stream);
+        if (e != hipSuccess) return fail_hip(e, "hipEventRecord");
+        ds.ws_stream = stream;
+        ds.ws_used = true;
+    }
     if (ev) {
         if (ds.ev_finalize.size() <= ds.ev_used) ds.ev_finalize.resize(ds.ev_used + 1);
         ds.ev_finalize[ds.ev_used] = schedule == ATTN_SCHED_ATOMIC;
@@ -295,168 +331,197 @@ using namespace attn;
 extern "C" int attn_bwd_deterministic(const void* q, const void* k, const void* v, const void* o,
                                       const void* dO, const float* lse, void* dq, void* dk, void* dv,
                                       int b, int h, int s, int d, int causal, int schedule) {
-    const float scale = (d > 0) ? 1.0f / std::sqrt((float)d) : 1.0f;
-    return backward(q, k, v, o, dO, lse, dq, dk, dv, b, h, s, d, causal, schedule, ATTN_BF16, scale,
-                    nullptr, 0, nullptr);
+    return guarded([&]() -> int {
+        const float scale = (d > 0) ? 1.0f / std::sqrt((float)d) : 1.0f;
+        return backward(q, k, v, o, dO, lse, dq, dk, dv, b, h, s, d, causal, schedule, ATTN_BF16, scale,
+                        nullptr, 0, nullptr);
+    });
 }
 
 extern "C" int attn_bwd_deterministic_ex(const void* q, const void* k, const void* v, const void* o,
                                          const void* dO, const float* lse, void* dq, void* dk, void* dv,
                                          int b, int h, int s, int d, int causal, int schedule, int dtype,
                                          float scale, void* workspace, size_t workspace_bytes, void* stream) {
-    return backward(q, k, v, o, dO, lse, dq, dk, dv, b, h, s, d, causal, schedule, dtype, scale, workspace,
-                    workspace_bytes, stream);
+    return guarded([&]() -> int {
+        return backward(q, k, v, o, dO, lse, dq, dk, dv, b, h, s, d, causal, schedule, dtype, scale, workspace,
+                        workspace_bytes, stream);
+    });
 }
 
 extern "C" int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int b, int h, int s,
                         int d, int causal, int dtype, float scale, void* stream) {
-    g_last_error.clear();
-    if (b < 0 || h < 0 || s < 0) return fail(ATTN_ERR_INVALID_ARG, "b, h and s must be >= 0");
-    if (causal != 0 && causal != 1) return fail(ATTN_ERR_INVALID_ARG, "causal must be 0 or 1");
-    if (dtype != ATTN_BF16 && dtype != ATTN_FP32) return fail(ATTN_ERR_INVALID_ARG, "unknown dtype");
-    if (!std::isfinite(scale)) return fail(ATTN_ERR_INVALID_ARG, "scale must be finite");
-    if (d != 64 && d != 128) return fail(ATTN_ERR_UNSUPPORTED, "head dimension must be 64 or 128");
-    const long long H = (long long)b * h;
-    if (H == 0 || s == 0) return ATTN_OK;
-    if (H * (long long)s * d >= (1LL << 40)) return fail(ATTN_ERR_INVALID_ARG, "problem too large");
-    if (!q || !k || !v || !o || !lse) return fail(ATTN_ERR_INVALID_ARG, "null tensor pointer");
-    if (((uintptr_t)q | (uintptr_t)k | (uintptr_t)v | (uintptr_t)o) & 15)
-        return fail(ATTN_ERR_INVALID_ARG, "tensor pointers must be 16-byte aligned");
-    if ((uintptr_t)lse & 3) return fail(ATTN_ERR_INVALID_ARG, "lse must be 4-byte aligned");
-    FwdArgs a{};
-    a.q = q; a.k = k; a.v = v; a.o = o; a.lse = lse;
-    a.H = (int)H; a.s = s; a.d = d; a.causal = causal != 0; a.dtype = dtype; a.scale = scale;
-    a.stream = stream;
-    return launch_forward(a);
+    return guarded([&]() -> int {
+        g_last_error.clear();
+        if (b < 0 || h < 0 || s < 0) return fail(ATTN_ERR_INVALID_ARG, "b, h and s must be >= 0");
+        if (causal != 0 && causal != 1) return fail(ATTN_ERR_INVALID_ARG, "causal must be 0 or 1");
+        if (dtype != ATTN_BF16 && dtype != ATTN_FP32) return fail(ATTN_ERR_INVALID_ARG, "unknown dtype");
+        if (!std::isfinite(scale) || !(scale > 0))
+            return fail(ATTN_ERR_INVALID_ARG, "scale must be a positive finite number");
+        if (d != 64 && d != 128) return fail(ATTN_ERR_UNSUPPORTED, "head dimension must be 64 or 128");
+        const long long H = (long long)b * h;
+        if (H == 0 || s == 0) return ATTN_OK;
+        if (s > kMaxSeq) return fail(ATTN_ERR_UNSUPPORTED, "sequence length above 262144 is not supported");
+        if (H > kMaxHeads || H * (long long)s * d >= (1LL << 40))
+            return fail(ATTN_ERR_INVALID_ARG, "problem too large");
+        if (!q || !k || !v || !o || !lse) return fail(ATTN_ERR_INVALID_ARG, "null tensor pointer");
+        if (((uintptr_t)q | (uintptr_t)k | (uintptr_t)v | (uintptr_t)o) & 15)
+            return fail(ATTN_ERR_INVALID_ARG, "tensor pointers must be 16-byte aligned");
+        if ((uintptr_t)lse & 3) return fail(ATTN_ERR_INVALID_ARG, "lse must be 4-byte aligned");
+        FwdArgs a{};
+        a.q = q; a.k = k; a.v = v; a.o = o; a.lse = lse;
+        a.H = (int)H; a.s = s; a.d = d; a.causal = causal != 0; a.dtype = dtype; a.scale = scale;
+        a.stream = stream;
+        return launch_forward(a);
+    });
 }
 
 extern "C" size_t attn_bwd_workspace_bytes(int b, int h, int s, int d, int causal, int schedule) {
-    if (b < 0 || h < 0 || s < 0) return 0;
-    const long long H = (long long)b * h;
-    WsLayout wl;
-    if (!ws_layout(H, s, d, H, wl)) return 0;
-    size_t total = wl.total;
-    // what XCD placement needs on the current device (either tile edge)
-    if (H > 0 && s > 0 && (causal == 0 || causal == 1) && schedule >= ATTN_SCHED_NAIVE &&
-        schedule < ATTN_SCHED_ATOMIC) {
-        std::lock_guard<std::mutex> lock(g_mutex);
-        int dev = 0;
-        if (hipGetDevice(&dev) == hipSuccess) {
-            DevState& ds = g_dev[dev];
-            if (dev_init(dev, ds) == ATTN_OK) {
-                for (int tile : {64, 128}) {
-                    const int n = (s + tile - 1) / tile;
-                    Schedule sc;
-                    if (n >= (1 << 24) || build_schedule(n, causal != 0, schedule, sc) != ATTN_OK) continue;
-                    DevSchedule shape;
-                    shape.items = sc.num_items();
-                    shape.item_begin = sc.item_begin;
-                    shape.min_workers = min_workers(sc);
-                    const XcdPlan plan = placement_plan(ds, shape, schedule, H);
-                    WsLayout w2;
-                    if (plan.chunks && ws_layout(H, s, d, kQueues * plan.slots, w2)) total = std::max(total, w2.total);
+    try {
+        if (b < 0 || h < 0 || s < 0 || s > kMaxSeq) return 0;
+        const long long H = (long long)b * h;
+        if (H > kMaxHeads || H * (long long)s * d >= (1LL << 40)) return 0;
+        WsLayout wl;
+        if (!ws_layout(H, s, d, H, wl)) return 0;
+        size_t total = wl.total;
+        // what XCD placement needs on the current device (either tile edge)
+        if (H > 0 && s > 0 && (causal == 0 || causal == 1) && schedule >= ATTN_SCHED_NAIVE &&
+            schedule < ATTN_SCHED_ATOMIC) {
+            std::lock_guard<std::mutex> lock(g_mutex);
+            int dev = 0;
+            if (hipGetDevice(&dev) == hipSuccess) {
+                DevState& ds = g_dev[dev];
+                if (dev_init(dev, ds) == ATTN_OK) {
+                    for (int tile : {64, 128}) {
+                        const int n = (s + tile - 1) / tile;
+                        Schedule sc;
+                        if (build_schedule(n, causal != 0, schedule, sc) != ATTN_OK) continue;
+                        DevSchedule shape;
+                        shape.items = sc.num_items();
+                        shape.item_begin = sc.item_begin;
+                        shape.min_workers = min_workers(sc);
+                        const XcdPlan plan = placement_plan(ds, shape, schedule, H);
+                        WsLayout w2;
+                        if (plan.chunks && ws_layout(H, s, d, kQueues * plan.slots, w2)) total = std::max(total, w2.total);
+                    }
                 }
             }
+            g_last_error.clear();
         }
-        g_last_error.clear();
+        return total;
+    } catch (...) {
+        fail_internal("host memory exhausted or unexpected host-side error");
+        return 0;
     }
-    return total;
 }
 
 extern "C" int attn_bwd_query_status(void* stream) {
-    g_last_error.clear();
-    hipError_t e = hipStreamSynchronize((hipStream_t)stream);
-    if (e != hipSuccess) return fail_hip(e, "hipStreamSynchronize");
-    std::lock_guard<std::mutex> lock(g_mutex);
-    int dev = 0;
-    e = hipGetDevice(&dev);
-    if (e != hipSuccess) return fail_hip(e, "hipGetDevice");
-    auto it = g_dev.find(dev);
-    if (it == g_dev.end() || !it->second.init) return ATTN_OK;
-    unsigned st = 0;
-    e = hipMemcpy(&st, it->second.status, sizeof(unsigned), hipMemcpyDeviceToHost);
-    if (e != hipSuccess) return fail_hip(e, "hipMemcpy(status)");
-    if (st) {
-        e = hipMemset(it->second.status, 0, sizeof(unsigned));
-        if (e != hipSuccess) return fail_hip(e, "hipMemset(status)");
-        if (st & 1u) return fail(ATTN_ERR_TIMEOUT, "a dQ flag wait expired; the results of that call are invalid");
-        return fail(ATTN_ERR_PLACEMENT, "XCD placement could not use the work groups as planned (an XCD "
-                                        "without work groups or an unknown XCD id); the results of that call "
-                                        "are invalid");
-    }
-    return ATTN_OK;
+    return guarded([&]() -> int {
+        g_last_error.clear();
+        hipError_t e = hipStreamSynchronize((hipStream_t)stream);
+        if (e != hipSuccess) return fail_hip(e, "hipStreamSynchronize");
+        std::lock_guard<std::mutex> lock(g_mutex);
+        int dev = 0;
+        e = hipGetDevice(&dev);
+        if (e != hipSuccess) return fail_hip(e, "hipGetDevice");
+        auto it = g_dev.find(dev);
+        if (it == g_dev.end() || !it->second.init) return ATTN_OK;
+        unsigned st = 0;
+        e = hipMemcpy(&st, it->second.status, sizeof(unsigned), hipMemcpyDeviceToHost);
+        if (e != hipSuccess) return fail_hip(e, "hipMemcpy(status)");
+        if (st) {
+            e = hipMemset(it->second.status, 0, sizeof(unsigned));
+            if (e != hipSuccess) return fail_hip(e, "hipMemset(status)");
+            if (st & 1u) return fail(ATTN_ERR_TIMEOUT, "a dQ flag wait expired; the results of that call are invalid");
+            return fail(ATTN_ERR_PLACEMENT, "XCD placement could not use the work groups as planned (an XCD "
+                                            "without work groups or an unknown XCD id); the results of that call "
+                                            "are invalid");
+        }
+        return ATTN_OK;
+    });
 }
 
 extern "C" const char* attn_bwd_last_error(void) { return g_last_error.c_str(); }
 
 extern "C" int attn_bwd_tile_size(int dtype) {
-    if (dtype != ATTN_BF16 && dtype != ATTN_FP32) return fail(ATTN_ERR_INVALID_ARG, "unknown dtype");
-    return tile_for(dtype);
+    return guarded([&]() -> int {
+        if (dtype != ATTN_BF16 && dtype != ATTN_FP32) return fail(ATTN_ERR_INVALID_ARG, "unknown dtype");
+        return tile_for(dtype);
+    });
 }
 
 extern "C" int attn_bwd_set_timing(int on) {
-    std::lock_guard<std::mutex> lock(g_mutex);
-    g_timing = on != 0;
-    if (g_timing)
-        for (auto& kv : g_dev) kv.second.ev_used = 0;
-    return ATTN_OK;
+    return guarded([&]() -> int {
+        std::lock_guard<std::mutex> lock(g_mutex);
+        g_timing = on != 0;
+        if (g_timing)
+            for (auto& kv : g_dev) kv.second.ev_used = 0;
+        return ATTN_OK;
+    });
 }
 
 extern "C" int attn_bwd_get_kernel_times(float* ms_pre, float* ms_main, float* ms_fin) {
-    std::lock_guard<std::mutex> lock(g_mutex);
-    if (ms_pre) *ms_pre = 0.f;
-    if (ms_main) *ms_main = 0.f;
-    if (ms_fin) *ms_fin = 0.f;
-    auto it = g_dev.find(g_last_dev);
-    if (it == g_dev.end() || it->second.ev_used == 0) return fail(ATTN_ERR_INVALID_ARG, "no timed call recorded");
-    DevState& ds = it->second;
-    const size_t calls = ds.ev_used;
-    hipError_t e = hipEventSynchronize(ds.ev_pool[4 * calls - 1]);
-    if (e != hipSuccess) return fail_hip(e, "hipEventSynchronize");
-    double sum[3] = {0, 0, 0};
-    for (size_t c = 0; c < calls; ++c) {
-        hipEvent_t* ev = &ds.ev_pool[4 * c];
-        for (int k = 0; k < 3; ++k) {
-            if (k == 2 && !ds.ev_finalize[c]) continue;
-            float t = 0.f;
-            e = hipEventElapsedTime(&t, ev[k], ev[k + 1]);
-            if (e != hipSuccess) return fail_hip(e, "hipEventElapsedTime");
-            sum[k] += t;
+    return guarded([&]() -> int {
+        std::lock_guard<std::mutex> lock(g_mutex);
+        if (ms_pre) *ms_pre = 0.f;
+        if (ms_main) *ms_main = 0.f;
+        if (ms_fin) *ms_fin = 0.f;
+        auto it = g_dev.find(g_last_dev);
+        if (it == g_dev.end() || it->second.ev_used == 0) return fail(ATTN_ERR_INVALID_ARG, "no timed call recorded");
+        DevState& ds = it->second;
+        const size_t calls = ds.ev_used;
+        hipError_t e = hipEventSynchronize(ds.ev_pool[4 * calls - 1]);
+        if (e != hipSuccess) return fail_hip(e, "hipEventSynchronize");
+        double sum[3] = {0, 0, 0};
+        for (size_t c = 0; c < calls; ++c) {
+            hipEvent_t* ev = &ds.ev_pool[4 * c];
+            for (int k = 0; k < 3; ++k) {
+                if (k == 2 && !ds.ev_finalize[c]) continue;
+                float t = 0.f;
+                e = hipEventElapsedTime(&t, ev[k], ev[k + 1]);
+                if (e != hipSuccess) return fail_hip(e, "hipEventElapsedTime");
+                sum[k] += t;
+            }
         }
-    }
-    if (ms_pre) *ms_pre = (float)(sum[0] / calls);
-    if (ms_main) *ms_main = (float)(sum[1] / calls);
-    if (ms_fin) *ms_fin = (float)(sum[2] / calls);
-    return ATTN_OK;
+        if (ms_pre) *ms_pre = (float)(sum[0] / calls);
+        if (ms_main) *ms_main = (float)(sum[1] / calls);
+        if (ms_fin) *ms_fin = (float)(sum[2] / calls);
+        return ATTN_OK;
+    });
 }
 
 extern "C" int attn_bwd_set_placement(int mode) {
-    if (mode != ATTN_PLACE_GLOBAL && mode != ATTN_PLACE_XCD)
-        return fail(ATTN_ERR_INVALID_ARG, "attn_bwd_set_placement: mode must be ATTN_PLACE_GLOBAL or ATTN_PLACE_XCD");
-    std::lock_guard<std::mutex> lock(g_mutex);
-    g_xcd_placement = mode == ATTN_PLACE_XCD;
-    return ATTN_OK;
+    return guarded([&]() -> int {
+        if (mode != ATTN_PLACE_GLOBAL && mode != ATTN_PLACE_XCD)
+            return fail(ATTN_ERR_INVALID_ARG, "attn_bwd_set_placement: mode must be ATTN_PLACE_GLOBAL or ATTN_PLACE_XCD");
+        std::lock_guard<std::mutex> lock(g_mutex);
+        g_xcd_placement = mode == ATTN_PLACE_XCD;
+        return ATTN_OK;
+    });
 }
 
 extern "C" int attn_bwd_set_wait_stats(int on) {
-    std::lock_guard<std::mutex> lock(g_mutex);
-    g_wait_stats = on != 0;
-    return ATTN_OK;
+    return guarded([&]() -> int {
+        std::lock_guard<std::mutex> lock(g_mutex);
+        g_wait_stats = on != 0;
+        return ATTN_OK;
+    });
 }
 
 extern "C" int attn_bwd_get_wait_stats(unsigned long long* wait_cycles, unsigned long long* item_cycles,
                                        unsigned long long* polls) {
-    std::lock_guard<std::mutex> lock(g_mutex);
-    auto it = g_dev.find(g_last_dev);
-    if (it == g_dev.end() || !it->second.stats_valid || !it->second.last_counters)
-        return fail(ATTN_ERR_INVALID_ARG, "no call with wait statistics recorded");
-    hipError_t e = hipDeviceSynchronize();
-    if (e != hipSuccess) return fail_hip(e, "hipDeviceSynchronize");
-    unsigned long long v[3] = {0, 0, 0};
-    e = hipMemcpy(v, static_cast<unsigned*>(it->second.last_counters) + 2, sizeof(v), hipMemcpyDeviceToHost);
-    if (e != hipSuccess) return fail_hip(e, "hipMemcpy(stats)");
-    if (wait_cycles) *wait_cycles = v[0];
-    if (item_cycles) *item_cycles = v[1];
-    if (polls) *polls = v[2];
-    return ATTN_OK;
+    return guarded([&]() -> int {
+        std::lock_guard<std::mutex> lock(g_mutex);
+        auto it = g_dev.find(g_last_dev);
+        if (it == g_dev.end() || !it->second.stats_valid || !it->second.last_counters)
+            return fail(ATTN_ERR_INVALID_ARG, "no call with wait statistics recorded");
+        hipError_t e = hipDeviceSynchronize();
+        if (e != hipSuccess) return fail_hip(e, "hipDeviceSynchronize");
+        unsigned long long v[3] = {0, 0, 0};
+        e = hipMemcpy(v, static_cast<unsigned*>(it->second.last_counters) + 2, sizeof(v), hipMemcpyDeviceToHost);
+        if (e != hipSuccess) return fail_hip(e, "hipMemcpy(stats)");
+        if (wait_cycles) *wait_cycles = v[0];
+        if (item_cycles) *item_cycles = v[1];
+        if (polls) *polls = v[2];
+        return ATTN_OK;
+    });
 }

@@ -2,9 +2,21 @@
 #pragma once
 
 #include <cstddef>
+#include <new>
 #include <vector>
 
 namespace attn {
+
+// Largest number of tiles per sequence the host side accepts: a head's task
+// table holds n^2 records of 16 bytes (64 MiB at n = 2048, twice that during
+// its construction), and every 32-bit offset of the kernels (per-head buffer
+// resources over s rows of d elements, accumulator offsets) stays far inside
+// its range.
+constexpr int kMaxTiles = 2048;
+// Largest problem the DAG simulator accepts: heads times tasks per head, and
+// the number of workers (both bound its memory and run time).
+constexpr long long kMaxSimTasks = 1LL << 27;
+constexpr int kMaxWorkers = 1 << 20;
 
 // One head's schedule pattern (see attn_sched_get in attn_bwd.h).
 struct Schedule {
@@ -25,6 +37,23 @@ int simulate(const Schedule& sc, int heads, int workers, int placement, double c
 
 // Records `msg` as the calling thread's last error and returns `code`.
 int fail(int code, const char* msg);
+// fail(ATTN_ERR_INTERNAL, msg) that never throws (used while handling an
+// exception, when even the message may not fit in memory).
+int fail_internal(const char* msg) noexcept;
+
+// Runs f() (returning a status) and turns any C++ exception into a status
+// code, so that none crosses the C ABI: host memory exhaustion and other
+// host-side failures become ATTN_ERR_INTERNAL.
+template <class F>
+int guarded(F&& f) noexcept {
+    try {
+        return f();
+    } catch (const std::bad_alloc&) {
+        return fail_internal("host memory exhausted");
+    } catch (...) {
+        return fail_internal("unexpected host-side error");
+    }
+}
 
 // Parameters of one backward launch (device pointers).
 struct BwdArgs {

@@ -33,6 +33,7 @@ static bool visible(bool causal, int kv, int q) { return !causal || kv <= q; }
 
 int build_schedule(int n, bool causal, int schedule, Schedule& out) {
     if (n < 0) return ATTN_ERR_INVALID_ARG;
+    if (n > kMaxTiles) return ATTN_ERR_UNSUPPORTED;
     if (schedule < ATTN_SCHED_NAIVE || schedule > ATTN_SCHED_ATOMIC) return ATTN_ERR_INVALID_ARG;
     int kind = schedule;
     if (kind == ATTN_SCHED_SYMMETRIC_SHIFT && !causal) kind = ATTN_SCHED_SHIFT;  // empty fold
@@ -188,6 +189,8 @@ int simulate(const Schedule& sc, int heads, int workers, int placement, double c
              double* makespan, double* wait_time, double* busy_time) {
     if (heads < 0 || workers <= 0 || c < 0 || r < 0 || e < 0 || placement < 0 || placement > 2)
         return ATTN_ERR_INVALID_ARG;
+    if (workers > kMaxWorkers || (long long)heads * (long long)sc.task_kv.size() > kMaxSimTasks)
+        return ATTN_ERR_UNSUPPORTED;
     const int n = sc.n, items_per_head = sc.num_items();
     const long long total_items = (long long)heads * items_per_head;
     const bool ordered = sc.schedule != ATTN_SCHED_ATOMIC;
@@ -337,51 +340,61 @@ int simulate(const Schedule& sc, int heads, int workers, int placement, double c
 }  // namespace attn
 
 extern "C" int attn_sched_size(int n, int causal, int schedule, int* num_items, int* num_tasks) {
-    attn::Schedule sc;
-    int rc = attn::build_schedule(n, causal != 0, schedule, sc);
-    if (rc != ATTN_OK) return attn::fail(rc, "attn_sched_size: invalid or unsupported schedule");
-    if (num_items) *num_items = sc.num_items();
-    if (num_tasks) *num_tasks = (int)sc.task_kv.size();
-    return ATTN_OK;
+    return attn::guarded([&]() -> int {
+        attn::Schedule sc;
+        int rc = attn::build_schedule(n, causal != 0, schedule, sc);
+        if (rc != ATTN_OK) return attn::fail(rc, "attn_sched_size: invalid or unsupported schedule (n < 0, n > 2048, or an odd n for the causal fold)");
+        if (num_items) *num_items = sc.num_items();
+        if (num_tasks) *num_tasks = (int)sc.task_kv.size();
+        return ATTN_OK;
+    });
 }
 
 extern "C" int attn_sched_get(int n, int causal, int schedule, int* item_begin, int* task_kv,
                               int* task_q, int* rank, int* count) {
-    attn::Schedule sc;
-    int rc = attn::build_schedule(n, causal != 0, schedule, sc);
-    if (rc != ATTN_OK) return attn::fail(rc, "attn_sched_get: invalid or unsupported schedule");
-    if (item_begin) std::memcpy(item_begin, sc.item_begin.data(), sc.item_begin.size() * sizeof(int));
-    if (task_kv) std::memcpy(task_kv, sc.task_kv.data(), sc.task_kv.size() * sizeof(int));
-    if (task_q) std::memcpy(task_q, sc.task_q.data(), sc.task_q.size() * sizeof(int));
-    if (rank) std::memcpy(rank, sc.rank.data(), sc.rank.size() * sizeof(int));
-    if (count) std::memcpy(count, sc.count.data(), sc.count.size() * sizeof(int));
-    return ATTN_OK;
+    return attn::guarded([&]() -> int {
+        attn::Schedule sc;
+        int rc = attn::build_schedule(n, causal != 0, schedule, sc);
+        if (rc != ATTN_OK) return attn::fail(rc, "attn_sched_get: invalid or unsupported schedule (n < 0, n > 2048, or an odd n for the causal fold)");
+        if (item_begin) std::memcpy(item_begin, sc.item_begin.data(), sc.item_begin.size() * sizeof(int));
+        if (task_kv) std::memcpy(task_kv, sc.task_kv.data(), sc.task_kv.size() * sizeof(int));
+        if (task_q) std::memcpy(task_q, sc.task_q.data(), sc.task_q.size() * sizeof(int));
+        if (rank) std::memcpy(rank, sc.rank.data(), sc.rank.size() * sizeof(int));
+        if (count) std::memcpy(count, sc.count.data(), sc.count.size() * sizeof(int));
+        return ATTN_OK;
+    });
 }
 
 extern "C" int attn_sched_min_workers(int n, int causal, int schedule) {
-    attn::Schedule sc;
-    int rc = attn::build_schedule(n, causal != 0, schedule, sc);
-    if (rc != ATTN_OK) return attn::fail(rc, "attn_sched_min_workers: invalid or unsupported schedule");
-    return attn::min_workers(sc);
+    return attn::guarded([&]() -> int {
+        attn::Schedule sc;
+        int rc = attn::build_schedule(n, causal != 0, schedule, sc);
+        if (rc != ATTN_OK) return attn::fail(rc, "attn_sched_min_workers: invalid or unsupported schedule (n < 0, n > 2048, or an odd n for the causal fold)");
+        return attn::min_workers(sc);
+    });
 }
 
 extern "C" int attn_dagsim(int n, int causal, int schedule, int heads, int workers, int placement,
                            double c, double r, double* makespan, double* wait_time,
                            double* busy_time) {
-    return attn_dagsim_edge(n, causal, schedule, heads, workers, placement, c, r, 0.0, makespan, wait_time,
-                            busy_time);
+    return attn::guarded([&]() -> int {
+        return attn_dagsim_edge(n, causal, schedule, heads, workers, placement, c, r, 0.0, makespan, wait_time,
+                                busy_time);
+    });
 }
 
 extern "C" int attn_dagsim_edge(int n, int causal, int schedule, int heads, int workers, int placement,
                                 double c, double r, double e, double* makespan, double* wait_time,
                                 double* busy_time) {
-    attn::Schedule sc;
-    int rc = attn::build_schedule(n, causal != 0, schedule, sc);
-    if (rc != ATTN_OK) return attn::fail(rc, "attn_dagsim: invalid or unsupported schedule");
-    rc = attn::simulate(sc, heads, workers, placement, c, r, e, makespan, wait_time, busy_time);
-    if (rc == ATTN_ERR_DEADLOCK) return attn::fail(rc, "attn_dagsim: the schedule deadlocks with this many workers");
-    if (rc != ATTN_OK) return attn::fail(rc, "attn_dagsim: invalid arguments");
-    return ATTN_OK;
+    return attn::guarded([&]() -> int {
+        attn::Schedule sc;
+        int rc = attn::build_schedule(n, causal != 0, schedule, sc);
+        if (rc != ATTN_OK) return attn::fail(rc, "attn_dagsim: invalid or unsupported schedule (n < 0, n > 2048, or an odd n for the causal fold)");
+        rc = attn::simulate(sc, heads, workers, placement, c, r, e, makespan, wait_time, busy_time);
+        if (rc == ATTN_ERR_DEADLOCK) return attn::fail(rc, "attn_dagsim: the schedule deadlocks with this many workers");
+        if (rc != ATTN_OK) return attn::fail(rc, "attn_dagsim: invalid arguments, or more heads * tasks or workers than the simulator accepts");
+        return ATTN_OK;
+    });
 }
 
 // ---------------------------------------------------------------------------
@@ -389,26 +402,28 @@ extern "C" int attn_dagsim_edge(int n, int causal, int schedule, int heads, int 
 // ---------------------------------------------------------------------------
 extern "C" int attn_sched_select(int n, int causal, int heads, int workers, int placement, double c, double r,
                                  double e, int* schedule, double* makespan) {
-    if (n <= 0 || heads <= 0 || workers <= 0 || placement < 0 || placement > 2 || !(c >= 0) || !(r >= 0) ||
-        !(e >= 0))
-        return attn::fail(ATTN_ERR_INVALID_ARG, "attn_sched_select: invalid arguments");
-    int best = -1;
-    double best_t = 0;
-    for (int s : {ATTN_SCHED_NAIVE, ATTN_SCHED_DESCENDING, ATTN_SCHED_SHIFT, ATTN_SCHED_SYMMETRIC_SHIFT}) {
-        attn::Schedule sc;
-        if (attn::build_schedule(n, causal != 0, s, sc) != ATTN_OK) continue;  // e.g. odd n, fold
-        if (attn::min_workers(sc) > workers) continue;                          // cannot be co-scheduled
-        double t = 0;
-        if (attn::simulate(sc, heads, workers, placement, c, r, e, &t, nullptr, nullptr) != ATTN_OK) continue;
-        if (best < 0 || t < best_t * (1 - 1e-12)) {
-            best = s;
-            best_t = t;
+    return attn::guarded([&]() -> int {
+        if (n <= 0 || heads <= 0 || workers <= 0 || placement < 0 || placement > 2 || !(c >= 0) || !(r >= 0) ||
+            !(e >= 0))
+            return attn::fail(ATTN_ERR_INVALID_ARG, "attn_sched_select: invalid arguments");
+        int best = -1;
+        double best_t = 0;
+        for (int s : {ATTN_SCHED_NAIVE, ATTN_SCHED_DESCENDING, ATTN_SCHED_SHIFT, ATTN_SCHED_SYMMETRIC_SHIFT}) {
+            attn::Schedule sc;
+            if (attn::build_schedule(n, causal != 0, s, sc) != ATTN_OK) continue;  // e.g. odd n, fold
+            if (attn::min_workers(sc) > workers) continue;                          // cannot be co-scheduled
+            double t = 0;
+            if (attn::simulate(sc, heads, workers, placement, c, r, e, &t, nullptr, nullptr) != ATTN_OK) continue;
+            if (best < 0 || t < best_t * (1 - 1e-12)) {
+                best = s;
+                best_t = t;
+            }
         }
-    }
-    if (best < 0) return attn::fail(ATTN_ERR_UNSUPPORTED, "attn_sched_select: no schedule runs on this many workers");
-    if (schedule) *schedule = best;
-    if (makespan) *makespan = best_t;
-    return ATTN_OK;
+        if (best < 0) return attn::fail(ATTN_ERR_UNSUPPORTED, "attn_sched_select: no schedule runs on this many workers");
+        if (schedule) *schedule = best;
+        if (makespan) *makespan = best_t;
+        return ATTN_OK;
+    });
 }
 
 namespace {
@@ -446,49 +461,51 @@ double fit_error(const FitData& f, double rho, double eps, double* c_out) {
 extern "C" int attn_sched_fit(int count, const int* n, const int* causal, const int* schedule, const int* heads,
                               const int* workers, int placement, const double* measured, double* c, double* r,
                               double* e, double* rms) {
-    if (count <= 0 || !n || !causal || !schedule || !heads || !workers || !measured || placement < 0 ||
-        placement > 2)
-        return attn::fail(ATTN_ERR_INVALID_ARG, "attn_sched_fit: invalid arguments");
-    for (int k = 0; k < count; ++k)
-        if (!(measured[k] > 0) || n[k] <= 0 || heads[k] <= 0 || workers[k] <= 0)
-            return attn::fail(ATTN_ERR_INVALID_ARG, "attn_sched_fit: invalid sample");
-    const FitData f{count, placement, n, causal, schedule, heads, workers, measured};
-    // search in u = log(r/c) in [log 1e-4, log 1e2] and v = log(e/c) in
-    // [log 1e-4, log 1e2], with v at its lower end standing for e = 0
-    const double ulo = std::log(1e-4), uhi = std::log(1e2), vlo = std::log(1e-4), vhi = std::log(1e2);
-    auto eval = [&](double u, double v) {
-        return fit_error(f, std::exp(u), v <= vlo ? 0.0 : std::exp(v), nullptr);
-    };
-    // 1. r/c alone on a grid (e = 0)
-    double bu = ulo, bv = vlo, be = -1;
-    for (int i = 0; i <= 30; ++i) {
-        const double u = ulo + (uhi - ulo) * i / 30, er = eval(u, vlo);
-        if (er < 0) return attn::fail(ATTN_ERR_UNSUPPORTED, "attn_sched_fit: a sample cannot be simulated");
-        if (be < 0 || er < be) { be = er; bu = u; }
-    }
-    // 2. e/c on a grid at that r/c
-    for (int j = 1; j <= 15; ++j) {
-        const double v = vlo + (vhi - vlo) * j / 15, er = eval(bu, v);
-        if (er < be) { be = er; bv = v; }
-    }
-    // 3. pattern search in (u, v), halving the step when no neighbour helps
-    double step = (uhi - ulo) / 30;
-    while (step > 1e-4) {
-        bool moved = false;
-        const double du[4] = {step, -step, 0, 0}, dv[4] = {0, 0, step, -step};
-        for (int d = 0; d < 4; ++d) {
-            const double u = std::min(uhi, std::max(ulo, bu + du[d]));
-            const double v = std::min(vhi, std::max(vlo, bv + dv[d]));
-            const double er = eval(u, v);
-            if (er >= 0 && er < be * (1 - 1e-12)) { be = er; bu = u; bv = v; moved = true; }
+    return attn::guarded([&]() -> int {
+        if (count <= 0 || !n || !causal || !schedule || !heads || !workers || !measured || placement < 0 ||
+            placement > 2)
+            return attn::fail(ATTN_ERR_INVALID_ARG, "attn_sched_fit: invalid arguments");
+        for (int k = 0; k < count; ++k)
+            if (!(measured[k] > 0) || n[k] <= 0 || heads[k] <= 0 || workers[k] <= 0)
+                return attn::fail(ATTN_ERR_INVALID_ARG, "attn_sched_fit: invalid sample");
+        const FitData f{count, placement, n, causal, schedule, heads, workers, measured};
+        // search in u = log(r/c) in [log 1e-4, log 1e2] and v = log(e/c) in
+        // [log 1e-4, log 1e2], with v at its lower end standing for e = 0
+        const double ulo = std::log(1e-4), uhi = std::log(1e2), vlo = std::log(1e-4), vhi = std::log(1e2);
+        auto eval = [&](double u, double v) {
+            return fit_error(f, std::exp(u), v <= vlo ? 0.0 : std::exp(v), nullptr);
+        };
+        // 1. r/c alone on a grid (e = 0)
+        double bu = ulo, bv = vlo, be = -1;
+        for (int i = 0; i <= 30; ++i) {
+            const double u = ulo + (uhi - ulo) * i / 30, er = eval(u, vlo);
+            if (er < 0) return attn::fail(ATTN_ERR_UNSUPPORTED, "attn_sched_fit: a sample cannot be simulated");
+            if (be < 0 || er < be) { be = er; bu = u; }
         }
-        if (!moved) step *= 0.5;
-    }
-    double cc = 0;
-    fit_error(f, std::exp(bu), bv <= vlo ? 0.0 : std::exp(bv), &cc);
-    if (c) *c = cc;
-    if (r) *r = cc * std::exp(bu);
-    if (e) *e = bv <= vlo ? 0.0 : cc * std::exp(bv);
-    if (rms) *rms = be;
-    return ATTN_OK;
+        // 2. e/c on a grid at that r/c
+        for (int j = 1; j <= 15; ++j) {
+            const double v = vlo + (vhi - vlo) * j / 15, er = eval(bu, v);
+            if (er < be) { be = er; bv = v; }
+        }
+        // 3. pattern search in (u, v), halving the step when no neighbour helps
+        double step = (uhi - ulo) / 30;
+        while (step > 1e-4) {
+            bool moved = false;
+            const double du[4] = {step, -step, 0, 0}, dv[4] = {0, 0, step, -step};
+            for (int d = 0; d < 4; ++d) {
+                const double u = std::min(uhi, std::max(ulo, bu + du[d]));
+                const double v = std::min(vhi, std::max(vlo, bv + dv[d]));
+                const double er = eval(u, v);
+                if (er >= 0 && er < be * (1 - 1e-12)) { be = er; bu = u; bv = v; moved = true; }
+            }
+            if (!moved) step *= 0.5;
+        }
+        double cc = 0;
+        fit_error(f, std::exp(bu), bv <= vlo ? 0.0 : std::exp(bv), &cc);
+        if (c) *c = cc;
+        if (r) *r = cc * std::exp(bu);
+        if (e) *e = bv <= vlo ? 0.0 : cc * std::exp(bv);
+        if (rms) *rms = be;
+        return ATTN_OK;
+    });
 }
