@@ -55,13 +55,24 @@ extern "C" {
  * Scheduling with two-phase workload folding for the causal mask (Fig. 7;
  * equals SHIFT under the full mask; needs an even tile count when causal).
  * ATOMIC is the non-deterministic comparison point: unordered fp32 atomic
- * dQ additions (Problem section: the non-deterministic counterpart). */
+ * dQ additions (Problem section: the non-deterministic counterpart).  AUTO
+ * picks one of the four deterministic schedules per configuration (review
+ * page, "If this is right": the schedules are complementary and an
+ * implementation selects one per configuration): the DAG model with task
+ * costs fitted on MI355X simulates each schedule the shape admits under the
+ * kernel's XCD placement and the shortest makespan wins, except that under
+ * the causal mask at head dimension 128 Descending replaces Symmetric Shift
+ * (measured faster; the summary page's Surprising findings report the same
+ * at headdim 128).  attn_bwd_resolve_schedule tells which one a call gets;
+ * the choice is deterministic for a shape, so AUTO is as reproducible as
+ * the schedule it resolves to. */
 typedef enum {
     ATTN_SCHED_NAIVE = 0,
     ATTN_SCHED_DESCENDING = 1,
     ATTN_SCHED_SHIFT = 2,
     ATTN_SCHED_SYMMETRIC_SHIFT = 3,
-    ATTN_SCHED_ATOMIC = 4
+    ATTN_SCHED_ATOMIC = 4,
+    ATTN_SCHED_AUTO = 5
 } attn_schedule_t;
 
 typedef enum { ATTN_BF16 = 0, ATTN_FP32 = 1 } attn_dtype_t;
@@ -127,6 +138,13 @@ int attn_bwd_deterministic_ex(const void* q, const void* k, const void* v, const
  * for invalid sizes. */
 size_t attn_bwd_workspace_bytes(int b, int h, int s, int d, int causal, int schedule);
 
+/* The deterministic schedule ATTN_SCHED_AUTO resolves to for these sizes,
+ * mask and element type on the current device (an attn_schedule_t >= 0), or
+ * a negative status (ATTN_ERR_INVALID_ARG, ATTN_ERR_UNSUPPORTED,
+ * ATTN_ERR_COSCHEDULE, ATTN_ERR_HIP).  Initialises the device state on
+ * first use; launches nothing. */
+int attn_bwd_resolve_schedule(int b, int h, int s, int d, int causal, int dtype);
+
 /* Synchronises `stream` (hipStream_t or NULL), then reports and clears the
  * device status word: ATTN_OK, or ATTN_ERR_TIMEOUT if a bounded flag wait
  * expired in any call since the last query (results of that call are
@@ -169,6 +187,14 @@ int attn_bwd_get_kernel_times(float* ms_preprocess, float* ms_main, float* ms_fi
 typedef enum { ATTN_PLACE_GLOBAL = 0, ATTN_PLACE_XCD = 1 } attn_placement_t;
 int attn_bwd_set_placement(int mode);
 
+/* Per-call times of the recording started by attn_bwd_set_timing(1): for
+ * the first min(calls recorded, max_calls) calls, ms_total[i] (preprocess to
+ * the end of the last kernel) and ms_main[i] (main kernel), either array may
+ * be NULL; *calls receives the count written.  Waits for the recorded
+ * events.  Returns ATTN_OK, ATTN_ERR_INVALID_ARG (nothing recorded,
+ * max_calls < 0) or ATTN_ERR_HIP. */
+int attn_bwd_get_call_times(float* ms_total, float* ms_main, int max_calls, int* calls);
+
 /* Flag-wait instrumentation.  When enabled, the main kernel of later calls
  * accumulates, per launch, the clock cycles its work groups spent inside
  * dQ flag waits, the cycles spent in whole work items, and the number of
@@ -177,6 +203,27 @@ int attn_bwd_set_placement(int mode);
 int attn_bwd_set_wait_stats(int on);
 int attn_bwd_get_wait_stats(unsigned long long* wait_cycles, unsigned long long* item_cycles,
                             unsigned long long* polls);
+
+/* The shader clock the main kernel of the last call with wait statistics
+ * ran at, in MHz: each work group's span on the shader clock counter
+ * (s_memtime) divided by its span on the constant-rate clock
+ * (s_memrealtime, hipDeviceAttributeWallClockRate), summed over work
+ * groups.  Returns ATTN_OK, ATTN_ERR_INVALID_ARG (no such call) or
+ * ATTN_ERR_HIP. */
+int attn_bwd_get_clock(double* mhz);
+
+/* Test hooks for the failure and race paths (they change timing, never the
+ * reduction order).  spin_limit: polls before a dQ flag wait gives up
+ * (0: the default of 2^20).  wait_offset (0..65535, normally 0): added to
+ * the flag value every wait looks for, so that with wait_offset > 0 no wait
+ * is ever satisfied and every call reports ATTN_ERR_TIMEOUT through
+ * attn_bwd_query_status once its bounded waits expire (results invalid; the
+ * kernel still ends).  delay_seed (0: off): before each reduction phase a
+ * work group sleeps a pseudo-random 0..8k cycles drawn from the seed, the
+ * work item and the task, so that hand-offs happen at other times and in
+ * other relative orders; results must stay bitwise the same.  Apply to
+ * later calls.  Returns ATTN_OK or ATTN_ERR_INVALID_ARG. */
+int attn_bwd_set_debug(unsigned spin_limit, int wait_offset, unsigned delay_seed);
 
 /* ------------------------------------------------------------------------
  * Attention forward (device).  Not on the pages, which take O and lse as

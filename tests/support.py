@@ -94,3 +94,12 @@ def to_np_heads(t, heads):
 
 
 TOL = {"bf16": 2e-2, "fp32": 1e-4}
+
+# Measured parity errors of this test session, (case, tensor) -> error; the
+# conftest writes them to the file named by ATTN_PARITY_RECORD, if set.
+# A measurement record only: no test reads it back as an expected value.
+ERRORS = {}
+
+
+def record_error(case, tensor, err, tol):
+    ERRORS[f"{case} | {tensor}"] = {"rel_err": float(err), "tol": None if tol is None else float(tol)}

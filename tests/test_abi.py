@@ -55,7 +55,8 @@ def test_argument_errors_need_no_gpu():
     assert _call(b=-1) == -1
     assert _call(s=-5) == -1
     assert _call(causal=2) == -1
-    assert _call(schedule=5) == -1
+    assert _call(schedule=6) == -1
+    assert "schedule" in tsa.last_error()
     assert _call(dtype=3) == -1
     assert _call(scale=float("nan")) == -1
     assert _call(d=96) == -2
@@ -210,3 +211,21 @@ def test_forward_rejects_bad_outputs(host_as_device, case):
         o = torch.empty_like(q, device="meta")
     with pytest.raises(ValueError):
         tsa.forward(q, k, v, False, out=(o, lse), stream=0)
+
+
+def test_debug_hooks_validate_arguments():
+    assert tsa.lib.attn_bwd_set_debug(0, -1, 0) == -1
+    assert tsa.lib.attn_bwd_set_debug(0, 70000, 0) == -1
+    assert tsa.lib.attn_bwd_set_debug(64, 0, 7) == 0
+    assert tsa.lib.attn_bwd_set_debug(0, 0, 0) == 0
+
+
+def test_auto_schedule_is_accepted_and_resolve_checks_arguments():
+    assert tsa.SCHEDULES["auto"] == 5
+    ptrs = dict(q=16, k=16, v=16, o=16, dO=16, lse=16, dq=16, dk=16, dv=16)
+    assert _call(schedule=5, d=96, **ptrs) == -2      # AUTO passes the schedule check
+    assert tsa.lib.attn_bwd_resolve_schedule(0, 1, 128, 64, 0, 0) == -1
+    assert tsa.lib.attn_bwd_resolve_schedule(1, 1, 128, 96, 0, 0) == -2
+    assert tsa.lib.attn_bwd_resolve_schedule(1, 1, 128, 64, 2, 0) == -1
+    assert tsa.attn_bwd_workspace_bytes(2, 16, 8192, 128, 0, "auto") >= \
+        tsa.attn_bwd_workspace_bytes(2, 16, 8192, 128, 0, "shift")

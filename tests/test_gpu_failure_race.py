@@ -1,0 +1,91 @@
+"""Failure and race paths of the deterministic backward, forced from the host
+through the library's test hooks (attn_bwd_set_debug); every kernel still
+runs to its end.
+
+* Race detection: bitwise determinism is the race detector.  With random
+  delays injected before every reduction phase (seeded from the host), the
+  hand-offs of the dQ reduction happen at other times and in other relative
+  orders than in an undisturbed run; a flag-protocol bug (a contributor
+  reading the accumulator before its predecessor's release) would change
+  bits.  The results must stay bitwise identical.
+* Failure detection: with a tiny poll limit and a flag value that is never
+  published, every bounded wait gives up; the call still ends, the device
+  status reports ATTN_ERR_TIMEOUT, and the next normal call is clean."""
+import sys
+
+import pytest
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+if not torch.cuda.is_available():  # pragma: no cover
+    pytest.skip("no GPU", allow_module_level=True)
+
+import tile_scheduling_attn_amd as tsa  # noqa: E402
+from support import Problem, TOL, rel_err, to_np_heads  # noqa: E402
+
+
+def _say(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+@pytest.fixture
+def debug_hooks():
+    yield tsa.attn_bwd_set_debug
+    tsa.attn_bwd_set_debug(0, 0, 0)
+
+
+# (b, h, s, d, causal, schedules): waits on every schedule kind, both head
+# dimensions, XCD placement with several chunks and the global queue
+RACE_CASES = [
+    (1, 8, 2048, 128, False, ("shift", "naive")),
+    (1, 8, 2048, 128, True, ("descending", "symmetric_shift", "shift")),
+    (2, 8, 1024, 64, True, ("symmetric_shift", "naive")),
+]
+
+
+@pytest.mark.parametrize("case", RACE_CASES, ids=lambda c: f"s{c[2]}-d{c[3]}-{'causal' if c[4] else 'full'}")
+def test_injected_delays_keep_results_bitwise(case, debug_hooks):
+    b, h, s, d, causal, scheds = case
+    pb = Problem(b, h, s, d, "bf16", 9090 + s + d, causal)
+    for sched in scheds:
+        debug_hooks(0, 0, 0)
+        ref = [t.clone() for t in pb.run(sched)]
+        torch.cuda.synchronize()
+        for seed in (1, 2, 0xdeadbeef):
+            _say(f"race {case[:5]} {sched} seed {seed:#x}")
+            debug_hooks(0, 0, seed)
+            for place in ("xcd", "global"):
+                tsa.attn_bwd_set_placement(place)
+                try:
+                    out = pb.run(sched)
+                    torch.cuda.synchronize()
+                finally:
+                    tsa.attn_bwd_set_placement("xcd")
+                assert tsa.attn_bwd_query_status() == 0, tsa.last_error()
+                for a, b_ in zip(ref, out):
+                    assert torch.equal(a.view(torch.int16), b_.view(torch.int16)), f"{sched} seed {seed} {place}"
+
+
+@pytest.mark.parametrize("sched", ["naive", "shift"])
+def test_expired_waits_report_timeout_and_next_call_is_clean(sched, debug_hooks):
+    pb = Problem(1, 4, 1024, 128, "bf16", 31337, False)
+    assert tsa.attn_bwd_query_status() == 0
+    # every wait looks for a flag value nobody publishes; 64 polls each
+    debug_hooks(64, 1000, 0)
+    _say(f"timeout path {sched}")
+    pb.run(sched)
+    rc = tsa.attn_bwd_query_status()
+    assert rc == -5, (rc, tsa.last_error())
+    assert "expired" in tsa.last_error()
+    # the status word was cleared by the query; a normal call is clean and right
+    debug_hooks(0, 0, 0)
+    g = pb.run(sched)
+    torch.cuda.synchronize()
+    assert tsa.attn_bwd_query_status() == 0, tsa.last_error()
+    ref = pb.oracle([0, 3])
+    for name, t in zip(("dq", "dk", "dv"), g):
+        assert rel_err(to_np_heads(t, [0, 3]), ref[name]) <= TOL["bf16"], name
+
+

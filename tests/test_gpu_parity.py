@@ -18,7 +18,7 @@ if not torch.cuda.is_available():  # pragma: no cover
 
 import tile_scheduling_attn_amd as tsa  # noqa: E402
 import workloads  # noqa: E402
-from support import Problem, TOL, rel_err, to_np_heads  # noqa: E402
+from support import Problem, TOL, rel_err, record_error, to_np_heads  # noqa: E402
 
 DET = ("naive", "descending", "shift", "symmetric_shift")
 
@@ -39,6 +39,7 @@ def _check_parity(pb, grads, heads, tag):
     errs = {}
     for name, g in zip(("dq", "dk", "dv"), grads):
         errs[name] = rel_err(to_np_heads(g, heads), ref[name])
+        record_error(tag, name, errs[name], tol)
     _say(f"{tag}: rel errs {errs}")
     for name, e in errs.items():
         assert e <= tol, f"{tag} {name}: {e} > {tol}"
@@ -120,13 +121,13 @@ def _run_config(name, causal, schedules, heads=None, tag=""):
 
 
 def test_config_s2k_d64_causal():
-    pb, res = _run_config("s2k_d64_causal", True, ("descending", "symmetric_shift", "naive", "atomic"))
+    pb, res = _run_config("s2k_d64_causal", True, ("descending", "symmetric_shift", "naive", "atomic", "auto"))
     # NAIVE and DESCENDING share the dQ order: dQ is bitwise equal
     assert torch.equal(res["naive"][0].view(torch.int16), res["descending"][0].view(torch.int16))
 
 
 def test_config_s8k_d128_full():
-    pb, res = _run_config("s8k_d128_full", False, ("shift", "naive", "atomic"), heads="sample")
+    pb, res = _run_config("s8k_d128_full", False, ("shift", "naive", "atomic", "auto"), heads="sample")
 
 
 def test_config_s8k_d128_causal():
@@ -135,21 +136,29 @@ def test_config_s8k_d128_causal():
 
 @pytest.mark.parametrize("causal", [False, True])
 def test_config_s16k_d128(causal):
-    scheds = ("shift", "naive", "atomic") if not causal else ("descending", "symmetric_shift", "shift")
-    _run_config("s16k_d128", causal, scheds, heads="sample")
+    scheds = (("shift", "naive", "descending", "atomic") if not causal
+              else ("descending", "symmetric_shift", "shift", "naive", "atomic"))
+    pb, res = _run_config("s16k_d128", causal, scheds, heads="sample")
+    # NAIVE and DESCENDING share the dQ order: dQ is bitwise equal
+    assert torch.equal(res["naive"][0].view(torch.int16), res["descending"][0].view(torch.int16))
 
 
 # ---------------------------------------------------------------- determinism
 @pytest.mark.parametrize("name,causal,scheds", [
+    ("tiny", False, DET),
+    ("tiny", True, DET),
     ("s2k_d64_causal", True, ("descending", "symmetric_shift", "naive", "shift")),
     ("s8k_d128_full", False, ("shift", "naive")),
     ("s8k_d128_causal", True, ("symmetric_shift", "descending")),
+    ("s16k_d128", False, ("shift", "naive")),
+    ("s16k_d128", True, ("descending", "symmetric_shift")),
 ])
 def test_bitwise_determinism_20_runs(name, causal, scheds):
     wl = workloads.WORKLOADS[name]
     pb = Problem(wl.b, wl.h, wl.s, wl.d, wl.dtype, wl.seed, causal)
+    view = torch.int32 if wl.dtype == "fp32" else torch.int16
     for sched in scheds:
-        _say(f"determinism {name} {sched}")
+        _say(f"determinism {name} causal={causal} {sched}")
         ref = [t.clone() for t in pb.run(sched)]
         out = [torch.empty_like(t) for t in ref]
         for it in range(19):
@@ -158,23 +167,31 @@ def test_bitwise_determinism_20_runs(name, causal, scheds):
             pb.run(sched, out=out)
             torch.cuda.synchronize()
             for a, b_ in zip(ref, out):
-                assert torch.equal(a.view(torch.int16), b_.view(torch.int16)), f"{sched} run {it + 1}"
+                assert torch.equal(a.view(view), b_.view(view)), f"{sched} run {it + 1}"
         assert tsa.attn_bwd_query_status() == 0
 
 
-def test_atomic_run_to_run_deviation_is_reported():
-    """The non-deterministic variant may differ between runs (the pages
-    report ~2.4e-4 full / 4.9e-4 causal on their shapes); it must still meet
-    the parity bar, which the config tests check.  Here the deviation is only
-    printed."""
-    wl = workloads.WORKLOADS["s8k_d128_full"]
-    pb = Problem(wl.b, wl.h, wl.s, wl.d, wl.dtype, wl.seed, False)
-    a = pb.run("atomic")[0].float()
-    dev = 0.0
+@pytest.mark.parametrize("name,causal", [("s8k_d128_full", False), ("s8k_d128_causal", True)])
+def test_atomic_run_to_run_deviation_is_reported(name, causal):
+    """The non-deterministic variant may differ between runs (the summary
+    page's Key results give ~2.4e-4 full / 4.9e-4 causal on unstated shapes);
+    it must still meet the parity bar, which the config tests check.  Here
+    the maximum deviation of dQ, dK and dV over 5 extra runs is recorded,
+    raw and relative to max|g|; the deterministic schedules' is exactly 0
+    (the 20-run tests)."""
+    wl = workloads.WORKLOADS[name]
+    pb = Problem(wl.b, wl.h, wl.s, wl.d, wl.dtype, wl.seed, causal)
+    ref = [t.float() for t in pb.run("atomic")]
+    dev = [0.0, 0.0, 0.0]
     for _ in range(5):
-        b_ = pb.run("atomic")[0].float()
-        dev = max(dev, float((a - b_).abs().max()))
-    _say(f"atomic dQ run-to-run max deviation: {dev:.3e} (relative {dev / float(a.abs().max()):.3e})")
+        out = pb.run("atomic")
+        for i, (a, b_) in enumerate(zip(ref, out)):
+            dev[i] = max(dev[i], float((a - b_.float()).abs().max()))
+    for i, tname in enumerate(("dq", "dk", "dv")):
+        rel = dev[i] / float(ref[i].abs().max())
+        record_error(f"{name} causal={causal} atomic run-to-run max deviation (raw {dev[i]:.3e})", tname, rel, None)
+        _say(f"atomic {tname} run-to-run max deviation: {dev[i]:.3e} (relative {rel:.3e})")
+    assert dev[1] == 0.0 and dev[2] == 0.0  # dK, dV never go through the atomics
 
 
 # ---------------------------------------------------------------- misc

@@ -16,7 +16,7 @@ import numpy as np
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libattn_bwd.so")
 
-SCHEDULES = {"naive": 0, "descending": 1, "shift": 2, "symmetric_shift": 3, "atomic": 4}
+SCHEDULES = {"naive": 0, "descending": 1, "shift": 2, "symmetric_shift": 3, "atomic": 4, "auto": 5}
 DTYPES = {"bf16": 0, "fp32": 1}
 STATUS = {0: "ATTN_OK", -1: "ATTN_ERR_INVALID_ARG", -2: "ATTN_ERR_UNSUPPORTED",
           -3: "ATTN_ERR_COSCHEDULE", -4: "ATTN_ERR_HIP", -5: "ATTN_ERR_TIMEOUT",
@@ -29,7 +29,8 @@ EXPORTS = ("attn_fwd", "attn_bwd_deterministic", "attn_bwd_deterministic_ex", "a
            "attn_bwd_set_timing", "attn_bwd_get_kernel_times", "attn_bwd_set_placement", "attn_bwd_set_wait_stats",
            "attn_bwd_get_wait_stats", "attn_sched_size", "attn_sched_get",
            "attn_sched_min_workers", "attn_dagsim", "attn_dagsim_edge", "attn_sched_select",
-           "attn_sched_fit")
+           "attn_sched_fit", "attn_bwd_get_call_times", "attn_bwd_get_clock", "attn_bwd_set_debug",
+           "attn_bwd_resolve_schedule")
 
 
 class AttnError(RuntimeError):
@@ -89,6 +90,14 @@ def _load():
     lib.attn_sched_select.restype = i
     lib.attn_sched_fit.argtypes = [i, ip, ip, ip, ip, ip, i, dp, dp, dp, dp, dp]
     lib.attn_sched_fit.restype = i
+    lib.attn_bwd_get_call_times.argtypes = [fp, fp, i, ip]
+    lib.attn_bwd_get_call_times.restype = i
+    lib.attn_bwd_get_clock.argtypes = [dp]
+    lib.attn_bwd_get_clock.restype = i
+    lib.attn_bwd_set_debug.argtypes = [ctypes.c_uint, i, ctypes.c_uint]
+    lib.attn_bwd_set_debug.restype = i
+    lib.attn_bwd_resolve_schedule.argtypes = [i] * 6
+    lib.attn_bwd_resolve_schedule.restype = i
     return lib
 
 
@@ -188,6 +197,37 @@ def attn_bwd_get_wait_stats():
     _check(lib.attn_bwd_get_wait_stats(ctypes.byref(a), ctypes.byref(b_), ctypes.byref(c)),
            "attn_bwd_get_wait_stats")
     return a.value, b_.value, c.value
+
+
+def attn_bwd_get_call_times(max_calls=4096):
+    """Per-call (total ms, main-kernel ms) lists of the current timing
+    recording."""
+    tot = (ctypes.c_float * max_calls)()
+    mai = (ctypes.c_float * max_calls)()
+    n = ctypes.c_int()
+    _check(lib.attn_bwd_get_call_times(tot, mai, max_calls, ctypes.byref(n)), "attn_bwd_get_call_times")
+    return list(tot[:n.value]), list(mai[:n.value])
+
+
+def attn_bwd_resolve_schedule(b, h, s, d, causal, dtype="bf16") -> str:
+    """Name of the schedule "auto" resolves to for this shape on the current device."""
+    dt = DTYPES[dtype] if isinstance(dtype, str) else int(dtype)
+    rc = _check(lib.attn_bwd_resolve_schedule(b, h, s, d, int(causal), dt), "attn_bwd_resolve_schedule")
+    return {v: k for k, v in SCHEDULES.items()}[rc]
+
+
+def attn_bwd_get_clock() -> float:
+    """Shader clock (MHz) of the last call made with wait statistics on."""
+    mhz = ctypes.c_double()
+    _check(lib.attn_bwd_get_clock(ctypes.byref(mhz)), "attn_bwd_get_clock")
+    return mhz.value
+
+
+def attn_bwd_set_debug(spin_limit=0, wait_offset=0, delay_seed=0) -> None:
+    """Test hooks: flag-wait poll limit (0: default), an offset that makes
+    every wait unsatisfiable, and a seed for random delays before each
+    reduction phase (0: off)."""
+    _check(lib.attn_bwd_set_debug(int(spin_limit), int(wait_offset), int(delay_seed)), "attn_bwd_set_debug")
 
 
 def attn_sched_size(n, causal, schedule):

@@ -93,6 +93,8 @@ struct DevState {
     bool ws_used = false;
     unsigned* status = nullptr;
     std::map<std::tuple<int, int, int>, DevSchedule> schedules;
+    // ATTN_SCHED_AUTO: the schedule picked per (n, causal, heads, d, dtype)
+    std::map<std::tuple<int, int, long long, int, int>, int> auto_pick;
     // kernel timing: 4 events per recorded call (before preprocess, before
     // main, after main, after finalize)
     std::vector<hipEvent_t> ev_pool;
@@ -110,6 +112,10 @@ static bool g_timing = false;
 static bool g_wait_stats = false;
 static bool g_xcd_placement = true;
 static int g_last_dev = -1;
+// test hooks (attn_bwd_set_debug)
+static unsigned g_spin_limit = 0;
+static int g_wait_offset = 0;
+static unsigned g_delay_seed = 0;
 
 static int dev_init(int dev, DevState& ds) {
     if (ds.init) return ATTN_OK;
@@ -176,6 +182,64 @@ static int get_schedule(DevState& ds, int n, bool causal, int schedule, DevSched
 
 static int tile_for(int dtype) { return dtype == ATTN_FP32 ? 64 : 128; }
 
+// Task costs of the DAG model fitted to this kernel on MI355X (microseconds
+// per compute phase c and reduction phase r, and per reduction hand-off e
+// between XCDs; simulator placement 2), per head dimension.
+struct FittedCosts {
+    double c, r, e;
+};
+static FittedCosts fitted_costs(int d) {
+    if (d == 64) return {3.56, 2.26, 0.0};
+    return {3.64, 3.64, 4.41};
+}
+
+// ATTN_SCHED_AUTO.  The review page ("If this is right") has an
+// implementation select one of the complementary schedules per
+// configuration; here the DAG model with the fitted costs and the kernel's
+// XCD placement simulates every deterministic schedule the shape admits on
+// the device's resident work groups and takes the shortest makespan.  One
+// measured exception the model cannot see: under the causal mask at head
+// dimension 128 Descending Q-Tile Iteration is taken instead of Symmetric
+// Shift (the summary page's Surprising findings report the same ordering on
+// H800 and put it down to register pressure; on MI355X the folded item's
+// run switch and its [key][query] dS layout cost more than the model's
+// constant c).
+static int resolve_auto(DevState& ds, int n, bool causal, long long H, int d, int dtype, int* out) {
+    const auto key = std::make_tuple(n, (int)causal, H, d, dtype);
+    auto it = ds.auto_pick.find(key);
+    if (it != ds.auto_pick.end()) {
+        *out = it->second;
+        return ATTN_OK;
+    }
+    const FittedCosts fc = fitted_costs(d);
+    const int workers = std::max(1, ds.num_cus);
+    const int heads = (int)std::min<long long>(H, 1 << 20);
+    int pick = -1;
+    double best = 0;
+    for (int sc : {ATTN_SCHED_NAIVE, ATTN_SCHED_DESCENDING, ATTN_SCHED_SHIFT, ATTN_SCHED_SYMMETRIC_SHIFT}) {
+        Schedule sch;
+        if (build_schedule(n, causal, sc, sch) != ATTN_OK) continue;
+        if (min_workers(sch) > workers) continue;
+        // large problems: simulate a head count that keeps the simulation
+        // small but fills every worker several times (the makespan per head
+        // is what is compared)
+        const long long per_head = (long long)sch.task_kv.size();
+        int hs = heads;
+        while (hs > 8 && (long long)hs * per_head > (1LL << 22)) hs /= 2;
+        double t = 0;
+        if (simulate(sch, hs, workers, 2, fc.c, fc.r, fc.e, &t, nullptr, nullptr) != ATTN_OK) continue;
+        if (pick < 0 || t < best * (1 - 1e-9)) {
+            pick = sc;
+            best = t;
+        }
+    }
+    if (pick < 0) return fail(ATTN_ERR_COSCHEDULE, "no deterministic schedule fits the resident work groups");
+    if (pick == ATTN_SCHED_SYMMETRIC_SHIFT && causal && d == 128) pick = ATTN_SCHED_DESCENDING;
+    ds.auto_pick[key] = pick;
+    *out = pick;
+    return ATTN_OK;
+}
+
 // XCD placement of a deterministic call, planned for one resident work group
 // per CU (the main kernel's LDS allows no more; a launch with more resident
 // work groups only has more per queue)
@@ -191,7 +255,7 @@ static int backward(const void* q, const void* k, const void* v, const void* o, 
     g_last_error.clear();
     if (b < 0 || h < 0 || s < 0) return fail(ATTN_ERR_INVALID_ARG, "b, h and s must be >= 0");
     if (causal != 0 && causal != 1) return fail(ATTN_ERR_INVALID_ARG, "causal must be 0 or 1");
-    if (schedule < ATTN_SCHED_NAIVE || schedule > ATTN_SCHED_ATOMIC)
+    if (schedule < ATTN_SCHED_NAIVE || schedule > ATTN_SCHED_AUTO)
         return fail(ATTN_ERR_INVALID_ARG, "unknown schedule");
     if (dtype != ATTN_BF16 && dtype != ATTN_FP32) return fail(ATTN_ERR_INVALID_ARG, "unknown dtype");
     if (!std::isfinite(scale) || !(scale > 0))
@@ -220,6 +284,10 @@ static int backward(const void* q, const void* k, const void* v, const void* o, 
     DevState& ds = g_dev[dev];
     int rc = dev_init(dev, ds);
     if (rc != ATTN_OK) return rc;
+    if (schedule == ATTN_SCHED_AUTO) {
+        rc = resolve_auto(ds, n, causal != 0, H, d, dtype, &schedule);
+        if (rc != ATTN_OK) return rc;
+    }
     DevSchedule* sch = nullptr;
     rc = get_schedule(ds, n, causal != 0, schedule, &sch);
     if (rc != ATTN_OK) return rc;
@@ -304,6 +372,9 @@ static int backward(const void* q, const void* k, const void* v, const void* o, 
     // flags and counters are contiguous: one clear covers both
     L.nclear32 = (int)((wl.total - wl.flags) / sizeof(unsigned));
     if (use_xcd) L.plan = plan;
+    L.spin_limit = g_spin_limit;
+    L.wait_offset = g_wait_offset;
+    L.delay_seed = g_delay_seed;
 
     rc = launch_backward(a, L);
     if (rc != ATTN_OK) return rc;
@@ -385,21 +456,24 @@ extern "C" size_t attn_bwd_workspace_bytes(int b, int h, int s, int d, int causa
         size_t total = wl.total;
         // what XCD placement needs on the current device (either tile edge)
         if (H > 0 && s > 0 && (causal == 0 || causal == 1) && schedule >= ATTN_SCHED_NAIVE &&
-            schedule < ATTN_SCHED_ATOMIC) {
+            schedule <= ATTN_SCHED_AUTO && schedule != ATTN_SCHED_ATOMIC) {
             std::lock_guard<std::mutex> lock(g_mutex);
             int dev = 0;
             if (hipGetDevice(&dev) == hipSuccess) {
                 DevState& ds = g_dev[dev];
                 if (dev_init(dev, ds) == ATTN_OK) {
-                    for (int tile : {64, 128}) {
+                    for (int tile : {64, 128})
+                    for (int sched = ATTN_SCHED_NAIVE; sched < ATTN_SCHED_ATOMIC; ++sched) {
+                        // AUTO may resolve to any deterministic schedule
+                        if (schedule != ATTN_SCHED_AUTO && sched != schedule) continue;
                         const int n = (s + tile - 1) / tile;
                         Schedule sc;
-                        if (build_schedule(n, causal != 0, schedule, sc) != ATTN_OK) continue;
+                        if (build_schedule(n, causal != 0, sched, sc) != ATTN_OK) continue;
                         DevSchedule shape;
                         shape.items = sc.num_items();
                         shape.item_begin = sc.item_begin;
                         shape.min_workers = min_workers(sc);
-                        const XcdPlan plan = placement_plan(ds, shape, schedule, H);
+                        const XcdPlan plan = placement_plan(ds, shape, sched, H);
                         WsLayout w2;
                         if (plan.chunks && ws_layout(H, s, d, kQueues * plan.slots, w2)) total = std::max(total, w2.total);
                     }
@@ -412,6 +486,28 @@ extern "C" size_t attn_bwd_workspace_bytes(int b, int h, int s, int d, int causa
         fail_internal("host memory exhausted or unexpected host-side error");
         return 0;
     }
+}
+
+extern "C" int attn_bwd_resolve_schedule(int b, int h, int s, int d, int causal, int dtype) {
+    return guarded([&]() -> int {
+        if (b <= 0 || h <= 0 || s <= 0 || s > kMaxSeq || (causal != 0 && causal != 1))
+            return fail(ATTN_ERR_INVALID_ARG, "invalid sizes or mask");
+        if (dtype != ATTN_BF16 && dtype != ATTN_FP32) return fail(ATTN_ERR_INVALID_ARG, "unknown dtype");
+        if (d != 64 && d != 128) return fail(ATTN_ERR_UNSUPPORTED, "head dimension must be 64 or 128");
+        const long long H = (long long)b * h;
+        if (H > kMaxHeads) return fail(ATTN_ERR_INVALID_ARG, "problem too large");
+        std::lock_guard<std::mutex> lock(g_mutex);
+        int dev = 0;
+        hipError_t e = hipGetDevice(&dev);
+        if (e != hipSuccess) return fail_hip(e, "hipGetDevice");
+        DevState& ds = g_dev[dev];
+        int rc = dev_init(dev, ds);
+        if (rc != ATTN_OK) return rc;
+        const int tile = tile_for(dtype);
+        int pick = -1;
+        rc = resolve_auto(ds, (s + tile - 1) / tile, causal != 0, H, d, dtype, &pick);
+        return rc != ATTN_OK ? rc : pick;
+    });
 }
 
 extern "C" int attn_bwd_query_status(void* stream) {
@@ -485,6 +581,68 @@ extern "C" int attn_bwd_get_kernel_times(float* ms_pre, float* ms_main, float* m
         if (ms_pre) *ms_pre = (float)(sum[0] / calls);
         if (ms_main) *ms_main = (float)(sum[1] / calls);
         if (ms_fin) *ms_fin = (float)(sum[2] / calls);
+        return ATTN_OK;
+    });
+}
+
+extern "C" int attn_bwd_get_call_times(float* ms_total, float* ms_main, int max_calls, int* calls) {
+    return guarded([&]() -> int {
+        std::lock_guard<std::mutex> lock(g_mutex);
+        if (calls) *calls = 0;
+        if (max_calls < 0) return fail(ATTN_ERR_INVALID_ARG, "max_calls must be >= 0");
+        auto it = g_dev.find(g_last_dev);
+        if (it == g_dev.end() || it->second.ev_used == 0) return fail(ATTN_ERR_INVALID_ARG, "no timed call recorded");
+        DevState& ds = it->second;
+        const int n = (int)std::min<size_t>(ds.ev_used, (size_t)max_calls);
+        hipError_t e = hipEventSynchronize(ds.ev_pool[4 * ds.ev_used - 1]);
+        if (e != hipSuccess) return fail_hip(e, "hipEventSynchronize");
+        for (int c = 0; c < n; ++c) {
+            hipEvent_t* ev = &ds.ev_pool[4 * (size_t)c];
+            float t = 0.f;
+            if (ms_total) {
+                e = hipEventElapsedTime(&t, ev[0], ev[3]);
+                if (e != hipSuccess) return fail_hip(e, "hipEventElapsedTime");
+                ms_total[c] = t;
+            }
+            if (ms_main) {
+                e = hipEventElapsedTime(&t, ev[1], ev[2]);
+                if (e != hipSuccess) return fail_hip(e, "hipEventElapsedTime");
+                ms_main[c] = t;
+            }
+        }
+        if (calls) *calls = n;
+        return ATTN_OK;
+    });
+}
+
+extern "C" int attn_bwd_set_debug(unsigned spin_limit, int wait_offset, unsigned delay_seed) {
+    return guarded([&]() -> int {
+        if (wait_offset < 0 || wait_offset > 0xffff) return fail(ATTN_ERR_INVALID_ARG, "wait_offset must be in [0, 65535]");
+        std::lock_guard<std::mutex> lock(g_mutex);
+        g_spin_limit = spin_limit;
+        g_wait_offset = wait_offset;
+        g_delay_seed = delay_seed;
+        return ATTN_OK;
+    });
+}
+
+extern "C" int attn_bwd_get_clock(double* mhz) {
+    return guarded([&]() -> int {
+        std::lock_guard<std::mutex> lock(g_mutex);
+        if (mhz) *mhz = 0;
+        auto it = g_dev.find(g_last_dev);
+        if (it == g_dev.end() || !it->second.stats_valid || !it->second.last_counters)
+            return fail(ATTN_ERR_INVALID_ARG, "no call with wait statistics recorded");
+        hipError_t e = hipDeviceSynchronize();
+        if (e != hipSuccess) return fail_hip(e, "hipDeviceSynchronize");
+        unsigned long long v[5] = {0, 0, 0, 0, 0};
+        e = hipMemcpy(v, static_cast<unsigned*>(it->second.last_counters) + 2, sizeof(v), hipMemcpyDeviceToHost);
+        if (e != hipSuccess) return fail_hip(e, "hipMemcpy(stats)");
+        int wall_khz = 0;
+        e = hipDeviceGetAttribute(&wall_khz, hipDeviceAttributeWallClockRate, g_last_dev);
+        if (e != hipSuccess) return fail_hip(e, "hipDeviceGetAttribute(wall clock rate)");
+        if (v[4] == 0 || wall_khz <= 0) return fail(ATTN_ERR_INVALID_ARG, "no clock span recorded");
+        if (mhz) *mhz = (double)v[3] / (double)v[4] * wall_khz / 1e3;
         return ATTN_OK;
     });
 }

@@ -51,12 +51,28 @@
 
 namespace attn {
 
-// A flag wait gives up after this many polls (each poll sleeps ~64 cycles
-// plus a memory round trip, so well under a second in all), sets the
-// call's abort word and the device status word, and continues; once the
-// abort word is set every later wait of the call is skipped, so a broken
-// schedule ends the kernel quickly instead of hanging the device.
+// A flag wait gives up after a bounded number of polls (by default 2^20;
+// each poll sleeps ~64 cycles plus a memory round trip, so well under a
+// second in all), sets the call's abort word and the device status word,
+// and continues; once the abort word is set every later wait of the call is
+// skipped, so a broken schedule ends the kernel quickly instead of hanging
+// the device.
 constexpr unsigned kSpinLimit = 1u << 20;
+
+// Test hooks (attn_bwd_set_debug).  delay_seed != 0: before every R phase
+// thread 0 sleeps a pseudo-random 0..31 x 256 cycles drawn from a hash of
+// the seed, the work item and the task, so that hand-offs happen in other
+// relative orders and at other times than in an undisturbed run; the
+// results must not change.  wait_offset != 0: every wait looks for a flag
+// value that is never published, so that the bounded wait expires.
+__device__ inline unsigned mix32(unsigned x) {
+    x ^= x >> 16;
+    x *= 0x7feb352dU;
+    x ^= x >> 15;
+    x *= 0x846ca68bU;
+    x ^= x >> 16;
+    return x;
+}
 
 // XCD placement.  A work group takes its items from the queue of the XCD it
 // runs on (HW_REG_XCC_ID), so a head's items run on one or a few XCDs and
@@ -100,6 +116,9 @@ struct KParams {
     long long acc_slots;  // heads of one XCD's accumulator copy
     long long total_items;
     float scale, scale_log2;
+    unsigned spin_limit;   // polls before a flag wait gives up
+    int wait_offset;       // test hook: added to the awaited flag value
+    unsigned delay_seed;   // test hook: pseudo-random sleep before each R phase
 };
 
 // LDS of one work group:
@@ -191,6 +210,10 @@ void bwd_main_kernel(KParams p) {
     if (DET && p.chunks && xcc >= (unsigned)kQueues && tid == 0) atomicOr(p.status, 2u);
 
     unsigned long long wait_cycles = 0, polls = 0, item_cycles = 0;
+    // shader clock (s_memtime) and constant 100 MHz clock (s_memrealtime) at
+    // the start: their spans give the clock the kernel actually ran at
+    const unsigned long long clk0 = p.stats ? __builtin_readcyclecounter() : 0;
+    const unsigned long long rt0 = p.stats ? __builtin_amdgcn_s_memrealtime() : 0;
 
     // dQ^T (deterministic) or dQ (atomic) of the task's whole Q tile, as
     // NSUB parts of BQ query rows, for this wave's DW columns, contracted
@@ -828,15 +851,20 @@ void bwd_main_kernel(KParams p) {
                 // ---- R phase.  One barrier ends the last sub-step (all of dS is in
                 // LDS) and, for rank > 0, the wait for this tile's turn: thread 0
                 // waits for the flag before arriving.
+                if (p.delay_seed && tid == 0) {
+                    const unsigned nap = mix32(p.delay_seed ^ mix32((unsigned)item * 0x9e3779b9u + (unsigned)t)) & 31u;
+                    for (unsigned z = 0; z < nap; ++z) __builtin_amdgcn_s_sleep(4);
+                }
                 if (DET && rank > 0 && tid == 0) {
                     const unsigned long long t0 = p.stats ? __builtin_readcyclecounter() : 0;
                     unsigned spins = 0;
                     unsigned seen = early;
-                    while ((seen & kRankMask) != (unsigned)rank) {
+                    const unsigned want = (unsigned)(rank + p.wait_offset) & kRankMask;
+                    while ((seen & kRankMask) != want) {
                         if ((spins & 1023u) == 0 && __hip_atomic_load(p.abort, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT))
                             break;
                         __builtin_amdgcn_s_sleep(1);
-                        if (++spins >= kSpinLimit) {
+                        if (++spins >= p.spin_limit) {
                             atomicOr(p.abort, 1u);
                             atomicOr(p.status, 1u);
                             break;
@@ -991,6 +1019,8 @@ void bwd_main_kernel(KParams p) {
         atomicAdd(p.stats + 0, wait_cycles);
         atomicAdd(p.stats + 1, item_cycles);
         atomicAdd(p.stats + 2, polls);
+        atomicAdd(p.stats + 3, __builtin_readcyclecounter() - clk0);
+        atomicAdd(p.stats + 4, __builtin_amdgcn_s_memrealtime() - rt0);
     }
 }
 
@@ -1201,6 +1231,9 @@ int launch_backward(const BwdArgs& a, const BwdLaunch& L) {
     kp.total_items = (long long)a.H * L.items_per_head;
     kp.scale = a.scale;
     kp.scale_log2 = a.scale * kLog2e;
+    kp.spin_limit = L.spin_limit ? L.spin_limit : kSpinLimit;
+    kp.wait_offset = L.wait_offset;
+    kp.delay_seed = L.delay_seed;
     if (a.dtype == ATTN_BF16) return launch_all<bf16, 128>(a, L, kp);
     return launch_all<float, 64>(a, L, kp);
 }

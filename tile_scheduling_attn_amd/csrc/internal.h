@@ -108,6 +108,9 @@ struct BwdLaunch {
     int items_per_head;
     int nclear32;                 // flags + counters words to clear
     XcdPlan plan;                 // XCD placement (chunks == 0: one global queue)
+    unsigned spin_limit = 0;      // test hooks (attn_bwd_set_debug); 0: default
+    int wait_offset = 0;
+    unsigned delay_seed = 0;
 };
 
 // first counter word of the per-XCD work queues
