@@ -128,6 +128,31 @@ int attn_bwd_deterministic_ex(const void* q, const void* k, const void* v, const
                               int dtype, float scale, void* workspace, size_t workspace_bytes,
                               void* stream);
 
+/* attn_bwd_deterministic_noalloc - for callers that cannot allocate device
+ * memory (code under stream capture, tight serving loops, harnesses that
+ * forbid hipMalloc): attn_bwd_deterministic_ex without a workspace argument,
+ * which allocates nothing.  Every buffer the call needs beyond its inputs
+ * and outputs (schedule table, fp32 dQ accumulator, D, lse*log2(e), flags,
+ * counters) comes from a fixed device array of the library,
+ * attn_bwd_noalloc_capacity() bytes (64 MiB) per device, held by every
+ * device the library runs on until the process ends.  The call uses the
+ * single global work queue (no per-XCD accumulator copies), records no
+ * kernel timing, and gives the same bits as the other entry points for the
+ * same schedule.  Problems whose workspace and schedule table do not fit
+ * return ATTN_ERR_WORKSPACE before anything is launched (the accumulator
+ * alone is b*h*ceil(s/128)*128*d*4 bytes).  Every call on a device shares
+ * that device's array: calls that overlap on one device (other streams or
+ * host threads without ordering) race and give wrong results; calls in
+ * sequence on one stream are safe.  Other arguments, errors and
+ * asynchrony as for attn_bwd_deterministic_ex. */
+int attn_bwd_deterministic_noalloc(const void* q, const void* k, const void* v, const void* o,
+                                   const void* dO, const float* lse, void* dq, void* dk, void* dv,
+                                   int b, int h, int s, int d, int causal, int schedule, int dtype,
+                                   float scale, void* stream);
+
+/* Size in bytes of the device array attn_bwd_deterministic_noalloc uses. */
+size_t attn_bwd_noalloc_capacity(void);
+
 /* Bytes of workspace a call with these sizes needs on the current device:
  * fp32 dQ accumulator (b*h*s_pad*d*4, or the per-XCD copies of XCD
  * placement, for either element type), per-(head, Q tile) flags,

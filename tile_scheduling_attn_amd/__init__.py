@@ -30,7 +30,7 @@ EXPORTS = ("attn_fwd", "attn_bwd_deterministic", "attn_bwd_deterministic_ex", "a
            "attn_bwd_get_wait_stats", "attn_sched_size", "attn_sched_get",
            "attn_sched_min_workers", "attn_dagsim", "attn_dagsim_edge", "attn_sched_select",
            "attn_sched_fit", "attn_bwd_get_call_times", "attn_bwd_get_clock", "attn_bwd_set_debug",
-           "attn_bwd_resolve_schedule")
+           "attn_bwd_resolve_schedule", "attn_bwd_deterministic_noalloc", "attn_bwd_noalloc_capacity")
 
 
 class AttnError(RuntimeError):
@@ -98,6 +98,10 @@ def _load():
     lib.attn_bwd_set_debug.restype = i
     lib.attn_bwd_resolve_schedule.argtypes = [i] * 6
     lib.attn_bwd_resolve_schedule.restype = i
+    lib.attn_bwd_deterministic_noalloc.argtypes = [vp] * 9 + [i] * 7 + [f, vp]
+    lib.attn_bwd_deterministic_noalloc.restype = i
+    lib.attn_bwd_noalloc_capacity.argtypes = []
+    lib.attn_bwd_noalloc_capacity.restype = sz
     return lib
 
 
@@ -149,6 +153,18 @@ def attn_bwd_deterministic_ex(q, k, v, o, dO, lse, dq, dk, dv, b, h, s, d, causa
                                          b, h, s, d, int(causal), _sched_id(schedule), dt,
                                          float(scale), _ptr(workspace), int(workspace_bytes),
                                          int(stream or 0))
+
+
+def attn_bwd_deterministic_noalloc(q, k, v, o, dO, lse, dq, dk, dv, b, h, s, d, causal, schedule,
+                                   dtype, scale, stream) -> int:
+    dt = DTYPES[dtype] if isinstance(dtype, str) else int(dtype)
+    return lib.attn_bwd_deterministic_noalloc(*(_ptr(t) for t in (q, k, v, o, dO, lse, dq, dk, dv)),
+                                              b, h, s, d, int(causal), _sched_id(schedule), dt,
+                                              float(scale), int(stream or 0))
+
+
+def attn_bwd_noalloc_capacity() -> int:
+    return lib.attn_bwd_noalloc_capacity()
 
 
 def attn_bwd_workspace_bytes(b, h, s, d, causal, schedule) -> int:

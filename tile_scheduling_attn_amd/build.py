@@ -13,7 +13,7 @@ CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(HERE, "libattn_bwd.so")
 
-SOURCES = ["api.cpp", "schedule.cpp", "bwd_kernels.hip", "fwd_kernels.hip"]
+SOURCES = ["api.cpp", "schedule.cpp", "bwd_kernels.hip", "fwd_kernels.hip", "noalloc.hip"]
 # Packed fp32 VALU forms are switched off for every HIP source.
 HIP_FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",
              "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",

@@ -75,7 +75,8 @@ struct DevSchedule {
     // item_begin (items+1 ints, padded to a multiple of 4) | one 16-byte
     // record per task: {kv tile, q tile, rank, item of the q tile's next
     // contributor or -1 for its last}
-    int* buf = nullptr;
+    int* buf = nullptr;           // device copy (null until uploaded)
+    std::vector<int> table;       // host copy of the same
     int items = 0, tasks = 0, n = 0, min_workers = 1;
     std::vector<int> item_begin;  // host copy
 };
@@ -106,7 +107,7 @@ struct DevState {
 
 constexpr size_t kMaxTimedCalls = 4096;
 
-static std::mutex g_mutex;
+std::mutex g_mutex;
 static std::map<int, DevState> g_dev;
 static bool g_timing = false;
 static bool g_wait_stats = false;
@@ -117,27 +118,44 @@ static unsigned g_spin_limit = 0;
 static int g_wait_offset = 0;
 static unsigned g_delay_seed = 0;
 
-static int dev_init(int dev, DevState& ds) {
+// First use of a device: its CU count, the device status word (a device
+// variable of the library, so no allocation) and the XCD dispatch probe
+// (into `probe_buf` when given, else a buffer of its own).
+static int dev_init(int dev, DevState& ds, void* probe_buf = nullptr) {
     if (ds.init) return ATTN_OK;
     hipDeviceProp_t prop;
     hipError_t e = hipGetDeviceProperties(&prop, dev);
     if (e != hipSuccess) return fail_hip(e, "hipGetDeviceProperties");
     ds.num_cus = prop.multiProcessorCount;
-    e = hipMalloc(&ds.status, sizeof(unsigned));
-    if (e != hipSuccess) return fail_hip(e, "hipMalloc(status)");
+    int rc = status_word_address(&ds.status);
+    if (rc != ATTN_OK) return rc;
     e = hipMemset(ds.status, 0, sizeof(unsigned));
     if (e != hipSuccess) return fail_hip(e, "hipMemset(status)");
-    int rc = probe_xcd_dispatch(ds.num_cus, &ds.xcd_ok);
-    if (rc != ATTN_OK) return rc;
+    if (!probe_buf || 16 * (size_t)ds.num_cus <= kNoAllocProbeBytes) {
+        rc = probe_xcd_dispatch(ds.num_cus, &ds.xcd_ok, static_cast<unsigned*>(probe_buf));
+        if (rc != ATTN_OK) return rc;
+    }
     ds.init = true;
     return ATTN_OK;
 }
 
-static int get_schedule(DevState& ds, int n, bool causal, int schedule, DevSchedule** out) {
+// The schedule tables of (n, mask, schedule), built once per device and
+// cached; `upload` also makes the device copy (an allocation).
+static int get_schedule(DevState& ds, int n, bool causal, int schedule, DevSchedule** out, bool upload = true) {
     auto key = std::make_tuple(n, (int)causal, schedule);
     auto it = ds.schedules.find(key);
     if (it != ds.schedules.end()) {
-        *out = &it->second;
+        DevSchedule& d = it->second;
+        if (upload && !d.buf) {
+            hipError_t e = hipMalloc(&d.buf, d.table.size() * sizeof(int));
+            if (e != hipSuccess) {
+                d.buf = nullptr;
+                return fail_hip(e, "hipMalloc(schedule)");
+            }
+            e = hipMemcpy(d.buf, d.table.data(), d.table.size() * sizeof(int), hipMemcpyHostToDevice);
+            if (e != hipSuccess) return fail_hip(e, "hipMemcpy(schedule)");
+        }
+        *out = &d;
         return ATTN_OK;
     }
     Schedule sc;
@@ -163,13 +181,16 @@ static int get_schedule(DevState& ds, int n, bool causal, int schedule, DevSched
         host.push_back(r >= 0 && r + 1 < sc.count[q] ? item_of[(size_t)q * n + r + 1] : -1);
     }
     DevSchedule d;
-    hipError_t e = hipMalloc(&d.buf, host.size() * sizeof(int));
-    if (e != hipSuccess) return fail_hip(e, "hipMalloc(schedule)");
-    e = hipMemcpy(d.buf, host.data(), host.size() * sizeof(int), hipMemcpyHostToDevice);
-    if (e != hipSuccess) {
-        (void)hipFree(d.buf);
-        return fail_hip(e, "hipMemcpy(schedule)");
+    if (upload) {
+        hipError_t e = hipMalloc(&d.buf, host.size() * sizeof(int));
+        if (e != hipSuccess) return fail_hip(e, "hipMalloc(schedule)");
+        e = hipMemcpy(d.buf, host.data(), host.size() * sizeof(int), hipMemcpyHostToDevice);
+        if (e != hipSuccess) {
+            (void)hipFree(d.buf);
+            return fail_hip(e, "hipMemcpy(schedule)");
+        }
     }
+    d.table = std::move(host);
     d.items = sc.num_items();
     d.item_begin = sc.item_begin;
     d.tasks = (int)sc.task_kv.size();
@@ -248,10 +269,14 @@ static XcdPlan placement_plan(const DevState& ds, const DevSchedule& sch, int sc
     return xcd_plan(sch.item_begin, sch.min_workers, std::min<long long>(ds.num_cus, H * sch.items), H);
 }
 
-static int backward(const void* q, const void* k, const void* v, const void* o, const void* dO,
-                    const float* lse, void* dq, void* dk, void* dv, int b, int h, int s, int d,
-                    int causal, int schedule, int dtype, float scale, void* workspace,
-                    size_t workspace_bytes, void* stream) {
+// One backward call.  `na` (the no-allocation entry point): every device
+// buffer comes from that area (XCD probe at its start, the schedule table,
+// then the workspace), the single global queue is used, no kernel timing is
+// recorded, and nothing is allocated.
+int backward(const void* q, const void* k, const void* v, const void* o, const void* dO,
+             const float* lse, void* dq, void* dk, void* dv, int b, int h, int s, int d,
+             int causal, int schedule, int dtype, float scale, void* workspace,
+             size_t workspace_bytes, void* stream, const NoAllocArea* na) {
     g_last_error.clear();
     if (b < 0 || h < 0 || s < 0) return fail(ATTN_ERR_INVALID_ARG, "b, h and s must be >= 0");
     if (causal != 0 && causal != 1) return fail(ATTN_ERR_INVALID_ARG, "causal must be 0 or 1");
@@ -282,27 +307,42 @@ static int backward(const void* q, const void* k, const void* v, const void* o, 
     hipError_t e = hipGetDevice(&dev);
     if (e != hipSuccess) return fail_hip(e, "hipGetDevice");
     DevState& ds = g_dev[dev];
-    int rc = dev_init(dev, ds);
+    int rc = dev_init(dev, ds, na ? na->base : nullptr);
     if (rc != ATTN_OK) return rc;
     if (schedule == ATTN_SCHED_AUTO) {
         rc = resolve_auto(ds, n, causal != 0, H, d, dtype, &schedule);
         if (rc != ATTN_OK) return rc;
     }
     DevSchedule* sch = nullptr;
-    rc = get_schedule(ds, n, causal != 0, schedule, &sch);
+    rc = get_schedule(ds, n, causal != 0, schedule, &sch, na == nullptr);
     if (rc != ATTN_OK) return rc;
+    int* table = sch->buf;
+    if (na) {
+        // the schedule table after the probe area, then the workspace
+        const size_t tbytes = align_up(sch->table.size() * sizeof(int));
+        if (kNoAllocProbeBytes + tbytes > na->bytes)
+            return fail(ATTN_ERR_WORKSPACE, "the schedule table does not fit the no-allocation area");
+        table = reinterpret_cast<int*>(na->base + kNoAllocProbeBytes);
+        hipError_t e = hipMemcpyAsync(table, sch->table.data(), sch->table.size() * sizeof(int),
+                                      hipMemcpyHostToDevice, (hipStream_t)stream);
+        if (e != hipSuccess) return fail_hip(e, "hipMemcpyAsync(schedule)");
+        workspace = na->base + kNoAllocProbeBytes + tbytes;
+        workspace_bytes = na->bytes - kNoAllocProbeBytes - tbytes;
+    }
 
     // XCD placement needs an accumulator copy per XCD; a caller workspace
     // too small for it but large enough for the global queue runs with that
     WsLayout wl;
     ws_layout(H, s, d, H, wl);
-    const XcdPlan plan = placement_plan(ds, *sch, schedule, H);
+    const XcdPlan plan = na ? XcdPlan{} : placement_plan(ds, *sch, schedule, H);
     WsLayout wl_xcd = wl;
     if (plan.chunks) ws_layout(H, s, d, kQueues * plan.slots, wl_xcd);
     char* ws = static_cast<char*>(workspace);
     bool use_xcd = plan.chunks > 0;
     if (ws) {
-        if (workspace_bytes < wl.total) return fail(ATTN_ERR_WORKSPACE, "workspace smaller than attn_bwd_workspace_bytes()");
+        if (workspace_bytes < wl.total)
+            return fail(ATTN_ERR_WORKSPACE, na ? "problem too large for the no-allocation area"
+                                               : "workspace smaller than attn_bwd_workspace_bytes()");
         use_xcd = use_xcd && workspace_bytes >= wl_xcd.total;
     }
     if (use_xcd) wl = wl_xcd;
@@ -349,7 +389,7 @@ static int backward(const void* q, const void* k, const void* v, const void* o, 
     a.acc_slots = use_xcd ? plan.slots : H;
 
     void** ev = nullptr;
-    if (g_timing && ds.ev_used < kMaxTimedCalls) {
+    if (g_timing && !na && ds.ev_used < kMaxTimedCalls) {
         while (ds.ev_pool.size() < 4 * (ds.ev_used + 1)) {
             hipEvent_t x;
             e = hipEventCreate(&x);
@@ -366,7 +406,7 @@ static int backward(const void* q, const void* k, const void* v, const void* o, 
     L.ev = ev;
     L.status = ds.status;
     L.stats = g_wait_stats ? reinterpret_cast<unsigned long long*>(a.counters + 2) : nullptr;
-    L.item_begin = sch->buf;
+    L.item_begin = table;
     L.tasks = L.item_begin + (sch->items + 1 + 3) / 4 * 4;
     L.items_per_head = sch->items;
     // flags and counters are contiguous: one clear covers both
@@ -405,7 +445,7 @@ extern "C" int attn_bwd_deterministic(const void* q, const void* k, const void* 
     return guarded([&]() -> int {
         const float scale = (d > 0) ? 1.0f / std::sqrt((float)d) : 1.0f;
         return backward(q, k, v, o, dO, lse, dq, dk, dv, b, h, s, d, causal, schedule, ATTN_BF16, scale,
-                        nullptr, 0, nullptr);
+                        nullptr, 0, nullptr, nullptr);
     });
 }
 
@@ -415,7 +455,7 @@ extern "C" int attn_bwd_deterministic_ex(const void* q, const void* k, const voi
                                          float scale, void* workspace, size_t workspace_bytes, void* stream) {
     return guarded([&]() -> int {
         return backward(q, k, v, o, dO, lse, dq, dk, dv, b, h, s, d, causal, schedule, dtype, scale, workspace,
-                        workspace_bytes, stream);
+                        workspace_bytes, stream, nullptr);
     });
 }
 

@@ -1082,6 +1082,17 @@ __global__ __launch_bounds__(256) void bwd_finalize_kernel(const float* __restri
 // ---------------------------------------------------------------------------
 // Launch
 // ---------------------------------------------------------------------------
+// The device status word that attn_bwd_query_status reports (bit 0: a flag
+// wait expired, bit 1: XCD placement could not run as planned); one copy per
+// device, found with hipGetSymbolAddress while that device is current.
+__device__ unsigned g_status_word;
+
+int status_word_address(unsigned** ptr) {
+    const hipError_t e = hipGetSymbolAddress((void**)ptr, HIP_SYMBOL(g_status_word));
+    if (e != hipSuccess) return fail(ATTN_ERR_HIP, "hipGetSymbolAddress(status word)");
+    return ATTN_OK;
+}
+
 // Records the XCD of every work group (one wave each).
 __global__ __launch_bounds__(64) void xcd_probe_kernel(unsigned* out) {
     unsigned x;
@@ -1090,17 +1101,18 @@ __global__ __launch_bounds__(64) void xcd_probe_kernel(unsigned* out) {
 }
 
 // Placement needs XCD ids 0..kQueues-1, each dealt an equal share of a grid.
-int probe_xcd_dispatch(int num_cus, bool* ok) {
+int probe_xcd_dispatch(int num_cus, bool* ok, unsigned* buf) {
     *ok = false;
     if (num_cus < kQueues || num_cus % kQueues) return ATTN_OK;
     const int grid = 4 * num_cus;
-    unsigned* d = nullptr;
-    if (hipMalloc(&d, grid * sizeof(unsigned)) != hipSuccess) return fail(ATTN_ERR_HIP, "hipMalloc(xcd probe)");
+    unsigned* d = buf;
+    if (!d && hipMalloc(&d, grid * sizeof(unsigned)) != hipSuccess) return fail(ATTN_ERR_HIP, "hipMalloc(xcd probe)");
     std::vector<unsigned> h(grid, ~0u);
     hipLaunchKernelGGL(xcd_probe_kernel, dim3(grid), dim3(64), 0, 0, d);
     hipError_t e = hipGetLastError();
     if (e == hipSuccess) e = hipMemcpy(h.data(), d, grid * sizeof(unsigned), hipMemcpyDeviceToHost);
-    if (hipFree(d) != hipSuccess || e != hipSuccess) return fail(ATTN_ERR_HIP, "XCD probe kernel failed");
+    const hipError_t ef = buf ? hipSuccess : hipFree(d);
+    if (ef != hipSuccess || e != hipSuccess) return fail(ATTN_ERR_HIP, "XCD probe kernel failed");
     std::vector<int> per(kQueues, 0);
     bool all = true;
     for (int b = 0; b < grid; ++b) {

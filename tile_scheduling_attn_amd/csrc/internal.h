@@ -93,7 +93,23 @@ struct XcdPlan {
 // task offsets (the work of each item).
 XcdPlan xcd_plan(const std::vector<int>& item_begin, int min_workers, long long grid, long long heads);
 // Whether work group b of a launch runs on XCD b % kQueues on this device.
-int probe_xcd_dispatch(int num_cus, bool* ok);
+// `buf`: device memory for the probe's 4 * num_cus words, or null to
+// allocate it.
+int probe_xcd_dispatch(int num_cus, bool* ok, unsigned* buf = nullptr);
+// Device address of the library's device status word (a device variable).
+int status_word_address(unsigned** ptr);
+
+// A device area that a call uses for every buffer it needs instead of
+// allocating (the no-allocation entry point): XCD probe words at its start
+// (kNoAllocProbeBytes), then the schedule table, then the workspace.
+struct NoAllocArea {
+    char* base;
+    size_t bytes;
+};
+constexpr size_t kNoAllocProbeBytes = 64 * 1024;
+int backward(const void* q, const void* k, const void* v, const void* o, const void* dO, const float* lse,
+             void* dq, void* dk, void* dv, int b, int h, int s, int d, int causal, int schedule, int dtype,
+             float scale, void* workspace, size_t workspace_bytes, void* stream, const NoAllocArea* na);
 
 // Launch-time context prepared by the API layer (device pointers).
 struct BwdLaunch {
