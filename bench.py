@@ -8,6 +8,14 @@ before timing starts.  The forward pass that produces O and lse runs once,
 untimed.  Throughput uses the FlashAttention FLOP convention
 (5 contractions x 2*s*s*d per head, halved under the causal mask).
 
+Besides the headline workload (b2 h16 s8192 d128, full mask, the schedule
+ATTN_SCHED_AUTO resolves to), every workload of the task's list is timed per
+schedule: median, min and max over the timed calls of each (config,
+schedule), % of the bf16 MFMA peak at the nominal 2.4 GHz and at the clock
+the kernel actually ran at, and the ratio to the non-deterministic atomic
+variant.  Those records go to stderr, one JSON object per line, and into the
+headline line under "per_config".
+
 Prints ONE JSON line on stdout; progress goes to stderr.
 """
 from __future__ import annotations
@@ -15,20 +23,31 @@ from __future__ import annotations
 import argparse
 import hashlib
 import json
-import math
 import os
+import statistics
 import sys
 import time
 
 ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
-PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA (2.4 GHz)
 PEAK_FP32_MFMA_TFLOPS = 157.3
+NOMINAL_MHZ = 2400.0
 METRIC = "deterministic attn-bwd TFLOPS (bf16, 1 GPU) & % of MFMA peak; vs non-det"
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_bwd_main_s8k_d128_full_shift.json")
 # the backward kernel's source: its own file and the device helpers it includes
 KERNEL_SOURCES = [os.path.join(ROOT, "tile_scheduling_attn_amd", "csrc", f) for f in ("bwd_kernels.hip", "attn_device.h")]
+# (workload, mask) -> schedules timed for the per-config records
+PER_CONFIG = [
+    ("tiny", False, ("naive", "descending", "shift", "atomic")),
+    ("tiny", True, ("naive", "descending", "shift", "symmetric_shift", "atomic")),
+    ("s2k_d64_causal", True, ("descending", "symmetric_shift", "naive", "atomic")),
+    ("s8k_d128_full", False, ("shift", "naive", "descending", "atomic")),
+    ("s8k_d128_causal", True, ("descending", "symmetric_shift", "shift", "naive", "atomic")),
+    ("s16k_d128", False, ("shift", "naive", "atomic")),
+    ("s16k_d128", True, ("descending", "symmetric_shift", "atomic")),
+]
 
 
 def log(msg):
@@ -59,6 +78,10 @@ def traffic_per_launch(workload, schedule):
 
 
 def time_calls(tsa, pb, schedule, steps, warmup, torch):
+    """`steps` timed calls after `warmup` untimed ones.  ms_per_step: events
+    around all timed calls on the launch stream; per-call times (preprocess
+    to the last kernel, and the main kernel alone) from the library's own
+    HIP events on that stream."""
     out = [torch.empty_like(pb.q) for _ in range(3)]
     stream = torch.cuda.current_stream()
     for _ in range(warmup):
@@ -76,11 +99,13 @@ def time_calls(tsa, pb, schedule, steps, warmup, torch):
     wall = time.perf_counter() - wall0
     tsa.attn_bwd_set_timing(False)
     pre, main, fin = tsa.attn_bwd_get_kernel_times()
+    totals, mains = tsa.attn_bwd_get_call_times(steps)
     rc = tsa.attn_bwd_query_status()
     if rc != 0:
         raise RuntimeError(f"device status {rc}: {tsa.last_error()}")
     return {"ms_per_step": start.elapsed_time(end) / steps, "wall_s": wall,
-            "ms_preprocess": pre, "ms_main": main, "ms_finalize": fin}
+            "ms_preprocess": pre, "ms_main": main, "ms_finalize": fin,
+            "call_ms": totals, "main_ms": mains}
 
 
 def time_forward(tsa, pb, steps, torch):
@@ -104,22 +129,23 @@ def time_forward(tsa, pb, steps, torch):
 
 def flag_wait_stats(tsa, pb, schedule, torch):
     """One extra, untimed call with the kernel's wait counters on: the share of
-    work-item cycles that work groups spent polling dQ flags for their turn."""
+    work-item cycles that work groups spent polling dQ flags for their turn,
+    and the shader clock the main kernel ran at."""
     out = [torch.empty_like(pb.q) for _ in range(3)]
     tsa.attn_bwd_set_wait_stats(True)
     try:
         pb.run(schedule, out=out)
         wait, item, polls = tsa.attn_bwd_get_wait_stats()
+        mhz = tsa.attn_bwd_get_clock()
     finally:
         tsa.attn_bwd_set_wait_stats(False)
     return {"wait_cycles": wait, "item_cycles": item, "polls": polls,
-            "fraction": round(wait / item, 5) if item else None}
+            "fraction": round(wait / item, 5) if item else None, "clock_mhz": round(mhz, 1)}
 
 
 def cpu_baseline(pb, heads, flops_per_head):
     """The fp64 oracle backward (as it stands) on `heads` heads of the same
     workload, using the O and lse of the forward pass; backward stage only."""
-    import numpy as np
     import oracle
     oracle.build(force=False)
     H = pb.b * pb.h
@@ -137,6 +163,48 @@ def cpu_baseline(pb, heads, flops_per_head):
                       f"{dt:.1f} s; same FLOP convention"}
 
 
+def config_records(tsa, torch, steps, warmup):
+    """One record per (workload, mask, schedule) of the task's list."""
+    import workloads
+    from tests.support import Problem
+    records = []
+    for name, causal, scheds in PER_CONFIG:
+        wl = workloads.WORKLOADS[name]
+        pb = Problem(wl.b, wl.h, wl.s, wl.d, wl.dtype, wl.seed, causal)
+        torch.cuda.synchronize()
+        flops = wl.flops(causal)
+        peak = PEAK_BF16_TFLOPS if wl.dtype == "bf16" else PEAK_FP32_MFMA_TFLOPS
+        auto = tsa.attn_bwd_resolve_schedule(wl.b, wl.h, wl.s, wl.d, causal, wl.dtype)
+        atomic_ms = None
+        rows = []
+        for sched in scheds:
+            r = time_calls(tsa, pb, sched, steps, warmup, torch)
+            waits = flag_wait_stats(tsa, pb, sched, torch)
+            med = statistics.median(r["call_ms"])
+            tfl = flops / (med * 1e-3) / 1e12
+            clock = waits["clock_mhz"]
+            rec = {"workload": name, "b": wl.b, "h": wl.h, "s": wl.s, "d": wl.d, "dtype": wl.dtype,
+                   "causal": causal, "schedule": sched, "auto_pick": sched == auto, "calls": len(r["call_ms"]),
+                   "ms_median": round(med, 4), "ms_min": round(min(r["call_ms"]), 4),
+                   "ms_max": round(max(r["call_ms"]), 4),
+                   "main_ms_median": round(statistics.median(r["main_ms"]), 4),
+                   "tflops": round(tfl, 2), "pct_of_peak": round(100 * tfl / peak, 2),
+                   "clock_mhz": clock,
+                   "pct_of_peak_at_clock": round(100 * tfl / (peak * clock / NOMINAL_MHZ), 2) if clock else None,
+                   "flag_wait_fraction": waits["fraction"]}
+            if sched == "atomic":
+                atomic_ms = med
+            rows.append(rec)
+        for rec in rows:
+            if atomic_ms and rec["schedule"] != "atomic":
+                rec["det_over_nondet"] = round(atomic_ms / rec["ms_median"], 4)
+            log(json.dumps(rec))
+        records.extend(rows)
+        del pb
+        torch.cuda.empty_cache()
+    return records
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__)
     ap.add_argument("--gpus", type=int, default=1)
@@ -144,9 +212,10 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="s8k_d128_full")
     ap.add_argument("--causal", type=int, default=None, help="override the workload's mask")
-    ap.add_argument("--schedule", default=None, help="default: shift (full) / descending (causal)")
+    ap.add_argument("--schedule", default="auto", help="schedule of the headline (default: auto)")
     ap.add_argument("--compare", default="naive,atomic",
                     help="comma list of schedules also timed for context ('none' for none)")
+    ap.add_argument("--per-config", type=int, default=1, help="time every workload and schedule (0: skip)")
     ap.add_argument("--cpu-heads", type=int, default=16, help="heads in the CPU oracle sample (0: skip)")
     ap.add_argument("--placement", default="xcd", choices=("xcd", "global"),
                     help="work placement of the deterministic kernel (per-XCD queues or one global queue)")
@@ -157,8 +226,8 @@ def main():
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
-        print("bench.py measures one GPU only: this path has no multi-GPU mode "
-              "(heads shard across GPUs without communication; see the design notes).",
+        print("bench.py measures one GPU only: heads are independent, so the path would shard "
+              "by heads across GPUs without communication, and this build runs on one GPU.",
               file=sys.stderr)
         sys.exit(2)
 
@@ -180,14 +249,16 @@ def main():
     tsa.attn_bwd_set_placement(args.placement)
     wl = workloads.WORKLOADS[args.workload]
     causal = (wl.masks[0] == "causal") if args.causal is None else bool(args.causal)
-    schedule = args.schedule or ("descending" if causal else "shift")
+    schedule = args.schedule
+    if schedule == "auto":
+        schedule = tsa.attn_bwd_resolve_schedule(wl.b, wl.h, wl.s, wl.d, causal, wl.dtype)
     log(f"workload {wl.name}: b={wl.b} h={wl.h} s={wl.s} d={wl.d} {wl.dtype} "
-        f"{'causal' if causal else 'full'}; schedule {schedule}")
+        f"{'causal' if causal else 'full'}; schedule {args.schedule} -> {schedule}")
     pb = Problem(wl.b, wl.h, wl.s, wl.d, wl.dtype, wl.seed, causal)
     torch.cuda.synchronize()
     flops = wl.flops(causal)
 
-    res = time_calls(tsa, pb, schedule, args.steps, args.warmup, torch)
+    res = time_calls(tsa, pb, args.schedule, args.steps, args.warmup, torch)
     tflops = flops / (res["ms_per_step"] * 1e-3) / 1e12
     main_tflops = flops / (res["ms_main"] * 1e-3) / 1e12
     log(f"{schedule}: {res['ms_per_step']:.3f} ms/step, {tflops:.1f} TFLOPS "
@@ -214,14 +285,21 @@ def main():
     log(f"forward (context): {fwd['ms']:.3f} ms, {fwd['tflops']:.1f} TFLOPS")
 
     waits = flag_wait_stats(tsa, pb, schedule, torch)
-    log(f"dQ flag waits: {waits['fraction']} of work-item cycles ({waits['polls']} polls)")
+    log(f"dQ flag waits: {waits['fraction']} of work-item cycles ({waits['polls']} polls); "
+        f"clock {waits['clock_mhz']} MHz")
 
     cpu = None
     if args.cpu_heads > 0:
         log(f"timing the CPU oracle on {args.cpu_heads} head(s)")
         cpu = cpu_baseline(pb, args.cpu_heads, flops / (wl.b * wl.h))
         log(f"cpu oracle: {cpu['value']} TFLOPS on {cpu['cores']} threads")
+    headline_ms = statistics.median(res["call_ms"])
+    del pb
+    torch.cuda.empty_cache()
 
+    per_config = config_records(tsa, torch, args.steps, args.warmup) if args.per_config else []
+
+    clock = waits["clock_mhz"]
     line = {
         "metric": METRIC,
         "value": round(tflops, 2),
@@ -236,11 +314,15 @@ def main():
         "dtype": wl.dtype,
         "data": "synthetic: Q,K,V,dO ~ N(0,1) (PCG64, seeded), O and lse from an fp32 forward",
         "config": {"workload": f"{wl.name}: b={wl.b} h={wl.h} s={wl.s} d={wl.d} "
-                               f"{'causal' if causal else 'full'} mask, schedule {schedule}",
+                               f"{'causal' if causal else 'full'} mask, schedule {args.schedule} -> {schedule}",
                    "b": wl.b, "h": wl.h, "s": wl.s, "d": wl.d, "causal": causal,
-                   "schedule": schedule, "tile": tsa.attn_bwd_tile_size(wl.dtype),
-                   "placement": args.placement},
+                   "schedule": schedule, "schedule_requested": args.schedule,
+                   "tile": tsa.attn_bwd_tile_size(wl.dtype), "placement": args.placement},
         "pct_of_peak": round(100 * tflops / peak, 2),
+        "pct_of_peak_at_clock": round(100 * tflops / (peak * clock / NOMINAL_MHZ), 2) if clock else None,
+        "clock_mhz": clock,
+        "call_ms": {"median": round(headline_ms, 4), "min": round(min(res["call_ms"]), 4),
+                    "max": round(max(res["call_ms"]), 4)},
         "kernel_ms": {"preprocess": round(res["ms_preprocess"], 4), "main": round(res["ms_main"], 4),
                       "finalize": round(res["ms_finalize"], 4)},
         "compare": extra,
@@ -248,6 +330,7 @@ def main():
         "flag_wait": waits,
         "forward": fwd,
         "cpu_baseline": cpu,
+        "per_config": per_config,
     }
     if "atomic" in extra:
         line["det_over_nondet"] = round(tflops / extra["atomic"]["tflops"], 4)
