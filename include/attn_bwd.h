@@ -180,8 +180,20 @@ int attn_bwd_query_status(void* stream);
  * The string is owned by the library and valid until the next call. */
 const char* attn_bwd_last_error(void);
 
-/* Tile edge T the backward uses for `dtype` (128 for bf16, 64 for fp32). */
+/* Tile edge T the backward uses for `dtype` (bf16: 128 unless
+ * attn_bwd_set_tile chose 64; fp32: 64). */
 int attn_bwd_tile_size(int dtype);
+
+/* Tile granularity of later bf16 calls (review page, "What would settle it"
+ * and "Where Pith is reading between the lines": vary the tile granularity
+ * and compare the measured makespan with the DAG model): tile = 128 (the
+ * default; 0 selects it) or 64, square tiles Br = Bc = T, the same
+ * schedules over n = ceil(s/T) tiles.  The 64-row kernel keeps 16 KV rows
+ * per wave (half the operand reuse of the 128-row one) and runs the
+ * compiler-scheduled sub-step.  Changing the tile changes the partial sums
+ * and so the bits, never determinism.  Returns ATTN_OK,
+ * ATTN_ERR_UNSUPPORTED (dtype not bf16) or ATTN_ERR_INVALID_ARG. */
+int attn_bwd_set_tile(int dtype, int tile);
 
 /* Kernel timing.  attn_bwd_set_timing(1) starts a recording: every later
  * backward call (up to 4096) records HIP events on its own stream around

@@ -229,3 +229,13 @@ def test_auto_schedule_is_accepted_and_resolve_checks_arguments():
     assert tsa.lib.attn_bwd_resolve_schedule(1, 1, 128, 64, 2, 0) == -1
     assert tsa.attn_bwd_workspace_bytes(2, 16, 8192, 128, 0, "auto") >= \
         tsa.attn_bwd_workspace_bytes(2, 16, 8192, 128, 0, "shift")
+
+
+def test_set_tile_validates_and_restores_the_default():
+    assert tsa.lib.attn_bwd_set_tile(1, 64) == -2
+    assert tsa.lib.attn_bwd_set_tile(0, 96) == -1
+    assert tsa.lib.attn_bwd_set_tile(0, 64) == 0
+    assert tsa.attn_bwd_tile_size("bf16") == 64
+    assert tsa.lib.attn_bwd_set_tile(0, 0) == 0
+    assert tsa.attn_bwd_tile_size("bf16") == 128
+    assert tsa.attn_bwd_tile_size("fp32") == 64

@@ -30,7 +30,8 @@ EXPORTS = ("attn_fwd", "attn_bwd_deterministic", "attn_bwd_deterministic_ex", "a
            "attn_bwd_get_wait_stats", "attn_sched_size", "attn_sched_get",
            "attn_sched_min_workers", "attn_dagsim", "attn_dagsim_edge", "attn_sched_select",
            "attn_sched_fit", "attn_bwd_get_call_times", "attn_bwd_get_clock", "attn_bwd_set_debug",
-           "attn_bwd_resolve_schedule", "attn_bwd_deterministic_noalloc", "attn_bwd_noalloc_capacity")
+           "attn_bwd_resolve_schedule", "attn_bwd_deterministic_noalloc", "attn_bwd_noalloc_capacity",
+           "attn_bwd_set_tile")
 
 
 class AttnError(RuntimeError):
@@ -102,6 +103,8 @@ def _load():
     lib.attn_bwd_deterministic_noalloc.restype = i
     lib.attn_bwd_noalloc_capacity.argtypes = []
     lib.attn_bwd_noalloc_capacity.restype = sz
+    lib.attn_bwd_set_tile.argtypes = [i, i]
+    lib.attn_bwd_set_tile.restype = i
     return lib
 
 
@@ -181,6 +184,12 @@ def attn_bwd_last_error() -> str:
 
 def attn_bwd_tile_size(dtype) -> int:
     return lib.attn_bwd_tile_size(DTYPES[dtype] if isinstance(dtype, str) else int(dtype))
+
+
+def attn_bwd_set_tile(dtype, tile) -> None:
+    """Tile edge of later bf16 calls: 128 (default, or 0) or 64."""
+    dt = DTYPES[dtype] if isinstance(dtype, str) else int(dtype)
+    _check(lib.attn_bwd_set_tile(dt, int(tile)), "attn_bwd_set_tile")
 
 
 def attn_bwd_set_timing(on: bool) -> int:

@@ -1,6 +1,7 @@
 """Calibrate the DAG model's task costs on this GPU, then pick schedules.
 
-    python tile_scheduling_attn_amd/calibrate.py [--steps K] [--measure-only | --samples FILE]
+    python tile_scheduling_attn_amd/calibrate.py [--steps K] [--tiles 128,64]
+                                                 [--measure-only | --samples FILE]
 
 Times the main kernel of the backward for every (workload, mask, schedule)
 below with the library's own launch-stream events (under the library's
@@ -13,7 +14,13 @@ the fitted costs, measured against simulated makespan for every sample, and
 the schedule
 `attn_sched_select` picks for each shape.  `--measure-only` prints the
 timings as JSON and stops (the fit is host work of a minute or two);
-`--samples FILE` fits timings saved that way.  Inputs are seeded N(0, 1) Q, K, V,
+`--samples FILE` fits timings saved that way.  `--tiles 128,64` also times
+every launch with 64-row tiles (attn_bwd_set_tile) and adds the tile
+granularity check the review page asks for ("What would settle it"): the
+costs fitted at 128 rows, scaled to 64 (a compute phase by its T^2 d MFMA
+work, a reduction by its T d accumulator bytes), predict the 64-row
+makespans, next to the measurements, a fit of their own, and the pages'
+closed form m*n*(c+r) for the full-mask Shift launches.  Inputs are seeded N(0, 1) Q, K, V,
 dO with O and lse of the right scale; the kernel's running time does not
 depend on the values.
 """
@@ -81,33 +88,74 @@ def zero_edge_fit(tsa, ss):
     return best
 
 
-def measure(steps):
+def measure(steps, tiles=(128,)):
     import torch
     import tile_scheduling_attn_amd as tsa
     import workloads
 
     workers = torch.cuda.get_device_properties(0).multi_processor_count  # one work group per CU
-    samples = []  # (n, causal, schedule, heads, workers, ms, workload, d)
+    samples = []  # (n, causal, schedule, heads, workers, ms, workload, d, tile)
     for name, causal, scheds in PLAN:
         wl = workloads.WORKLOADS[name]
-        tile = tsa.attn_bwd_tile_size(wl.dtype)
-        n = -(-wl.s // tile)
         args = inputs(wl, torch)
-        for sched in scheds:
-            ms = time_main(tsa, args, sched, causal, steps, torch)
-            print(f"{name} causal={causal} {sched}: {ms:.4f} ms", file=sys.stderr, flush=True)
-            samples.append((n, causal, sched, wl.b * wl.h, workers, ms, name, wl.d))
+        for t in tiles:
+            tsa.attn_bwd_set_tile(wl.dtype, t)
+            try:
+                tile = tsa.attn_bwd_tile_size(wl.dtype)
+                n = -(-wl.s // tile)
+                for sched in scheds:
+                    ms = time_main(tsa, args, sched, causal, steps, torch)
+                    print(f"{name} causal={causal} tile={tile} {sched}: {ms:.4f} ms", file=sys.stderr, flush=True)
+                    samples.append((n, causal, sched, wl.b * wl.h, workers, ms, name, wl.d, tile))
+            finally:
+                tsa.attn_bwd_set_tile(wl.dtype, 0)
         del args
         torch.cuda.empty_cache()
     return samples
 
 
+def granularity(tsa, samples, fits):
+    """Tile granularity check: 64-row launches against the 128-row costs
+    scaled to 64 rows, a fit of their own, and the closed form m*n*(c+r)."""
+    out = {}
+    for d in sorted({s[7] for s in samples}):
+        f = fits.get(f"d{d}")
+        s64 = [s for s in samples if s[7] == d and s[8] == 64]
+        if not f or not s64:
+            continue
+        c, r, e = f["c_us"] * 1e-3, f["r_us"] * 1e-3, f["e_us"] * 1e-3
+        c64, r64 = c * 0.25, r * 0.5
+        cf, rf, ef, rms = tsa.attn_sched_fit([s[:6] for s in s64], placement=PLACEMENT)
+        rows = []
+        for n, causal, sched, heads, w, ms, name, _, _ in s64:
+            pred = tsa.attn_dagsim_edge(n, causal, sched, heads, w, PLACEMENT, c64, r64, e)[0]
+            row = {"workload": name, "causal": causal, "schedule": sched, "n": n, "measured_ms": round(ms, 4),
+                   "scaled_model_ms": round(pred, 4)}
+            t128 = [x for x in samples if x[6] == name and x[1] == causal and x[2] == sched and x[8] == 128]
+            if t128:
+                row["measured_ms_tile128"] = round(t128[0][5], 4)
+            if not causal and sched == "shift":
+                # the pages' closed form for n workers per head, m heads in turn,
+                # spread over the resident work groups: m*n*(c+r) * n / workers
+                row["closed_form_ms_tile64"] = round(heads * n * (c64 + r64) * n / w, 4)
+                row["closed_form_ms_tile128"] = round(heads * (n // 2) * (c + r) * (n // 2) / w, 4)
+            rows.append(row)
+        rel = [abs(x["scaled_model_ms"] / x["measured_ms"] - 1) for x in rows]
+        out[f"d{d}"] = {"scaled_costs_us": {"c": round(c64 * 1e3, 4), "r": round(r64 * 1e3, 4), "e": round(e * 1e3, 4)},
+                        "scaled_model_rms_rel_err": round(math.sqrt(sum(x * x for x in rel) / len(rel)), 4),
+                        "own_fit_us": {"c": round(cf * 1e3, 4), "r": round(rf * 1e3, 4), "e": round(ef * 1e3, 4),
+                                       "rms_rel_err": round(rms, 4)},
+                        "samples": rows}
+    return out
+
+
 def fit(samples):
     import tile_scheduling_attn_amd as tsa
 
+    samples = [tuple(s) + ((128,) if len(s) < 9 else ()) for s in samples]
     report = {"fits": {}}
     for d in sorted({s[7] for s in samples}):
-        ss = [tuple(s[:7]) for s in samples if s[7] == d]
+        ss = [tuple(s[:7]) for s in samples if s[7] == d and s[8] == 128]
         print(f"fitting d={d} ({len(ss)} samples)", file=sys.stderr, flush=True)
         c, r, e, rms = tsa.attn_sched_fit([s[:6] for s in ss], placement=PLACEMENT)
         c0, r0, _, rms0 = zero_edge_fit(tsa, ss)
@@ -128,12 +176,15 @@ def fit(samples):
                                    "e0": {"c_us": round(c0 * 1e3, 4), "r_us": round(r0 * 1e3, 4),
                                           "rms_rel_err": round(rms0, 4)},
                                    "samples": rows, "selected": picks}
+    if any(s[8] == 64 for s in samples):
+        report["granularity"] = granularity(tsa, samples, report["fits"])
     return report
 
 
 def main():
     ap = argparse.ArgumentParser(description=__doc__)
     ap.add_argument("--steps", type=int, default=5)
+    ap.add_argument("--tiles", default="128", help="comma list of bf16 tile edges to time (128, 64)")
     g = ap.add_mutually_exclusive_group()
     g.add_argument("--measure-only", action="store_true")
     g.add_argument("--samples", metavar="FILE")
@@ -142,7 +193,7 @@ def main():
         with open(a.samples) as f:
             samples = json.load(f)["samples"]
     else:
-        samples = measure(a.steps)
+        samples = measure(a.steps, tuple(int(t) for t in a.tiles.split(",")))
         if a.measure_only:
             print(json.dumps({"samples": samples}))
             return

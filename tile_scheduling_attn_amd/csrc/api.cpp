@@ -4,6 +4,7 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <atomic>
 #include <cmath>
 #include <cstdint>
 #include <cstring>
@@ -201,7 +202,9 @@ static int get_schedule(DevState& ds, int n, bool causal, int schedule, DevSched
     return ATTN_OK;
 }
 
-static int tile_for(int dtype) { return dtype == ATTN_FP32 ? 64 : 128; }
+// Tile edge of later bf16 calls (attn_bwd_set_tile): 128 by default, or 64.
+static std::atomic<int> g_tile_bf16{128};
+static int tile_for(int dtype) { return dtype == ATTN_FP32 ? 64 : g_tile_bf16.load(); }
 
 // Task costs of the DAG model fitted to this kernel on MI355X (microseconds
 // per compute phase c and reduction phase r, and per reduction hand-off e
@@ -209,9 +212,13 @@ static int tile_for(int dtype) { return dtype == ATTN_FP32 ? 64 : 128; }
 struct FittedCosts {
     double c, r, e;
 };
-static FittedCosts fitted_costs(int d) {
-    if (d == 64) return {3.56, 2.26, 0.0};
-    return {3.64, 3.64, 4.41};
+// (fitted at the default tile edge of 128; for another edge T a compute
+// phase scales with its T^2 d MFMA work and a reduction with its T d
+// accumulator bytes)
+static FittedCosts fitted_costs(int d, int tile) {
+    const double f = tile / 128.0;
+    if (d == 64) return {3.56 * f * f, 2.26 * f, 0.0};
+    return {3.64 * f * f, 3.64 * f, 4.41};
 }
 
 // ATTN_SCHED_AUTO.  The review page ("If this is right") has an
@@ -226,13 +233,13 @@ static FittedCosts fitted_costs(int d) {
 // run switch and its [key][query] dS layout cost more than the model's
 // constant c).
 static int resolve_auto(DevState& ds, int n, bool causal, long long H, int d, int dtype, int* out) {
-    const auto key = std::make_tuple(n, (int)causal, H, d, dtype);
+    const auto key = std::make_tuple(n, (int)causal, H, d, dtype * 1000 + tile_for(dtype));
     auto it = ds.auto_pick.find(key);
     if (it != ds.auto_pick.end()) {
         *out = it->second;
         return ATTN_OK;
     }
-    const FittedCosts fc = fitted_costs(d);
+    const FittedCosts fc = fitted_costs(d, tile_for(dtype));
     const int workers = std::max(1, ds.num_cus);
     const int heads = (int)std::min<long long>(H, 1 << 20);
     int pick = -1;
@@ -683,6 +690,17 @@ extern "C" int attn_bwd_get_clock(double* mhz) {
         if (e != hipSuccess) return fail_hip(e, "hipDeviceGetAttribute(wall clock rate)");
         if (v[4] == 0 || wall_khz <= 0) return fail(ATTN_ERR_INVALID_ARG, "no clock span recorded");
         if (mhz) *mhz = (double)v[3] / (double)v[4] * wall_khz / 1e3;
+        return ATTN_OK;
+    });
+}
+
+extern "C" int attn_bwd_set_tile(int dtype, int tile) {
+    return guarded([&]() -> int {
+        if (dtype != ATTN_BF16) return fail(ATTN_ERR_UNSUPPORTED, "attn_bwd_set_tile: only bf16 has a choice of tile");
+        if (tile != 0 && tile != 64 && tile != 128)
+            return fail(ATTN_ERR_INVALID_ARG, "attn_bwd_set_tile: tile must be 0 (default), 64 or 128");
+        std::lock_guard<std::mutex> lock(g_mutex);
+        g_tile_bf16 = tile == 0 ? 128 : tile;
         return ATTN_OK;
     });
 }

@@ -1165,7 +1165,7 @@ static int launch_main_t(const KParams& kp, const BwdLaunch& L) {
 
 template <typename T, int D, int TILE>
 static int launch_main_d(const KParams& kp, const BwdLaunch& L, bool causal, bool det, bool dst) {
-    if constexpr (sizeof(T) == 2 && D == 128) {
+    if constexpr (sizeof(T) == 2 && D == 128 && TILE == 128) {
         if (causal && det && dst) return launch_main_t<T, D, TILE, true, true, true>(kp, L);
     }
     if (causal)
@@ -1246,7 +1246,7 @@ int launch_backward(const BwdArgs& a, const BwdLaunch& L) {
     kp.spin_limit = L.spin_limit ? L.spin_limit : kSpinLimit;
     kp.wait_offset = L.wait_offset;
     kp.delay_seed = L.delay_seed;
-    if (a.dtype == ATTN_BF16) return launch_all<bf16, 128>(a, L, kp);
+    if (a.dtype == ATTN_BF16) return a.tile == 64 ? launch_all<bf16, 64>(a, L, kp) : launch_all<bf16, 128>(a, L, kp);
     return launch_all<float, 64>(a, L, kp);
 }
 
