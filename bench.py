@@ -37,7 +37,8 @@ NOMINAL_MHZ = 2400.0
 METRIC = "deterministic attn-bwd TFLOPS (bf16, 1 GPU) & % of MFMA peak; vs non-det"
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_bwd_main_s8k_d128_full_shift.json")
 # the backward kernel's source: its own file and the device helpers it includes
-KERNEL_SOURCES = [os.path.join(ROOT, "tile_scheduling_attn_amd", "csrc", f) for f in ("bwd_kernels.hip", "attn_device.h")]
+KERNEL_SOURCES = [os.path.join(ROOT, "tile_scheduling_attn_amd", "csrc", f)
+                  for f in ("bwd_main.h", "bwd_kernels.hip", "attn_device.h")]
 # (workload, mask) -> schedules timed for the per-config records
 PER_CONFIG = [
     ("tiny", False, ("naive", "descending", "shift", "atomic")),

@@ -13,7 +13,10 @@ CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(HERE, "libattn_bwd.so")
 
-SOURCES = ["api.cpp", "schedule.cpp", "bwd_kernels.hip", "fwd_kernels.hip", "noalloc.hip"]
+SOURCES = ["api.cpp", "schedule.cpp", "bwd_kernels.hip", "bwd_kernels_d64.hip", "fwd_kernels.hip", "noalloc.hip"]
+# per-source extra flags: the bf16 d = 64 kernels keep MFMA results in
+# architectural registers (see the comment at the top of that file)
+SOURCE_FLAGS = {"bwd_kernels_d64.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"]}
 # Packed fp32 VALU forms are switched off for every HIP source.
 HIP_FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",
              "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
@@ -27,7 +30,7 @@ def build(verbose: bool = False, extra_flags=None) -> str:
     objs = []
     for src in SOURCES:
         obj = os.path.join(objdir, src + ".o")
-        cmd = ["hipcc", *HIP_FLAGS, *(extra_flags or []), "-I", INCLUDE, "-I", CSRC,
+        cmd = ["hipcc", *HIP_FLAGS, *SOURCE_FLAGS.get(src, []), *(extra_flags or []), "-I", INCLUDE, "-I", CSRC,
                "-c", os.path.join(CSRC, src), "-o", obj]
         if verbose:
             print(" ".join(cmd), flush=True)
