@@ -29,6 +29,12 @@ notes):
     accumulated by KV j, j-1, ..., j+1 (mod n), i.e. in the order the tasks
     occur.  Under the causal mask the same cyclic order is kept and masked
     tiles are skipped.
+  * Shift with more KV tiles than SMs (Axiom ledger: the case KV tiles != SMs
+    is handled by refining heads): the KV tiles of a head are cut into
+    consecutive rounds of at most `round_size` tiles; every item keeps
+    Shift's cyclic visiting order, and dQ_j is accumulated round by round,
+    inside a round in the order the round's tasks occur.  With one round
+    (round_size >= n) this is Shift.
   * Symmetric Shift (causal, n even, h = n/2): the SM p < h owns KV_p and then
     KV_{n-1-p}.  Phase 1 (steps t < h): (KV_p, Q_{h + (p+t) mod h}), the dense
     lower-left rectangle.  Phase 2 (steps h+u, u = 0..h): (KV_p, Q_{p+u})
@@ -83,14 +89,18 @@ def head_items(name: str, n: int, causal: bool):
     raise ValueError(f"unknown schedule {name!r}")
 
 
-def dq_orders(name: str, n: int, causal: bool):
-    """For each Q tile, the list of KV tiles in dQ accumulation order."""
+def dq_orders(name: str, n: int, causal: bool, round_size=None):
+    """For each Q tile, the list of KV tiles in dQ accumulation order.
+    round_size (Shift only): KV tiles per round; None means one round."""
     if name == "symmetric_shift" and not causal:
         name = "shift"
     if name in ("naive", "descending"):
         return [[i for i in range(n) if allowed(causal, i, j)] for j in range(n)]
     if name == "shift":
-        return [[(j - t) % n for t in range(n) if allowed(causal, (j - t) % n, j)]
+        w = round_size or n
+        # round first (KV tile i is in round i // w), then the step at which
+        # KV tile i reaches Q tile j: (j - i) mod n
+        return [sorted((i for i in range(n) if allowed(causal, i, j)), key=lambda i: (i // w, (j - i) % n))
                 for j in range(n)]
     if name == "symmetric_shift":
         # step order: position of each task inside its item
@@ -103,11 +113,11 @@ def dq_orders(name: str, n: int, causal: bool):
     raise ValueError(f"unknown schedule {name!r}")
 
 
-def rank_table(name: str, n: int, causal: bool):
+def rank_table(name: str, n: int, causal: bool, round_size=None):
     """rank[kv][q] = position of KV tile kv in dQ_q's accumulation order, or
     -1 for a masked task."""
     rank = [[-1] * n for _ in range(n)]
-    for q, order in enumerate(dq_orders(name, n, causal)):
+    for q, order in enumerate(dq_orders(name, n, causal, round_size)):
         for pos, kv in enumerate(order):
             rank[kv][q] = pos
     return rank
@@ -168,7 +178,7 @@ def longest_path(weight, edges):
     return max(finish.values(), default=0), start, finish
 
 
-def place_static(name, n, causal, heads, sms):
+def place_static(name, n, causal, heads, sms, round_size=None):
     """Head-major items dealt round-robin to `sms` SMs, each SM running its
     items in increasing item order (one head's items are numbered in the
     order head_items lists them)."""
@@ -180,14 +190,14 @@ def place_static(name, n, causal, heads, sms):
             sm_tasks[g % sms].extend((hd, kv, q) for kv, q in tasks)
             g += 1
     orders = {(hd, q): kvs for hd in range(heads)
-              for q, kvs in enumerate(dq_orders(name, n, causal))}
+              for q, kvs in enumerate(dq_orders(name, n, causal, round_size))}
     return sm_tasks, orders
 
 
-def makespan(name, n, causal, heads=1, sms=None, c=1, r=1):
+def makespan(name, n, causal, heads=1, sms=None, c=1, r=1, round_size=None):
     """Critical path of a schedule under static head-major placement on `sms`
     SMs (default n).  None means deadlock."""
-    sm_tasks, orders = place_static(name, n, causal, heads, sms or n)
+    sm_tasks, orders = place_static(name, n, causal, heads, sms or n, round_size)
     res = longest_path(*build_dag(sm_tasks, orders, c, r))
     return None if res is None else res[0]
 
@@ -213,6 +223,15 @@ def closed_form_full(m, n, c, r):
     """Optimal full-mask makespan m*n*(c+r) stated for Shift Scheduling
     ("What would settle it" on the review page)."""
     return m * n * (c + r)
+
+
+def closed_form_full_rounds(m, n, w, c, r):
+    """Full-mask Shift in rounds of w KV tiles on w SMs (w divides n): each
+    round is n steps of c + r on every SM, and a round's first contribution
+    to a Q tile comes no earlier than the previous round's last, so the
+    makespan is the total work over w SMs, m*(n/w)*n*(c+r); with w = n it
+    is the pages' m*n*(c+r)."""
+    return m * (n // w) * n * (c + r)
 
 
 def closed_form_causal(m, n, c, r):

@@ -160,3 +160,49 @@ def test_rank_table_matches_orders():
                 for i in range(n):
                     if not dag.allowed(causal, i, j):
                         assert rank[i][j] == -1
+
+
+# ------------------------------------------------ Shift in rounds (refining)
+@pytest.mark.parametrize("n,w", [(4, 2), (6, 2), (6, 3), (8, 4), (9, 3), (8, 8), (5, 2)])
+@pytest.mark.parametrize("causal", [False, True])
+def test_shift_rounds_orders_are_round_major_and_conflict_free(n, w, causal):
+    """Every dQ order lists its contributors round by round (round of KV tile
+    i = i // w), inside a round in the order they reach the Q tile; inside a
+    round no two SMs touch one Q tile at one step; one round is plain Shift."""
+    orders = dag.dq_orders("shift", n, causal, round_size=w)
+    items = dag.head_items("shift", n, causal)
+    step = {(kv, q): t for it in items for t, (kv, q) in enumerate(it)}
+    for j, kvs in enumerate(orders):
+        assert sorted(kvs) == [i for i in range(n) if dag.allowed(causal, i, j)]
+        rounds = [i // w for i in kvs]
+        assert rounds == sorted(rounds)
+        for a, b in zip(kvs, kvs[1:]):
+            if a // w == b // w:
+                assert (j - a) % n < (j - b) % n
+    if not causal:
+        for r0 in range(0, n, w):
+            for t in range(n):
+                qs = [(i + t) % n for i in range(r0, min(n, r0 + w))]
+                assert len(qs) == len(set(qs))
+    if w >= n:
+        assert orders == dag.dq_orders("shift", n, causal)
+
+
+@pytest.mark.parametrize("n,w", [(4, 2), (6, 2), (6, 3), (8, 4), (8, 2)])
+def test_shift_rounds_reach_the_total_work_bound(n, w):
+    """Full mask, w SMs, rounds of w tiles: the critical path equals the work
+    per SM, m*(n/w)*n*(c+r) (m*n*(c+r) when w = n, the review page's
+    T_full^opt), for several cost ratios and two heads."""
+    for c, r in COSTS:
+        for m in (1, 2):
+            got = dag.makespan("shift", n, False, heads=m, sms=w, c=c, r=r, round_size=w)
+            assert got == dag.closed_form_full_rounds(m, n, w, c, r), (n, w, c, r, m)
+    assert dag.closed_form_full_rounds(3, 8, 8, 2, 1) == dag.closed_form_full(3, 8, 2, 1)
+
+
+@pytest.mark.parametrize("n,w", [(4, 2), (6, 3), (8, 4)])
+def test_shift_rounds_need_a_whole_round_resident(n, w):
+    """Waits inside a round wrap around the round (as in Shift), so a round's
+    w items must run at once: w SMs finish, w - 1 SMs deadlock."""
+    assert dag.makespan("shift", n, False, sms=w, round_size=w) is not None
+    assert dag.makespan("shift", n, False, sms=w - 1, round_size=w) is None
