@@ -51,7 +51,11 @@ extern "C" {
  * dQ accumulated in ascending KV order).  DESCENDING is Descending Q-Tile
  * Iteration (Fig. 4; same dQ order as NAIVE).  SHIFT is Shift Scheduling
  * (Fig. 6: the owner of KV tile i visits Q tiles i, i+1, ..., wrapping; dQ_j
- * accumulated in visiting order).  SYMMETRIC_SHIFT is Symmetric Shift
+ * accumulated in visiting order); with more than 256 KV tiles (more than the
+ * work groups MI355X keeps resident) the KV tiles are cut into equal rounds
+ * of at most 256 consecutive tiles and dQ_j is accumulated round by round,
+ * inside a round in visiting order (Axiom ledger: KV tiles != SMs is handled
+ * by refining heads).  SYMMETRIC_SHIFT is Symmetric Shift
  * Scheduling with two-phase workload folding for the causal mask (Fig. 7;
  * equals SHIFT under the full mask; needs an even tile count when causal).
  * ATOMIC is the non-deterministic comparison point: unordered fp32 atomic
@@ -308,8 +312,10 @@ int attn_sched_get(int n, int causal, int schedule, int* item_begin, int* task_k
 /* Smallest number of simultaneously resident work groups with which the
  * schedule always makes progress when items are handed out in increasing
  * order: 1 for NAIVE, DESCENDING and ATOMIC (every wait points to an
- * earlier item), the items per head for SHIFT and SYMMETRIC_SHIFT (cyclic
- * waits inside a head).  Returns a negative status on bad arguments. */
+ * earlier item), the KV tiles of a round for SHIFT (n up to 256, else
+ * ceil(n / ceil(n / 256))) and the items per head for SYMMETRIC_SHIFT
+ * (cyclic waits inside a round or a head).  Returns a negative status on
+ * bad arguments. */
 int attn_sched_min_workers(int n, int causal, int schedule);
 
 /* ------------------------------------------------------------------------

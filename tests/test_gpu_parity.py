@@ -329,17 +329,36 @@ def test_gradient_identities_full_size():
 def test_items_longer_than_one_record_block():
     """An item with more tasks than the kernel keeps in LDS at once (257 Q
     tiles of 64 rows, fp32, ragged tail): the records are reloaded mid-item.
-    Shift at this size needs 257 resident work groups; the launcher either
-    runs it or refuses with ATTN_ERR_COSCHEDULE, never hangs."""
+    Shift with 257 KV tiles runs in two rounds of 129 (more KV tiles than the
+    256 resident work groups)."""
     s = 257 * 64 - 40
     pb = Problem(1, 1, s, 64, "fp32", 4242, False)
-    _say(f"long item fp32 s={s} naive")
-    g = pb.run("naive")
-    torch.cuda.synchronize()
-    _check_parity(pb, g, [0], f"long item s={s} naive")
-    try:
-        g2 = pb.run("shift")
+    for sched in ("naive", "shift"):
+        _say(f"long item fp32 s={s} {sched}")
+        g = pb.run(sched)
         torch.cuda.synchronize()
-        _check_parity(pb, g2, [0], f"long item s={s} shift")
-    except tsa.AttnError as e:
-        assert e.code == -3, e
+        _check_parity(pb, g, [0], f"long item s={s} {sched}")
+    assert tsa.attn_sched_min_workers(257, False, "shift") == 129
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_shift_rounds_with_more_tiles_than_work_groups(causal):
+    """bf16 with 257 KV tiles of 128 rows (s = 32896, more KV tiles than the
+    256 resident work groups): Shift runs in two rounds; parity with the
+    oracle, bitwise repeatable, and the same bits under both placements."""
+    s = 257 * 128
+    pb = Problem(1, 1, s, 64, "bf16", 2570 + causal, causal)
+    _say(f"shift rounds s={s} causal={causal}")
+    ref = [t.clone() for t in pb.run("shift")]
+    torch.cuda.synchronize()
+    assert tsa.attn_bwd_query_status() == 0, tsa.last_error()
+    _check_parity(pb, ref, [0], f"shift rounds s={s} causal={causal}")
+    for place in ("global", "xcd"):
+        tsa.attn_bwd_set_placement(place)
+        try:
+            out = pb.run("shift")
+            torch.cuda.synchronize()
+        finally:
+            tsa.attn_bwd_set_placement("xcd")
+        for a, b_ in zip(ref, out):
+            assert torch.equal(a.view(torch.int16), b_.view(torch.int16)), place

@@ -244,3 +244,44 @@ def test_fit_argument_errors():
         tsa.attn_sched_fit([(8, False, "shift", 1, 8, 0.0)])
     with pytest.raises(tsa.AttnError):  # Shift on fewer workers than it needs deadlocks
         tsa.attn_sched_fit([(8, False, "shift", 1, 4, 1.0)])
+
+
+# ------------------------------------------------ Shift in rounds (n > 256)
+@pytest.mark.parametrize("n", [257, 300, 513])
+@pytest.mark.parametrize("causal", [False, True])
+def test_shift_rounds_match_the_oracle(n, causal):
+    """With more than 256 KV tiles Shift runs in rounds of
+    ceil(n / ceil(n / 256)) tiles: items, rank table and contributor counts
+    equal the oracle's definition with that round size, and the resident
+    work groups it needs are one round."""
+    rounds = -(-n // 256)
+    w = -(-n // rounds)
+    got = tsa.attn_sched_get(n, causal, "shift")
+    want_items = dag.head_items("shift", n, causal)
+    ib = got["item_begin"]
+    assert len(ib) == n + 1
+    for i, tasks in enumerate(want_items):
+        assert list(zip(got["task_kv"][ib[i]:ib[i + 1]], got["task_q"][ib[i]:ib[i + 1]])) == tasks
+    assert got["rank"].tolist() == dag.rank_table("shift", n, causal, round_size=w)
+    assert tsa.attn_sched_min_workers(n, causal, "shift") == w
+    if n <= 256:
+        assert w == n
+
+
+def test_shift_up_to_256_tiles_is_one_round():
+    for n in (2, 64, 255, 256):
+        assert tsa.attn_sched_min_workers(n, False, "shift") == n
+        assert tsa.attn_sched_get(n, False, "shift")["rank"].tolist() == dag.rank_table("shift", n, False)
+
+
+def test_shift_rounds_simulate_to_the_total_work_bound():
+    """n = 512 full mask on 256 workers: two rounds of 256, no waits, the
+    critical path is the work per worker, 2 * 512 * (c + r), as the oracle's
+    closed form for rounds states; one worker fewer than a round deadlocks."""
+    c, r = 3.0, 1.0
+    mk, wait, _ = tsa.attn_dagsim(512, False, "shift", 1, 256, 1, c, r)
+    assert mk == pytest.approx(dag.closed_form_full_rounds(1, 512, 256, c, r))
+    assert wait == pytest.approx(0.0)
+    with pytest.raises(tsa.AttnError) as e:
+        tsa.attn_dagsim(512, False, "shift", 1, 255, 1, c, r)
+    assert e.value.code == -7

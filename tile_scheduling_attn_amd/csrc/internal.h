@@ -27,8 +27,14 @@ struct Schedule {
     std::vector<int> task_kv, task_q;
     std::vector<int> rank;        // n*n, -1 = masked (or ATOMIC)
     std::vector<int> count;       // n
+    int round_size = 0;           // Shift: KV tiles per round (0: not Shift)
     int num_items() const { return (int)item_begin.size() - 1; }
 };
+
+// Shift cuts a head's KV tiles into rounds of at most this many tiles (the
+// work groups MI355X keeps resident: one per CU), so that a round's items,
+// which wait on each other cyclically, always run together.
+constexpr int kShiftRound = 256;
 
 int build_schedule(int n, bool causal, int schedule, Schedule& out);
 int min_workers(const Schedule& sc);

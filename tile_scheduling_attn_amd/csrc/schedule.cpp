@@ -9,6 +9,11 @@
 //  - descending: Q tiles descending, same dQ order as the baseline;
 //  - shift: KV tile i visits Q tiles i, i+1, ... (mod n); dQ_j is accumulated
 //    in visiting order, i.e. by KV j, j-1, ... (mod n); masked tiles skipped;
+//    with more KV tiles than kShiftRound (more than the work groups that can
+//    be resident at once; Axiom ledger: KV tiles != SMs is handled by refining
+//    heads) the KV tiles are cut into rounds of at most kShiftRound
+//    consecutive tiles, items keep the cyclic order, and dQ_j is accumulated
+//    round by round, inside a round in visiting order;
 //  - symmetric shift (causal, n even, h = n/2): work item p < h runs
 //    phase 1 = (KV p, Q h + (p+t) mod h) for t < h, then phase 2 walks the
 //    folded square from the diagonal: (KV p, Q p+u) while u < h-p, then
@@ -76,13 +81,17 @@ int build_schedule(int n, bool causal, int schedule, Schedule& out) {
             close_item();
         }
         // KV kv reaches Q q after (q - kv) mod n steps; the dQ order of q is
-        // the order in which its contributors visit it.
+        // the order in which its contributors visit it, round by round
+        const int rounds = (n + kShiftRound - 1) / kShiftRound;
+        const int w = n > 0 ? (n + rounds - 1) / rounds : 0;
+        out.round_size = w;
         for (int q = 0; q < n; ++q) {
             int pos = 0;
-            for (int t = 0; t < n; ++t) {
-                int kv = ((q - t) % n + n) % n;
-                if (visible(causal, kv, q)) out.rank[(size_t)kv * n + q] = pos++;
-            }
+            for (int rd = 0; rd < rounds; ++rd)
+                for (int t = 0; t < n; ++t) {
+                    int kv = ((q - t) % n + n) % n;
+                    if (kv / w == rd && visible(causal, kv, q)) out.rank[(size_t)kv * n + q] = pos++;
+                }
         }
     } else {  // symmetric shift, causal, n even
         const int h = n / 2;
@@ -176,6 +185,9 @@ int min_workers(const Schedule& sc) {
     if (sc.schedule == ATTN_SCHED_NAIVE || sc.schedule == ATTN_SCHED_DESCENDING ||
         sc.schedule == ATTN_SCHED_ATOMIC)
         return 1;
+    // the Shift family waits cyclically inside a round (Shift: a round of at
+    // most kShiftRound KV tiles; Symmetric Shift: all of a head's items)
+    if (sc.round_size > 0) return std::max(1, sc.round_size);
     return std::max(1, sc.num_items());
 }
 
