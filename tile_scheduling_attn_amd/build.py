@@ -50,5 +50,39 @@ def build(verbose: bool = False, extra_flags=None) -> str:
     return LIB
 
 
+def resource_usage() -> str:
+    """Per-kernel register, scratch and occupancy figures of the HIP sources,
+    from the compiler's kernel-resource-usage remarks, as a markdown table
+    (compiles the device code again, with the build's flags)."""
+    import re
+    rows = []
+    for src in SOURCES:
+        if not src.endswith(".hip"):
+            continue
+        cmd = ["hipcc", *HIP_FLAGS, *SOURCE_FLAGS.get(src, []), "-I", INCLUDE, "-I", CSRC, "--cuda-device-only",
+               "-c", os.path.join(CSRC, src), "-o", os.devnull, "-Rpass-analysis=kernel-resource-usage"]
+        r = subprocess.run(cmd, capture_output=True, text=True)
+        if r.returncode != 0:
+            raise RuntimeError(f"hipcc failed on {src}:\n{r.stderr}")
+        cur = None
+        for line in r.stderr.splitlines():
+            m = re.search(r"remark: Function Name: (\S+)", line)
+            if m:
+                cur = {"source": src, "kernel": m.group(1)}
+                rows.append(cur)
+                continue
+            m = re.search(r"remark:\s+([A-Za-z ]+?)(?: \[[^\]]*\])?:\s+(-?\d+)", line)
+            if m and cur is not None:
+                cur[m.group(1).strip()] = int(m.group(2))
+    cols = ["VGPRs", "AGPRs", "TotalSGPRs", "ScratchSize", "VGPRs Spill", "SGPRs Spill", "Occupancy", "LDS Size"]
+    out = ["| source | kernel | " + " | ".join(cols) + " |", "|" + "---|" * (len(cols) + 2)]
+    for r in rows:
+        out.append(f"| {r['source']} | `{r['kernel']}` | " + " | ".join(str(r.get(c, "")) for c in cols) + " |")
+    return "\n".join(out)
+
+
 if __name__ == "__main__":
-    print(build(verbose="-v" in sys.argv))
+    if "--resource-usage" in sys.argv:
+        print(resource_usage())
+    else:
+        print(build(verbose="-v" in sys.argv))
