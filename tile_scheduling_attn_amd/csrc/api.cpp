@@ -208,17 +208,18 @@ static int tile_for(int dtype) { return dtype == ATTN_FP32 ? 64 : g_tile_bf16.lo
 
 // Task costs of the DAG model fitted to this kernel on MI355X (microseconds
 // per compute phase c and reduction phase r, and per reduction hand-off e
-// between XCDs; simulator placement 2), per head dimension.
+// between XCDs; simulator placement 2), per head dimension and tile edge.
+// Each tile edge has a fit of its own: scaling the 128-row costs to 64 rows
+// (c by the T^2 d matrix work, r by the T d accumulator bytes) predicts the
+// 64-row makespans 30-50% short, because at 64 rows the ordered dQ traffic
+// and the flag hand-offs, not the matrix work, set the pace.  fp32 (64-row
+// tiles only) takes the bf16 64-row costs: only their ratios matter here.
 struct FittedCosts {
     double c, r, e;
 };
-// (fitted at the default tile edge of 128; for another edge T a compute
-// phase scales with its T^2 d MFMA work and a reduction with its T d
-// accumulator bytes)
 static FittedCosts fitted_costs(int d, int tile) {
-    const double f = tile / 128.0;
-    if (d == 64) return {3.56 * f * f, 2.26 * f, 0.0};
-    return {3.64 * f * f, 3.64 * f, 4.41};
+    if (tile == 64) return d == 64 ? FittedCosts{0.396, 1.976, 0.0} : FittedCosts{1.078, 3.118, 1.392};
+    return d == 64 ? FittedCosts{3.668, 2.152, 0.0} : FittedCosts{5.562, 1.807, 0.0};
 }
 
 // ATTN_SCHED_AUTO.  The review page ("If this is right") has an
