@@ -206,6 +206,27 @@ def config_records(tsa, torch, steps, warmup):
     return records
 
 
+def atomic_roofline(tsa, torch, wl, causal, ms_main):
+    """The ATOMIC variant's main kernel against the device's fp32 atomic-add
+    throughput: the library's rate kernel makes as many adds, in the same
+    pattern, into an accumulator of the same size."""
+    tile = tsa.attn_bwd_tile_size(wl.dtype)
+    n = -(-wl.s // tile)
+    heads = wl.b * wl.h
+    tasks = heads * (n * (n + 1) // 2 if causal else n * n)
+    adds = tasks * tile * wl.d                     # one fp32 add per dQ element of each task
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    acc = torch.empty(heads * n * tile * wl.d, dtype=torch.float32, device="cuda")
+    per_group = max(1, round(adds / (cus * 128 * 128)))
+    ms, made = tsa.attn_bwd_atomic_rate(acc, per_group)
+    del acc
+    rate = made / (ms * 1e-3)
+    achieved = adds / (ms_main * 1e-3)
+    return {"bound": "fp32 atomic adds", "achieved_adds_per_s": float(f"{achieved:.4g}"),
+            "peak_adds_per_s": float(f"{rate:.4g}"), "frac": round(achieved / rate, 4),
+            "variant_adds": adds, "rate_kernel_adds": int(made), "rate_kernel_ms": round(ms, 4)}
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__)
     ap.add_argument("--gpus", type=int, default=1)
@@ -274,6 +295,10 @@ def main():
         extra[other] = {"ms_per_step": round(r2["ms_per_step"], 4), "tflops": round(t2, 2),
                         "ms_main": round(r2["ms_main"], 4)}
         log(f"{other}: {r2['ms_per_step']:.3f} ms/step, {t2:.1f} TFLOPS")
+
+    if "atomic" in extra:
+        extra["atomic"]["atomic_roofline"] = atomic_roofline(tsa, torch, wl, causal, extra["atomic"]["ms_main"])
+        log(f"atomic variant: {extra['atomic']['atomic_roofline']}")
 
     peak = PEAK_BF16_TFLOPS if wl.dtype == "bf16" else PEAK_FP32_MFMA_TFLOPS
     roofline = {"bound": "mfma", "achieved": round(main_tflops, 2), "peak": peak,

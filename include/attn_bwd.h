@@ -253,6 +253,20 @@ int attn_bwd_get_wait_stats(unsigned long long* wait_cycles, unsigned long long*
  * ATTN_ERR_HIP. */
 int attn_bwd_get_clock(double* mhz);
 
+/* Reference rate for the ATOMIC schedule: fp32 global atomic adds without
+ * return value on the current device, in the pattern of the ATOMIC main
+ * kernel's dQ (one instruction adds 64 contiguous bytes to each of four rows
+ * of a 128x128 fp32 tile; one work group of 256 threads per CU adds `tasks`
+ * whole tiles, tile (group * 7 + task) mod ntiles of acc).  acc: device
+ * buffer of acc_bytes (at least 65536, 256-byte aligned, overwritten;
+ * ntiles = acc_bytes / 65536).  Runs one untimed and one timed launch on
+ * `stream` (hipStream_t; NULL = default stream) and waits for them; *ms
+ * receives the timed launch's duration, *adds its number of adds (either
+ * may be NULL).  Measurement only: touches no attention state.  Returns
+ * ATTN_OK, ATTN_ERR_INVALID_ARG (null or misaligned acc, acc_bytes < 65536,
+ * tasks outside 1..65536) or ATTN_ERR_HIP. */
+int attn_bwd_atomic_rate(void* acc, size_t acc_bytes, int tasks, void* stream, float* ms, double* adds);
+
 /* Test hooks for the failure and race paths (they change timing, never the
  * reduction order).  spin_limit: polls before a dQ flag wait gives up
  * (0: the default of 2^20).  wait_offset (0..65535, normally 0): added to

@@ -239,3 +239,17 @@ def test_set_tile_validates_and_restores_the_default():
     assert tsa.lib.attn_bwd_set_tile(0, 0) == 0
     assert tsa.attn_bwd_tile_size("bf16") == 128
     assert tsa.attn_bwd_tile_size("fp32") == 64
+
+
+def test_atomic_rate_validates_arguments_before_any_gpu_call():
+    import ctypes
+    ms, adds = ctypes.c_float(1.0), ctypes.c_double(1.0)
+    r = tsa.lib.attn_bwd_atomic_rate
+    assert r(None, 1 << 20, 4, None, ctypes.byref(ms), ctypes.byref(adds)) == -1   # null buffer
+    assert ms.value == 0 and adds.value == 0                                      # outputs cleared
+    assert r(ctypes.c_void_p(256 + 16), 1 << 20, 4, None, None, None) == -1        # misaligned
+    assert r(ctypes.c_void_p(256), 65535, 4, None, None, None) == -1               # below one tile
+    assert r(ctypes.c_void_p(256), 1 << 20, 0, None, None, None) == -1             # no tasks
+    assert r(ctypes.c_void_p(256), 1 << 20, 65537, None, None, None) == -1         # too many tasks
+    with pytest.raises(tsa.AttnError):
+        tsa.attn_bwd_atomic_rate(__import__("torch").zeros(1 << 14), 4)            # host tensor

@@ -31,7 +31,7 @@ EXPORTS = ("attn_fwd", "attn_bwd_deterministic", "attn_bwd_deterministic_ex", "a
            "attn_sched_min_workers", "attn_dagsim", "attn_dagsim_edge", "attn_sched_select",
            "attn_sched_fit", "attn_bwd_get_call_times", "attn_bwd_get_clock", "attn_bwd_set_debug",
            "attn_bwd_resolve_schedule", "attn_bwd_deterministic_noalloc", "attn_bwd_noalloc_capacity",
-           "attn_bwd_set_tile")
+           "attn_bwd_set_tile", "attn_bwd_atomic_rate")
 
 
 class AttnError(RuntimeError):
@@ -97,6 +97,8 @@ def _load():
     lib.attn_bwd_get_clock.restype = i
     lib.attn_bwd_set_debug.argtypes = [ctypes.c_uint, i, ctypes.c_uint]
     lib.attn_bwd_set_debug.restype = i
+    lib.attn_bwd_atomic_rate.argtypes = [vp, ctypes.c_size_t, i, vp, ctypes.POINTER(ctypes.c_float), dp]
+    lib.attn_bwd_atomic_rate.restype = i
     lib.attn_bwd_resolve_schedule.argtypes = [i] * 6
     lib.attn_bwd_resolve_schedule.restype = i
     lib.attn_bwd_deterministic_noalloc.argtypes = [vp] * 9 + [i] * 7 + [f, vp]
@@ -246,6 +248,21 @@ def attn_bwd_get_clock() -> float:
     mhz = ctypes.c_double()
     _check(lib.attn_bwd_get_clock(ctypes.byref(mhz)), "attn_bwd_get_clock")
     return mhz.value
+
+
+def attn_bwd_atomic_rate(acc, tasks: int):
+    """fp32 atomic adds per second in the ATOMIC variant's dQ pattern, on
+    `acc` (a device float32 tensor of at least 64 KiB, overwritten) and the
+    current stream: returns (ms of the timed launch, adds made)."""
+    import torch
+    if not _on_device(acc) or acc.dtype != torch.float32 or not acc.is_contiguous():
+        raise AttnError(-1, "attn_bwd_atomic_rate", "acc must be a contiguous float32 device tensor")
+    ms, adds = ctypes.c_float(), ctypes.c_double()
+    stream = torch.cuda.current_stream().cuda_stream
+    _check(lib.attn_bwd_atomic_rate(ctypes.c_void_p(acc.data_ptr()), acc.numel() * 4, int(tasks),
+                                    ctypes.c_void_p(stream), ctypes.byref(ms), ctypes.byref(adds)),
+           "attn_bwd_atomic_rate")
+    return ms.value, adds.value
 
 
 def attn_bwd_set_debug(spin_limit=0, wait_offset=0, delay_seed=0) -> None:

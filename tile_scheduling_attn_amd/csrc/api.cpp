@@ -308,7 +308,9 @@ int backward(const void* q, const void* k, const void* v, const void* o, const v
         return fail(ATTN_ERR_INVALID_ARG, "workspace must be 256-byte aligned");
 
     const int tile = tile_for(dtype);
-    const int n = (s + tile - 1) / tile;  // <= kMaxTiles since s <= kMaxSeq
+    // at most kMaxTiles at 128-row tiles; 64-row tiles can exceed it, which
+    // build_schedule rejects as unsupported
+    const int n = (s + tile - 1) / tile;
 
     std::lock_guard<std::mutex> lock(g_mutex);
     int dev = 0;
@@ -691,6 +693,39 @@ extern "C" int attn_bwd_get_clock(double* mhz) {
         if (e != hipSuccess) return fail_hip(e, "hipDeviceGetAttribute(wall clock rate)");
         if (v[4] == 0 || wall_khz <= 0) return fail(ATTN_ERR_INVALID_ARG, "no clock span recorded");
         if (mhz) *mhz = (double)v[3] / (double)v[4] * wall_khz / 1e3;
+        return ATTN_OK;
+    });
+}
+
+extern "C" int attn_bwd_atomic_rate(void* acc, size_t acc_bytes, int tasks, void* stream, float* ms, double* adds) {
+    return guarded([&]() -> int {
+        if (ms) *ms = 0;
+        if (adds) *adds = 0;
+        if (!acc || ((uintptr_t)acc & (kAlign - 1))) return fail(ATTN_ERR_INVALID_ARG, "acc must be a 256-byte aligned device pointer");
+        if (acc_bytes < 65536) return fail(ATTN_ERR_INVALID_ARG, "acc must hold at least one 128x128 fp32 tile");
+        if (tasks < 1 || tasks > 65536) return fail(ATTN_ERR_INVALID_ARG, "tasks must be in 1..65536");
+        const int ntiles = (int)std::min<size_t>(acc_bytes / 65536, (size_t)1 << 30);
+        int dev = 0, cus = 0;
+        hipError_t e = hipGetDevice(&dev);
+        if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+        if (e != hipSuccess) return fail_hip(e, "device query");
+        if (cus < 1) return fail(ATTN_ERR_HIP, "no compute units reported");
+        hipEvent_t ev[2] = {nullptr, nullptr};
+        for (auto& x : ev)
+            if ((e = hipEventCreate(&x)) != hipSuccess) break;
+        int rc = e == hipSuccess ? ATTN_OK : fail_hip(e, "hipEventCreate");
+        if (rc == ATTN_OK) rc = launch_atomic_rate(static_cast<float*>(acc), ntiles, cus, tasks, stream);
+        if (rc == ATTN_OK && (e = hipEventRecord(ev[0], (hipStream_t)stream)) != hipSuccess) rc = fail_hip(e, "hipEventRecord");
+        if (rc == ATTN_OK) rc = launch_atomic_rate(static_cast<float*>(acc), ntiles, cus, tasks, stream);
+        if (rc == ATTN_OK && (e = hipEventRecord(ev[1], (hipStream_t)stream)) != hipSuccess) rc = fail_hip(e, "hipEventRecord");
+        if (rc == ATTN_OK && (e = hipEventSynchronize(ev[1])) != hipSuccess) rc = fail_hip(e, "hipEventSynchronize");
+        float t = 0;
+        if (rc == ATTN_OK && (e = hipEventElapsedTime(&t, ev[0], ev[1])) != hipSuccess) rc = fail_hip(e, "hipEventElapsedTime");
+        for (auto& x : ev)
+            if (x) (void)hipEventDestroy(x);
+        if (rc != ATTN_OK) return rc;
+        if (ms) *ms = t;
+        if (adds) *adds = (double)cus * tasks * 128.0 * 128.0;
         return ATTN_OK;
     });
 }

@@ -108,6 +108,31 @@ int probe_xcd_dispatch(int num_cus, bool* ok, unsigned* buf) {
     return ATTN_OK;
 }
 
+// Throughput of fp32 atomic adds without return value in the pattern of the
+// atomic variant's dQ: per task a work group adds one 128x128 fp32 tile into
+// tile (group * 7 + task) mod ntiles of acc, each instruction covering 64
+// contiguous bytes of four rows.  A measurement kernel: the ATOMIC schedule's
+// main kernel is compared with the rate it reaches.
+__global__ __launch_bounds__(256) void atomic_rate_kernel(float* acc, int ntiles, int tasks) {
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    for (int t = 0; t < tasks; ++t) {
+        const int tile = (int)(((long long)blockIdx.x * 7 + t) % ntiles);
+        float* base = acc + (size_t)tile * 128 * 128;
+#pragma unroll 4
+        for (int i = 0; i < 64; ++i) {
+            const int row = (i >> 1) * 4 + (lane >> 4);
+            const int col = w * 32 + (i & 1) * 16 + (lane & 15);
+            unsafeAtomicAdd(base + row * 128 + col, 1.0f);
+        }
+    }
+}
+
+int launch_atomic_rate(float* acc, int ntiles, int grid, int tasks, void* stream) {
+    hipLaunchKernelGGL(atomic_rate_kernel, dim3(grid), dim3(256), 0, (hipStream_t)stream, acc, ntiles, tasks);
+    if (hipGetLastError() != hipSuccess) return fail(ATTN_ERR_HIP, "atomic rate kernel launch failed");
+    return ATTN_OK;
+}
+
 template <typename T, int TILE>
 static int launch_all(const BwdArgs& a, const BwdLaunch& L, KParams& kp) {
     const T* o = static_cast<const T*>(a.o);

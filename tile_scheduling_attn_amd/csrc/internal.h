@@ -104,6 +104,9 @@ XcdPlan xcd_plan(const std::vector<int>& item_begin, int min_workers, long long 
 int probe_xcd_dispatch(int num_cus, bool* ok, unsigned* buf = nullptr);
 // Device address of the library's device status word (a device variable).
 int status_word_address(unsigned** ptr);
+// fp32 atomic-add throughput kernel (tasks 128x128 tiles per work group into
+// acc, which holds ntiles such tiles)
+int launch_atomic_rate(float* acc, int ntiles, int grid, int tasks, void* stream);
 
 // A device area that a call uses for every buffer it needs instead of
 // allocating (the no-allocation entry point): XCD probe words at its start
