@@ -64,10 +64,8 @@ extern "C" {
  * page, "If this is right": the schedules are complementary and an
  * implementation selects one per configuration): the DAG model with task
  * costs fitted on MI355X simulates each schedule the shape admits under the
- * kernel's XCD placement and the shortest makespan wins, except that under
- * the causal mask at head dimension 128 Descending replaces Symmetric Shift
- * (measured faster; the summary page's Surprising findings report the same
- * at headdim 128).  attn_bwd_resolve_schedule tells which one a call gets;
+ * kernel's XCD placement and the shortest makespan wins.
+ * attn_bwd_resolve_schedule tells which one a call gets;
  * the choice is deterministic for a shape, so AUTO is as reproducible as
  * the schedule it resolves to. */
 typedef enum {

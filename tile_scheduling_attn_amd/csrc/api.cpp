@@ -226,13 +226,7 @@ static FittedCosts fitted_costs(int d, int tile) {
 // implementation select one of the complementary schedules per
 // configuration; here the DAG model with the fitted costs and the kernel's
 // XCD placement simulates every deterministic schedule the shape admits on
-// the device's resident work groups and takes the shortest makespan.  One
-// measured exception the model cannot see: under the causal mask at head
-// dimension 128 Descending Q-Tile Iteration is taken instead of Symmetric
-// Shift (the summary page's Surprising findings report the same ordering on
-// H800 and put it down to register pressure; on MI355X the folded item's
-// run switch and its [key][query] dS layout cost more than the model's
-// constant c).
+// the device's resident work groups and takes the shortest makespan.
 static int resolve_auto(DevState& ds, int n, bool causal, long long H, int d, int dtype, int* out) {
     const auto key = std::make_tuple(n, (int)causal, H, d, dtype * 1000 + tile_for(dtype));
     auto it = ds.auto_pick.find(key);
@@ -263,7 +257,6 @@ static int resolve_auto(DevState& ds, int n, bool causal, long long H, int d, in
         }
     }
     if (pick < 0) return fail(ATTN_ERR_COSCHEDULE, "no deterministic schedule fits the resident work groups");
-    if (pick == ATTN_SCHED_SYMMETRIC_SHIFT && causal && d == 128) pick = ATTN_SCHED_DESCENDING;
     ds.auto_pick[key] = pick;
     *out = pick;
     return ATTN_OK;

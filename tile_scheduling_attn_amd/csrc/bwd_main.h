@@ -1002,6 +1002,13 @@ void bwd_main_kernel(KParams p) {
                     more = __builtin_amdgcn_readfirstlane(stask[(t - t_beg) % L::MAXT][0]) == kv;
                 }
             } while (more);
+            // The run's last release goes out now, once its stores are
+            // acknowledged, not at the next run's first staging barrier: that
+            // barrier comes only after the dK/dV stores and the next run's K/V
+            // loads, and when the next contributor is itself on the last task
+            // of its run (a reduction chain of run ends, as under Symmetric
+            // Shift's fold) every link would add that delay to the chain.
+            if (pend_flag) publish();
             store_dkdv(kv);
         }
         // the prefetch issued by the item's last sub-step lands before the
