@@ -128,20 +128,33 @@ def time_forward(tsa, pb, steps, torch):
     return {"ms": round(ms, 4), "tflops": round(flops / (ms * 1e-3) / 1e12, 2)}
 
 
-def flag_wait_stats(tsa, pb, schedule, torch):
+def flag_wait_stats(tsa, pb, schedule, torch, hist_file=None):
     """One extra, untimed call with the kernel's wait counters on: the share of
     work-item cycles that work groups spent polling dQ flags for their turn,
-    and the shader clock the main kernel ran at."""
+    the task positions (steps of an item) where most of that waiting
+    happened, and the shader clock the main kernel ran at.  hist_file: also
+    write the whole (item mod 64, step) histogram there as JSON."""
     out = [torch.empty_like(pb.q) for _ in range(3)]
     tsa.attn_bwd_set_wait_stats(True)
     try:
         pb.run(schedule, out=out)
         wait, item, polls = tsa.attn_bwd_get_wait_stats()
         mhz = tsa.attn_bwd_get_clock()
+        hist = tsa.attn_bwd_get_wait_hist()
     finally:
         tsa.attn_bwd_set_wait_stats(False)
+    by_step = [sum(row[j] for row in hist) for j in range(len(hist[0]))]
+    total = sum(by_step)
+    top = sorted(range(len(by_step)), key=lambda j: -by_step[j])[:4]
+    if hist_file:
+        with open(hist_file, "w") as f:
+            json.dump({"workload": f"b={pb.b} h={pb.h} s={pb.s} d={pb.d} causal={pb.causal}",
+                       "schedule": schedule, "wait_cycles": wait, "item_cycles": item,
+                       "rows": "work item of the head mod 64", "columns": "task position in the item (last: 127 or more)",
+                       "cycles": hist}, f)
     return {"wait_cycles": wait, "item_cycles": item, "polls": polls,
-            "fraction": round(wait / item, 5) if item else None, "clock_mhz": round(mhz, 1)}
+            "fraction": round(wait / item, 5) if item else None, "clock_mhz": round(mhz, 1),
+            "top_steps": {str(j): round(by_step[j] / total, 4) for j in top} if total else {}}
 
 
 def cpu_baseline(pb, heads, flops_per_head):
@@ -241,6 +254,8 @@ def main():
     ap.add_argument("--cpu-heads", type=int, default=16, help="heads in the CPU oracle sample (0: skip)")
     ap.add_argument("--placement", default="xcd", choices=("xcd", "global"),
                     help="work placement of the deterministic kernel (per-XCD queues or one global queue)")
+    ap.add_argument("--wait-hist", metavar="FILE", default=None,
+                    help="write the headline schedule's flag-wait histogram (item mod 64 x step) to FILE")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of MIB MiB five times (scales the HBM "
                          "traffic counters of a profiler run) and exit")
@@ -310,7 +325,7 @@ def main():
     fwd = time_forward(tsa, pb, max(5, args.steps // 2), torch)
     log(f"forward (context): {fwd['ms']:.3f} ms, {fwd['tflops']:.1f} TFLOPS")
 
-    waits = flag_wait_stats(tsa, pb, schedule, torch)
+    waits = flag_wait_stats(tsa, pb, schedule, torch, args.wait_hist)
     log(f"dQ flag waits: {waits['fraction']} of work-item cycles ({waits['polls']} polls); "
         f"clock {waits['clock_mhz']} MHz")
 

@@ -243,6 +243,15 @@ int attn_bwd_set_wait_stats(int on);
 int attn_bwd_get_wait_stats(unsigned long long* wait_cycles, unsigned long long* item_cycles,
                             unsigned long long* polls);
 
+/* Where the waits of the last call with wait statistics happened: cycles[64 *
+ * 128] (caller's host buffer) receives, for each (work item of the head
+ * modulo 64, position of the task in its item, positions past 127 counted as
+ * 127), the clock cycles work groups spent waiting for that task's dQ flag,
+ * summed over heads.  A schedule's reduction chains show up as the steps and
+ * items where waits pile up.  Synchronises the device.  Returns ATTN_OK,
+ * ATTN_ERR_INVALID_ARG (null buffer, no such call) or ATTN_ERR_HIP. */
+int attn_bwd_get_wait_hist(unsigned long long* cycles);
+
 /* The shader clock the main kernel of the last call with wait statistics
  * ran at, in MHz: each work group's span on the shader clock counter
  * (s_memtime) divided by its span on the constant-rate clock

@@ -253,3 +253,7 @@ def test_atomic_rate_validates_arguments_before_any_gpu_call():
     assert r(ctypes.c_void_p(256), 1 << 20, 65537, None, None, None) == -1         # too many tasks
     with pytest.raises(tsa.AttnError):
         tsa.attn_bwd_atomic_rate(__import__("torch").zeros(1 << 14), 4)            # host tensor
+
+
+def test_wait_histogram_validates_arguments_before_any_gpu_call():
+    assert tsa.lib.attn_bwd_get_wait_hist(None) == -1

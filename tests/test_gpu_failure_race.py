@@ -89,3 +89,24 @@ def test_expired_waits_report_timeout_and_next_call_is_clean(sched, debug_hooks)
         assert rel_err(to_np_heads(t, [0, 3]), ref[name]) <= TOL["bf16"], name
 
 
+
+
+def test_wait_histogram_accounts_for_every_wait_cycle():
+    """The per-(item, step) wait histogram sums exactly to the wait-cycle
+    total of the same call, puts nothing on a rank-0 task (Shift's first
+    task of every item is its Q tile's first contribution), and is cleared
+    between calls."""
+    pb = Problem(1, 8, 2048, 128, "bf16", 4242, False)
+    tsa.attn_bwd_set_wait_stats(True)
+    try:
+        for _ in range(2):
+            pb.run("shift")
+            wait, item, polls = tsa.attn_bwd_get_wait_stats()
+            hist = tsa.attn_bwd_get_wait_hist()
+            assert tsa.attn_bwd_query_status() == 0, tsa.last_error()
+            _say(f"wait {wait} of {item} cycles, {polls} polls")
+            assert sum(map(sum, hist)) == wait
+            assert all(row[0] == 0 for row in hist)
+            assert all(v == 0 for row in hist[16:] for v in row)  # 16 items per head
+    finally:
+        tsa.attn_bwd_set_wait_stats(False)

@@ -31,7 +31,7 @@ EXPORTS = ("attn_fwd", "attn_bwd_deterministic", "attn_bwd_deterministic_ex", "a
            "attn_sched_min_workers", "attn_dagsim", "attn_dagsim_edge", "attn_sched_select",
            "attn_sched_fit", "attn_bwd_get_call_times", "attn_bwd_get_clock", "attn_bwd_set_debug",
            "attn_bwd_resolve_schedule", "attn_bwd_deterministic_noalloc", "attn_bwd_noalloc_capacity",
-           "attn_bwd_set_tile", "attn_bwd_atomic_rate")
+           "attn_bwd_set_tile", "attn_bwd_atomic_rate", "attn_bwd_get_wait_hist")
 
 
 class AttnError(RuntimeError):
@@ -99,6 +99,8 @@ def _load():
     lib.attn_bwd_set_debug.restype = i
     lib.attn_bwd_atomic_rate.argtypes = [vp, ctypes.c_size_t, i, vp, ctypes.POINTER(ctypes.c_float), dp]
     lib.attn_bwd_atomic_rate.restype = i
+    lib.attn_bwd_get_wait_hist.argtypes = [ull]
+    lib.attn_bwd_get_wait_hist.restype = i
     lib.attn_bwd_resolve_schedule.argtypes = [i] * 6
     lib.attn_bwd_resolve_schedule.restype = i
     lib.attn_bwd_deterministic_noalloc.argtypes = [vp] * 9 + [i] * 7 + [f, vp]
@@ -241,6 +243,15 @@ def attn_bwd_resolve_schedule(b, h, s, d, causal, dtype="bf16") -> str:
     dt = DTYPES[dtype] if isinstance(dtype, str) else int(dtype)
     rc = _check(lib.attn_bwd_resolve_schedule(b, h, s, d, int(causal), dt), "attn_bwd_resolve_schedule")
     return {v: k for k, v in SCHEDULES.items()}[rc]
+
+
+def attn_bwd_get_wait_hist():
+    """Flag-wait cycles of the last call made with wait statistics on, as a
+    64 x 128 nested list: [work item of the head mod 64][task position in
+    the item, capped at 127]."""
+    buf = (ctypes.c_ulonglong * (64 * 128))()
+    _check(lib.attn_bwd_get_wait_hist(buf), "attn_bwd_get_wait_hist")
+    return [list(buf[r * 128:(r + 1) * 128]) for r in range(64)]
 
 
 def attn_bwd_get_clock() -> float:

@@ -44,6 +44,9 @@ constexpr size_t kAlign = 256;
 constexpr int kPadRows = 128;     // s is padded to a multiple of this
 constexpr int kMinTile = 64;      // smallest tile: bounds the flag count
 constexpr int kCounterWords = 64; // ticket + wait statistics
+// wait histogram (when wait statistics are on): u64 wait cycles per
+// (item of the head mod kHistItems, task position in the item, capped)
+constexpr int kHistItems = 64, kHistSteps = 128;
 // Accepted sizes: s up to kMaxTiles tiles of the largest tile edge (128), and
 // b*h within an int (the kernels index heads with ints).
 constexpr int kMaxSeq = kMaxTiles * 128;
@@ -52,7 +55,7 @@ constexpr long long kMaxHeads = (1LL << 31) - 1;
 static size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 
 struct WsLayout {
-    size_t s_pad, acc, delta, flags, counters, total;
+    size_t s_pad, acc, delta, flags, counters, hist, total;
     int nflags;
 };
 
@@ -68,7 +71,8 @@ static bool ws_layout(long long H, long long s, int d, long long acc_heads, WsLa
     // D, then lse * log2(e), [H][s_pad] each
     w.flags = align_up(w.delta + 2 * (size_t)H * w.s_pad * sizeof(float));
     w.counters = align_up(w.flags + (size_t)w.nflags * sizeof(unsigned));
-    w.total = align_up(w.counters + kCounterWords * sizeof(unsigned));
+    w.hist = align_up(w.counters + kCounterWords * sizeof(unsigned));
+    w.total = align_up(w.hist + (size_t)kHistItems * kHistSteps * sizeof(unsigned long long));
     return true;
 }
 
@@ -103,6 +107,7 @@ struct DevState {
     std::vector<char> ev_finalize;   // per recorded call: finalize launched
     size_t ev_used = 0;
     void* last_counters = nullptr;
+    void* last_hist = nullptr;
     bool stats_valid = false;
 };
 
@@ -218,8 +223,8 @@ struct FittedCosts {
     double c, r, e;
 };
 static FittedCosts fitted_costs(int d, int tile) {
-    if (tile == 64) return d == 64 ? FittedCosts{0.396, 1.976, 0.0} : FittedCosts{1.078, 3.118, 1.392};
-    return d == 64 ? FittedCosts{3.668, 2.152, 0.0} : FittedCosts{5.562, 1.807, 0.0};
+    if (tile == 64) return d == 64 ? FittedCosts{0.392, 1.845, 0.0} : FittedCosts{1.185, 2.996, 0.711};
+    return d == 64 ? FittedCosts{3.115, 2.273, 0.0} : FittedCosts{3.297, 3.775, 2.904};
 }
 
 // ATTN_SCHED_AUTO.  The review page ("If this is right") has an
@@ -409,11 +414,13 @@ int backward(const void* q, const void* k, const void* v, const void* o, const v
     L.ev = ev;
     L.status = ds.status;
     L.stats = g_wait_stats ? reinterpret_cast<unsigned long long*>(a.counters + 2) : nullptr;
+    L.whist = g_wait_stats ? reinterpret_cast<unsigned long long*>(ws + wl.hist) : nullptr;
     L.item_begin = table;
     L.tasks = L.item_begin + (sch->items + 1 + 3) / 4 * 4;
     L.items_per_head = sch->items;
-    // flags and counters are contiguous: one clear covers both
-    L.nclear32 = (int)((wl.total - wl.flags) / sizeof(unsigned));
+    // flags, counters and the wait histogram are contiguous: one clear
+    // covers them (the histogram only when it is written)
+    L.nclear32 = (int)(((g_wait_stats ? wl.total : wl.hist) - wl.flags) / sizeof(unsigned));
     if (use_xcd) L.plan = plan;
     L.spin_limit = g_spin_limit;
     L.wait_offset = g_wait_offset;
@@ -433,6 +440,7 @@ int backward(const void* q, const void* k, const void* v, const void* o, const v
         ds.ev_used++;
     }
     ds.last_counters = a.counters;
+    ds.last_hist = ws + wl.hist;
     ds.stats_valid = g_wait_stats;
     g_last_dev = dev;
     return ATTN_OK;
@@ -748,6 +756,22 @@ extern "C" int attn_bwd_set_wait_stats(int on) {
     return guarded([&]() -> int {
         std::lock_guard<std::mutex> lock(g_mutex);
         g_wait_stats = on != 0;
+        return ATTN_OK;
+    });
+}
+
+extern "C" int attn_bwd_get_wait_hist(unsigned long long* cycles) {
+    return guarded([&]() -> int {
+        if (!cycles) return fail(ATTN_ERR_INVALID_ARG, "null histogram buffer");
+        std::lock_guard<std::mutex> lock(g_mutex);
+        auto it = g_dev.find(g_last_dev);
+        if (it == g_dev.end() || !it->second.stats_valid || !it->second.last_hist)
+            return fail(ATTN_ERR_INVALID_ARG, "no call with wait statistics recorded");
+        hipError_t e = hipDeviceSynchronize();
+        if (e != hipSuccess) return fail_hip(e, "hipDeviceSynchronize");
+        e = hipMemcpy(cycles, it->second.last_hist, (size_t)kHistItems * kHistSteps * sizeof(unsigned long long),
+                      hipMemcpyDeviceToHost);
+        if (e != hipSuccess) return fail_hip(e, "hipMemcpy(wait histogram)");
         return ATTN_OK;
     });
 }

@@ -200,6 +200,7 @@ int launch_backward(const BwdArgs& a, const BwdLaunch& L) {
     kp.abort = a.counters + 1;
     kp.status = L.status;
     kp.stats = L.stats;
+    kp.whist = L.whist;
     kp.item_begin = L.item_begin;
     kp.tasks = reinterpret_cast<const i32x4*>(L.tasks);
     kp.H = a.H;

@@ -111,6 +111,7 @@ struct KParams {
     unsigned* abort;    // counters[1]: a wait of this call expired
     unsigned* status;   // device status word, reported by attn_bwd_query_status
     unsigned long long* stats;  // null unless wait statistics are on
+    unsigned long long* whist;  // wait cycles per (item of the head mod 64, task position), or null
     const int* item_begin;
     const i32x4* tasks;  // {kv tile, q tile, rank, contributors} per task
     int H, s, n, items_per_head, s_pad;
@@ -878,8 +879,10 @@ void bwd_main_kernel(KParams p) {
                         seen = __hip_atomic_load(flag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
                     }
                     if (p.stats) {
-                        wait_cycles += __builtin_readcyclecounter() - t0;
+                        const unsigned long long dw = __builtin_readcyclecounter() - t0;
+                        wait_cycles += dw;
                         polls += spins + 1;
+                        atomicAdd(p.whist + (pat & 63) * 128 + min(t - t_beg, 127), dw);
                     }
                     s_prev = seen;
                 }

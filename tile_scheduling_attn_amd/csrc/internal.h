@@ -128,6 +128,7 @@ struct BwdLaunch {
     void** ev;                    // 4 hipEvent_t to record, or null
     unsigned* status;             // device status word (bit 0: wait expired)
     unsigned long long* stats;    // wait statistics or null
+    unsigned long long* whist;    // wait histogram [64][128] or null
     const int* item_begin;        // per item pattern: first task, items+1 entries
     const int* tasks;             // 4 ints per task: kv, q, rank, contributors
     int items_per_head;
