@@ -274,6 +274,28 @@ int attn_bwd_get_clock(double* mhz);
  * tasks outside 1..65536) or ATTN_ERR_HIP. */
 int attn_bwd_atomic_rate(void* acc, size_t acc_bytes, int tasks, void* stream, float* ms, double* adds);
 
+/* Latency of one dQ hand-off between two work groups, for calibrating the
+ * DAG model's reduction cost r and release edge e (the survey of the
+ * review page's model asks for the flag latency per XCD distance).  Work
+ * group 0 and work group `pong` (1..63) take turns `iters` times (2..2^20):
+ * a turn waits for a flag in device memory to reach its number (relaxed
+ * agent-scope loads), then, for mode 1 or 2, reads the previous turn's
+ * 64 KiB fp32 tile, adds to it and writes its own, waits for its stores and
+ * moves the flag on (relaxed agent-scope store) - the main kernel's R phase.
+ * mode 0: the flag alone; 1: the tile through the L2 of the XCD (plain
+ * stores, L2-scope loads; meaningful when both groups share an XCD); 2: the
+ * tile written through to memory and read from it, as between XCDs.  The
+ * device deals work groups to its XCDs in turn, so `pong` selects the XCD
+ * distance; *xcd_ping and *xcd_pong receive the XCD each group ran on.
+ * buf: device buffer of at least attn_bwd_handoff_bytes() bytes, 256-byte
+ * aligned, overwritten.  Runs on `stream` and waits for it; *ns receives
+ * the time per turn in nanoseconds.  Every wait is bounded.  Returns
+ * ATTN_OK, ATTN_ERR_INVALID_ARG, ATTN_ERR_TIMEOUT (a wait gave up) or
+ * ATTN_ERR_HIP.  Measurement only: touches no attention state. */
+int attn_bwd_handoff_latency(void* buf, size_t buf_bytes, int pong, int iters, int mode, void* stream,
+                             double* ns, int* xcd_ping, int* xcd_pong);
+size_t attn_bwd_handoff_bytes(void);
+
 /* Test hooks for the failure and race paths (they change timing, never the
  * reduction order).  spin_limit: polls before a dQ flag wait gives up
  * (0: the default of 2^20).  wait_offset (0..65535, normally 0): added to

@@ -257,3 +257,18 @@ def test_atomic_rate_validates_arguments_before_any_gpu_call():
 
 def test_wait_histogram_validates_arguments_before_any_gpu_call():
     assert tsa.lib.attn_bwd_get_wait_hist(None) == -1
+
+
+def test_handoff_latency_validates_arguments_before_any_gpu_call():
+    import ctypes
+    r = tsa.lib.attn_bwd_handoff_latency
+    n = tsa.lib.attn_bwd_handoff_bytes()
+    assert n >= 2 * 65536
+    ns = ctypes.c_double(1.0)
+    assert r(None, n, 8, 100, 0, None, ctypes.byref(ns), None, None) == -1 and ns.value == 0
+    assert r(ctypes.c_void_p(256 + 8), n, 8, 100, 0, None, None, None, None) == -1     # misaligned
+    assert r(ctypes.c_void_p(256), n - 1, 8, 100, 0, None, None, None, None) == -1     # too small
+    assert r(ctypes.c_void_p(256), n, 0, 100, 0, None, None, None, None) == -1         # pong 0 is ping
+    assert r(ctypes.c_void_p(256), n, 64, 100, 0, None, None, None, None) == -1
+    assert r(ctypes.c_void_p(256), n, 8, 1, 0, None, None, None, None) == -1           # one turn
+    assert r(ctypes.c_void_p(256), n, 8, 100, 3, None, None, None, None) == -1         # unknown mode

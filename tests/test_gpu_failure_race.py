@@ -110,3 +110,19 @@ def test_wait_histogram_accounts_for_every_wait_cycle():
             assert all(v == 0 for row in hist[16:] for v in row)  # 16 items per head
     finally:
         tsa.attn_bwd_set_wait_stats(False)
+
+
+def test_handoff_latency_measures_every_xcd_distance():
+    """The hand-off probe runs its bounded ping-pong to the end between work
+    group 0 and work groups 1..8 (every XCD distance, the last one on work
+    group 0's XCD when the device deals groups to its XCDs in turn), and a
+    64 KiB tile written through to memory costs more per turn than the flag
+    alone."""
+    seen = set()
+    for pong in range(1, 9):
+        flag_ns, a, b = tsa.attn_bwd_handoff_latency(pong, iters=200, mode=0)
+        tile_ns, a2, b2 = tsa.attn_bwd_handoff_latency(pong, iters=200, mode=2)
+        _say(f"pong {pong}: XCD {a} -> {b}: flag {flag_ns:.0f} ns, tile {tile_ns:.0f} ns")
+        assert 0 <= a < 8 and 0 <= b < 8 and 0 < flag_ns < tile_ns < 1e6
+        seen.add((b - a) % 8)
+    assert len(seen) == 8

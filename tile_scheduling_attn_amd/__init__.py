@@ -31,7 +31,8 @@ EXPORTS = ("attn_fwd", "attn_bwd_deterministic", "attn_bwd_deterministic_ex", "a
            "attn_sched_min_workers", "attn_dagsim", "attn_dagsim_edge", "attn_sched_select",
            "attn_sched_fit", "attn_bwd_get_call_times", "attn_bwd_get_clock", "attn_bwd_set_debug",
            "attn_bwd_resolve_schedule", "attn_bwd_deterministic_noalloc", "attn_bwd_noalloc_capacity",
-           "attn_bwd_set_tile", "attn_bwd_atomic_rate", "attn_bwd_get_wait_hist")
+           "attn_bwd_set_tile", "attn_bwd_atomic_rate", "attn_bwd_get_wait_hist",
+           "attn_bwd_handoff_latency", "attn_bwd_handoff_bytes")
 
 
 class AttnError(RuntimeError):
@@ -101,6 +102,10 @@ def _load():
     lib.attn_bwd_atomic_rate.restype = i
     lib.attn_bwd_get_wait_hist.argtypes = [ull]
     lib.attn_bwd_get_wait_hist.restype = i
+    lib.attn_bwd_handoff_latency.argtypes = [vp, sz, i, i, i, vp, dp, ip, ip]
+    lib.attn_bwd_handoff_latency.restype = i
+    lib.attn_bwd_handoff_bytes.argtypes = []
+    lib.attn_bwd_handoff_bytes.restype = sz
     lib.attn_bwd_resolve_schedule.argtypes = [i] * 6
     lib.attn_bwd_resolve_schedule.restype = i
     lib.attn_bwd_deterministic_noalloc.argtypes = [vp] * 9 + [i] * 7 + [f, vp]
@@ -243,6 +248,22 @@ def attn_bwd_resolve_schedule(b, h, s, d, causal, dtype="bf16") -> str:
     dt = DTYPES[dtype] if isinstance(dtype, str) else int(dtype)
     rc = _check(lib.attn_bwd_resolve_schedule(b, h, s, d, int(causal), dt), "attn_bwd_resolve_schedule")
     return {v: k for k, v in SCHEDULES.items()}[rc]
+
+
+def attn_bwd_handoff_latency(pong: int, iters: int = 2000, mode: int = 0, buf=None):
+    """Nanoseconds per dQ hand-off between work group 0 and work group
+    `pong` (mode 0: flag only; 1: a 64 KiB tile through the XCD's L2; 2: the
+    tile written through to memory), with the XCDs the two groups ran on:
+    returns (ns, xcd_ping, xcd_pong)."""
+    import torch
+    if buf is None:
+        buf = torch.empty(int(lib.attn_bwd_handoff_bytes()) // 4, dtype=torch.float32, device="cuda")
+    ns, a, b = ctypes.c_double(), ctypes.c_int(), ctypes.c_int()
+    stream = torch.cuda.current_stream().cuda_stream
+    _check(lib.attn_bwd_handoff_latency(ctypes.c_void_p(buf.data_ptr()), buf.numel() * buf.element_size(), int(pong),
+                                        int(iters), int(mode), ctypes.c_void_p(stream), ctypes.byref(ns),
+                                        ctypes.byref(a), ctypes.byref(b)), "attn_bwd_handoff_latency")
+    return ns.value, a.value, b.value
 
 
 def attn_bwd_get_wait_hist():

@@ -1,7 +1,7 @@
 """Calibrate the DAG model's task costs on this GPU, then pick schedules.
 
     python tile_scheduling_attn_amd/calibrate.py [--steps K] [--tiles 128,64]
-                                                 [--measure-only | --samples FILE]
+                                                 [--measure-only | --samples FILE | --handoff]
 
 Times the main kernel of the backward for every (workload, mask, schedule)
 below with the library's own launch-stream events (under the library's
@@ -20,7 +20,10 @@ granularity check the review page asks for ("What would settle it"): the
 costs fitted at 128 rows, scaled to 64 (a compute phase by its T^2 d MFMA
 work, a reduction by its T d accumulator bytes), predict the 64-row
 makespans, next to the measurements, a fit of their own, and the pages'
-closed form m*n*(c+r) for the full-mask Shift launches.  Inputs are seeded N(0, 1) Q, K, V,
+closed form m*n*(c+r) for the full-mask Shift launches.  `--handoff` measures
+what the fit only infers: the latency of one dQ hand-off (flag, and flag
+plus a 64 KiB tile) between work groups at every XCD distance.  Inputs are
+seeded N(0, 1) Q, K, V,
 dO with O and lse of the right scale; the kernel's running time does not
 depend on the values.
 """
@@ -181,6 +184,33 @@ def fit(samples):
     return report
 
 
+def handoff(iters=2000, reps=3):
+    """Measured hand-off latency per XCD distance (attn_bwd_handoff_latency):
+    for work group 0 and work groups 1..8, the nanoseconds per turn of the
+    flag alone, of a 64 KiB tile written through to memory (the main
+    kernel's hand-off between XCDs), and, when both groups share an XCD, of
+    the tile through that XCD's L2 (its hand-off within an XCD); median of
+    `reps` runs of `iters` turns."""
+    import statistics
+    import torch
+    import tile_scheduling_attn_amd as tsa
+
+    buf = torch.empty(int(tsa.lib.attn_bwd_handoff_bytes()) // 4, dtype=torch.float32, device="cuda")
+    rows = []
+    for pong in range(1, 9):
+        row = {"pong": pong}
+        for mode, key in ((0, "flag_ns"), (2, "tile_through_memory_ns"), (1, "tile_through_l2_ns")):
+            runs = [tsa.attn_bwd_handoff_latency(pong, iters, mode, buf) for _ in range(reps)]
+            row["xcd_ping"], row["xcd_pong"] = runs[0][1], runs[0][2]
+            if mode == 1 and row["xcd_ping"] != row["xcd_pong"]:
+                continue  # L2-scope hand-offs are only coherent within one XCD
+            row[key] = round(statistics.median(r[0] for r in runs), 1)
+        row["xcd_distance"] = (row["xcd_pong"] - row["xcd_ping"]) % 8
+        print(json.dumps(row), file=sys.stderr, flush=True)
+        rows.append(row)
+    return {"iters": iters, "reps": reps, "rows": rows}
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__)
     ap.add_argument("--steps", type=int, default=5)
@@ -188,7 +218,11 @@ def main():
     g = ap.add_mutually_exclusive_group()
     g.add_argument("--measure-only", action="store_true")
     g.add_argument("--samples", metavar="FILE")
+    g.add_argument("--handoff", action="store_true", help="measure the hand-off latency per XCD distance and stop")
     a = ap.parse_args()
+    if a.handoff:
+        print(json.dumps(handoff(), indent=1))
+        return
     if a.samples:
         with open(a.samples) as f:
             samples = json.load(f)["samples"]

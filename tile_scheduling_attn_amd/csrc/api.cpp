@@ -41,6 +41,7 @@ static int fail_hip(hipError_t e, const char* what) {
 }
 
 constexpr size_t kAlign = 256;
+constexpr size_t kHandoffBytes = 256 + 2 * 65536;  // flag words, then two 64 KiB tiles
 constexpr int kPadRows = 128;     // s is padded to a multiple of this
 constexpr int kMinTile = 64;      // smallest tile: bounds the flag count
 constexpr int kCounterWords = 64; // ticket + wait statistics
@@ -730,6 +731,41 @@ extern "C" int attn_bwd_atomic_rate(void* acc, size_t acc_bytes, int tasks, void
         return ATTN_OK;
     });
 }
+
+extern "C" int attn_bwd_handoff_latency(void* buf, size_t buf_bytes, int pong, int iters, int mode, void* stream,
+                                        double* ns, int* xcd_ping, int* xcd_pong) {
+    return guarded([&]() -> int {
+        if (ns) *ns = 0;
+        if (!buf || ((uintptr_t)buf & (kAlign - 1))) return fail(ATTN_ERR_INVALID_ARG, "buf must be a 256-byte aligned device pointer");
+        if (buf_bytes < kHandoffBytes) return fail(ATTN_ERR_INVALID_ARG, "buf smaller than attn_bwd_handoff_bytes");
+        if (pong < 1 || pong > 63) return fail(ATTN_ERR_INVALID_ARG, "pong must be in 1..63");
+        if (iters < 2 || iters > (1 << 20)) return fail(ATTN_ERR_INVALID_ARG, "iters must be in 2..2^20");
+        if (mode < 0 || mode > 2) return fail(ATTN_ERR_INVALID_ARG, "mode must be 0, 1 or 2");
+        int dev = 0, khz = 0;
+        hipError_t e = hipGetDevice(&dev);
+        if (e == hipSuccess) e = hipDeviceGetAttribute(&khz, hipDeviceAttributeWallClockRate, dev);
+        if (e != hipSuccess) return fail_hip(e, "device query");
+        if (khz <= 0) return fail(ATTN_ERR_HIP, "no constant-rate clock reported");
+        unsigned* words = static_cast<unsigned*>(buf);
+        float* tiles = reinterpret_cast<float*>(static_cast<char*>(buf) + 256);
+        e = hipMemsetAsync(words, 0, 256, (hipStream_t)stream);
+        if (e != hipSuccess) return fail_hip(e, "hipMemsetAsync");
+        int rc = launch_handoff(words, tiles, pong, iters, mode, stream);
+        if (rc != ATTN_OK) return rc;
+        unsigned h[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+        e = hipMemcpyAsync(h, words, sizeof(h), hipMemcpyDeviceToHost, (hipStream_t)stream);
+        if (e == hipSuccess) e = hipStreamSynchronize((hipStream_t)stream);
+        if (e != hipSuccess) return fail_hip(e, "hand-off result copy");
+        if (h[3]) return fail(ATTN_ERR_TIMEOUT, "a hand-off wait gave up");
+        if (xcd_ping) *xcd_ping = (int)h[1];
+        if (xcd_pong) *xcd_pong = (int)h[2];
+        const unsigned long long span = (unsigned long long)h[4] | ((unsigned long long)h[5] << 32);
+        if (ns) *ns = (double)span / khz * 1e6 / iters;
+        return ATTN_OK;
+    });
+}
+
+extern "C" size_t attn_bwd_handoff_bytes(void) { return kHandoffBytes; }
 
 extern "C" int attn_bwd_set_tile(int dtype, int tile) {
     return guarded([&]() -> int {

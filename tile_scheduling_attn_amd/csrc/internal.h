@@ -107,6 +107,9 @@ int status_word_address(unsigned** ptr);
 // fp32 atomic-add throughput kernel (tasks 128x128 tiles per work group into
 // acc, which holds ntiles such tiles)
 int launch_atomic_rate(float* acc, int ntiles, int grid, int tasks, void* stream);
+// dQ hand-off latency kernel between work group 0 and work group `pong`
+// (words: 8 u32 cleared by the caller; tiles: 2 x 64 KiB)
+int launch_handoff(unsigned* words, float* tiles, int pong, int iters, int mode, void* stream);
 
 // A device area that a call uses for every buffer it needs instead of
 // allocating (the no-allocation entry point): XCD probe words at its start
