@@ -42,6 +42,21 @@ notes):
     (KV_{n-1-p}, Q_{n-1+h-p-u}) (lower-right triangle from the bottom row up
     to the diagonal).  dQ_j is accumulated in step order.  Under the full
     mask the fold is empty and the schedule is Shift.
+  * Rectangular tiles (Br != Bc; the pages draw square tiles only), with
+    r = Bc / Br (`ratio` in the code): a KV tile of Bc rows and Q tiles of
+    Br rows, so a head
+    has n KV tiles and r*n Q tiles.  Q tile j sees KV tile i under the causal
+    mask when some key of the KV tile is at or before some query of the Q
+    tile: r*i <= j.  Naive and Descending keep their orders.  Shift: KV tile
+    i visits Q tiles (r*i + t) mod r*n, so at every step the items of a head
+    are on distinct Q tiles, and dQ_j is accumulated in visiting order.
+    Symmetric Shift (causal, n even, h = n/2): item p pairs KV p (Q tiles
+    r*p .. r*n-1) with KV n-1-p (Q tiles r*(n-1-p) .. r*n-1), n*r + r tasks
+    in all; phase 1 (t < r*h): (KV p, Q r*h + (r*p + t) mod r*h); phase 2
+    (u < r*h + r), with x = r*p + u: (KV p, Q x) while x < r*h, then
+    (KV n-1-p, Q 3*r*h - 1 - x).  At a fixed step x differs between items
+    and maps to distinct Q tiles, so the fold stays conflict-free; with r = 1
+    every rule above is the square one.
 """
 from __future__ import annotations
 
@@ -51,73 +66,81 @@ from itertools import permutations, product
 SCHEDULES = ("naive", "descending", "shift", "symmetric_shift")
 
 
-def allowed(causal: bool, kv: int, q: int) -> bool:
-    """Task (KV_kv, Q_q) exists unless the causal mask removes it (square
-    tiles, query tile q sees key tiles 0..q)."""
-    return (not causal) or kv <= q
+def allowed(causal: bool, kv: int, q: int, ratio: int = 1) -> bool:
+    """Task (KV_kv, Q_q) exists unless the causal mask removes it: with
+    `ratio` Q tiles per KV tile, query tile q sees key tiles
+    0..floor(q/ratio) (square tiles, ratio 1: key tiles 0..q)."""
+    return (not causal) or ratio * kv <= q
 
 
 # --------------------------------------------------------------------------
 # Schedule definitions for one head: work items and dQ accumulation orders.
 # --------------------------------------------------------------------------
-def head_items(name: str, n: int, causal: bool):
-    """Work items of one head, each an ordered list of (kv, q) tasks.  An item
-    runs start to finish on one SM; a KV tile never spans two items."""
+def head_items(name: str, n: int, causal: bool, ratio: int = 1):
+    """Work items of one head, each an ordered list of (kv, q) tasks, for n KV
+    tiles and ratio*n Q tiles.  An item runs start to finish on one SM; a KV tile
+    never spans two items."""
     if name == "symmetric_shift" and not causal:
         name = "shift"
+    nq = ratio * n
     if name == "naive":
-        return [[(i, j) for j in range(n) if allowed(causal, i, j)] for i in range(n)]
+        return [[(i, j) for j in range(nq) if allowed(causal, i, j, ratio)] for i in range(n)]
     if name == "descending":
-        return [[(i, j) for j in reversed(range(n)) if allowed(causal, i, j)] for i in range(n)]
+        return [[(i, j) for j in reversed(range(nq)) if allowed(causal, i, j, ratio)] for i in range(n)]
     if name == "shift":
-        return [[(i, (i + t) % n) for t in range(n) if allowed(causal, i, (i + t) % n)]
+        return [[(i, (ratio * i + t) % nq) for t in range(nq) if allowed(causal, i, (ratio * i + t) % nq, ratio)]
                 for i in range(n)]
     if name == "symmetric_shift":
         if n % 2:
-            raise ValueError("symmetric shift needs an even number of tiles")
+            raise ValueError("symmetric shift needs an even number of KV tiles")
         h = n // 2
         items = []
         for p in range(h):
-            tasks = [(p, h + (p + t) % h) for t in range(h)]
-            for u in range(h + 1):
-                if u < h - p:
-                    tasks.append((p, p + u))
+            tasks = [(p, ratio * h + (ratio * p + t) % (ratio * h)) for t in range(ratio * h)]
+            for u in range(ratio * h + ratio):
+                x = ratio * p + u
+                if x < ratio * h:
+                    tasks.append((p, x))
                 else:
-                    tasks.append((n - 1 - p, n - 1 + h - p - u))
+                    tasks.append((n - 1 - p, 3 * ratio * h - 1 - x))
             items.append(tasks)
         return items
     raise ValueError(f"unknown schedule {name!r}")
 
 
-def dq_orders(name: str, n: int, causal: bool, round_size=None):
-    """For each Q tile, the list of KV tiles in dQ accumulation order.
-    round_size (Shift only): KV tiles per round; None means one round."""
+def dq_orders(name: str, n: int, causal: bool, round_size=None, ratio: int = 1):
+    """For each of the ratio*n Q tiles, the list of KV tiles in dQ accumulation
+    order.  round_size (Shift, square tiles only): KV tiles per round; None
+    means one round."""
     if name == "symmetric_shift" and not causal:
         name = "shift"
+    nq = ratio * n
     if name in ("naive", "descending"):
-        return [[i for i in range(n) if allowed(causal, i, j)] for j in range(n)]
+        return [[i for i in range(n) if allowed(causal, i, j, ratio)] for j in range(nq)]
     if name == "shift":
+        if round_size and ratio != 1:
+            raise ValueError("Shift in rounds is defined for square tiles")
         w = round_size or n
         # round first (KV tile i is in round i // w), then the step at which
-        # KV tile i reaches Q tile j: (j - i) mod n
-        return [sorted((i for i in range(n) if allowed(causal, i, j)), key=lambda i: (i // w, (j - i) % n))
-                for j in range(n)]
+        # KV tile i reaches Q tile j: (j - ratio*i) mod ratio*n
+        return [sorted((i for i in range(n) if allowed(causal, i, j, ratio)), key=lambda i: (i // w, (j - ratio * i) % nq))
+                for j in range(nq)]
     if name == "symmetric_shift":
         # step order: position of each task inside its item
         step = {}
-        for tasks in head_items(name, n, causal):
+        for tasks in head_items(name, n, causal, ratio):
             for t, (kv, q) in enumerate(tasks):
                 step[(kv, q)] = t
-        return [sorted((i for i in range(n) if allowed(causal, i, j)),
-                       key=lambda i: step[(i, j)]) for j in range(n)]
+        return [sorted((i for i in range(n) if allowed(causal, i, j, ratio)),
+                       key=lambda i: step[(i, j)]) for j in range(nq)]
     raise ValueError(f"unknown schedule {name!r}")
 
 
-def rank_table(name: str, n: int, causal: bool, round_size=None):
+def rank_table(name: str, n: int, causal: bool, round_size=None, ratio: int = 1):
     """rank[kv][q] = position of KV tile kv in dQ_q's accumulation order, or
-    -1 for a masked task."""
-    rank = [[-1] * n for _ in range(n)]
-    for q, order in enumerate(dq_orders(name, n, causal, round_size)):
+    -1 for a masked task (n rows, ratio*n columns)."""
+    rank = [[-1] * (ratio * n) for _ in range(n)]
+    for q, order in enumerate(dq_orders(name, n, causal, round_size, ratio)):
         for pos, kv in enumerate(order):
             rank[kv][q] = pos
     return rank
@@ -178,11 +201,11 @@ def longest_path(weight, edges):
     return max(finish.values(), default=0), start, finish
 
 
-def place_static(name, n, causal, heads, sms, round_size=None):
+def place_static(name, n, causal, heads, sms, round_size=None, ratio=1):
     """Head-major items dealt round-robin to `sms` SMs, each SM running its
     items in increasing item order (one head's items are numbered in the
     order head_items lists them)."""
-    items = head_items(name, n, causal)
+    items = head_items(name, n, causal, ratio)
     sm_tasks = [[] for _ in range(sms)]
     g = 0
     for hd in range(heads):
@@ -190,29 +213,31 @@ def place_static(name, n, causal, heads, sms, round_size=None):
             sm_tasks[g % sms].extend((hd, kv, q) for kv, q in tasks)
             g += 1
     orders = {(hd, q): kvs for hd in range(heads)
-              for q, kvs in enumerate(dq_orders(name, n, causal, round_size))}
+              for q, kvs in enumerate(dq_orders(name, n, causal, round_size, ratio))}
     return sm_tasks, orders
 
 
-def makespan(name, n, causal, heads=1, sms=None, c=1, r=1, round_size=None):
+def makespan(name, n, causal, heads=1, sms=None, c=1, r=1, round_size=None, ratio=1):
     """Critical path of a schedule under static head-major placement on `sms`
-    SMs (default n).  None means deadlock."""
-    sm_tasks, orders = place_static(name, n, causal, heads, sms or n, round_size)
+    SMs (default n), with `ratio` Q tiles per KV tile.  None means
+    deadlock.  (r is the reduction cost, as in the pages' notation.)"""
+    sm_tasks, orders = place_static(name, n, causal, heads, sms or n, round_size, ratio)
     res = longest_path(*build_dag(sm_tasks, orders, c, r))
     return None if res is None else res[0]
 
 
-def brute_force_optimum(n, causal, c, r):
+def brute_force_optimum(n, causal, c, r, ratio=1):
     """Smallest makespan over every schedule of one head on n SMs with KV_i on
     SM i: every visiting order of each SM and every dQ accumulation order of
-    each Q tile (tiny n only)."""
-    per_sm = [[q for q in range(n) if allowed(causal, i, q)] for i in range(n)]
-    per_q = [[i for i in range(n) if allowed(causal, i, q)] for q in range(n)]
+    each of the ratio*n Q tiles (tiny n only)."""
+    nq = ratio * n
+    per_sm = [[q for q in range(nq) if allowed(causal, i, q, ratio)] for i in range(n)]
+    per_q = [[i for i in range(n) if allowed(causal, i, q, ratio)] for q in range(nq)]
     best = None
     for visit in product(*(list(permutations(x)) for x in per_sm)):
         sm_tasks = [[(0, i, q) for q in visit[i]] for i in range(n)]
         for red in product(*(list(permutations(x)) for x in per_q)):
-            orders = {(0, q): list(red[q]) for q in range(n)}
+            orders = {(0, q): list(red[q]) for q in range(nq)}
             res = longest_path(*build_dag(sm_tasks, orders, c, r))
             if res is not None and (best is None or res[0] < best):
                 best = res[0]
@@ -232,6 +257,21 @@ def closed_form_full_rounds(m, n, w, c, r):
     makespan is the total work over w SMs, m*(n/w)*n*(c+r); with w = n it
     is the pages' m*n*(c+r)."""
     return m * (n // w) * n * (c + r)
+
+
+def closed_form_full_rect(m, n, ratio, c, r):
+    """Full-mask Shift with `ratio` Q tiles per KV tile on n SMs: each SM
+    runs m*ratio*n tasks, and every Q tile's contributors arrive `ratio`
+    steps apart, so nothing waits: the total work per SM, m*ratio*n*(c+r)."""
+    return m * ratio * n * (c + r)
+
+
+def closed_form_causal_rect(m, n, ratio, c, r):
+    """Causal Symmetric Shift with `ratio` Q tiles per KV tile, m even, on n
+    SMs: every folded item has ratio*n + ratio tasks and each SM runs m/2 of
+    them, so the total work per SM is m*(ratio*n + ratio)*(c+r)/2 (ratio 1:
+    the pages' m*(n+1)*(c+r)/2)."""
+    return Fraction(m * (ratio * n + ratio)) * (c + r) / 2
 
 
 def closed_form_causal(m, n, c, r):

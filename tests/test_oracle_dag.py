@@ -206,3 +206,103 @@ def test_shift_rounds_need_a_whole_round_resident(n, w):
     w items must run at once: w SMs finish, w - 1 SMs deadlock."""
     assert dag.makespan("shift", n, False, sms=w, round_size=w) is not None
     assert dag.makespan("shift", n, False, sms=w - 1, round_size=w) is None
+
+
+# --------------------------------------------------------------------------
+# Rectangular tiles: `ratio` Q tiles of Br = Bc/ratio rows per KV tile of Bc
+# rows (Br != Bc).  The pins are coverage, KV contiguity, conflict-freedom,
+# the total-work bounds (each SM's task count times c + r) and brute force.
+# --------------------------------------------------------------------------
+RATIOS = [2, 3, 4]
+
+
+@pytest.mark.parametrize("ratio", RATIOS)
+@pytest.mark.parametrize("name", dag.SCHEDULES)
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("n", [1, 2, 3, 4, 6])
+def test_rect_schedule_covers_every_task_once_and_contiguously(ratio, name, causal, n):
+    if name == "symmetric_shift" and causal and n % 2:
+        with pytest.raises(ValueError):
+            dag.head_items(name, n, causal, ratio)
+        return
+    items = dag.head_items(name, n, causal, ratio)
+    tasks = [t for it in items for t in it]
+    # the causal mask by hand: KV tile i holds keys i*Bc .. i*Bc+Bc-1, Q tile
+    # j holds queries j*Br .. j*Br+Br-1 with Bc = ratio*Br; the task exists
+    # when the first key is at or before the last query
+    br = 4
+    bc = ratio * br
+    want = {(i, j) for i in range(n) for j in range(ratio * n) if not causal or i * bc <= j * br + br - 1}
+    assert len(tasks) == len(set(tasks)) and set(tasks) == want
+    for it in items:  # each KV tile's tasks are one contiguous run
+        kvs = [kv for kv, _ in it]
+        runs = [k for i, k in enumerate(kvs) if i == 0 or kvs[i - 1] != k]
+        assert len(runs) == len(set(runs))
+
+
+@pytest.mark.parametrize("ratio", RATIOS)
+@pytest.mark.parametrize("n", [2, 3, 5, 8])
+def test_rect_shift_is_conflict_free_with_contributions_ratio_steps_apart(ratio, n):
+    items = dag.head_items("shift", n, False, ratio)
+    for t in range(ratio * n):
+        qs = [it[t][1] for it in items]
+        assert len(qs) == len(set(qs))
+    step = {(kv, q): t for it in items for t, (kv, q) in enumerate(it)}
+    for q, order in enumerate(dag.dq_orders("shift", n, False, None, ratio)):
+        steps = [step[(kv, q)] for kv in order]
+        assert steps == sorted(steps) and all(b - a == ratio for a, b in zip(steps, steps[1:]))
+
+
+@pytest.mark.parametrize("ratio", RATIOS)
+@pytest.mark.parametrize("n", [2, 4, 6, 8])
+def test_rect_symmetric_shift_is_conflict_free_and_balanced(ratio, n):
+    items = dag.head_items("symmetric_shift", n, True, ratio)
+    assert len(items) == n // 2
+    assert all(len(it) == ratio * n + ratio for it in items)
+    for t in range(ratio * n + ratio):
+        qs = [it[t][1] for it in items]
+        assert len(qs) == len(set(qs))
+
+
+def test_rect_symmetric_shift_with_ratio_one_is_the_square_fold():
+    for n in (2, 4, 6, 8):
+        h = n // 2
+        square = []
+        for p in range(h):
+            tasks = [(p, h + (p + t) % h) for t in range(h)]
+            tasks += [(p, p + u) if u < h - p else (n - 1 - p, n - 1 + h - p - u) for u in range(h + 1)]
+            square.append(tasks)
+        assert dag.head_items("symmetric_shift", n, True, 1) == square
+
+
+@pytest.mark.parametrize("ratio", RATIOS)
+@pytest.mark.parametrize("m,n", [(1, 2), (2, 4), (3, 6)])
+@pytest.mark.parametrize("c,r", COSTS)
+def test_rect_shift_reaches_the_total_work_bound(ratio, m, n, c, r):
+    got = dag.makespan("shift", n, False, heads=m, sms=n, c=c, r=r, ratio=ratio)
+    assert got == dag.closed_form_full_rect(m, n, ratio, c, r) == m * ratio * n * (c + r)
+
+
+@pytest.mark.parametrize("ratio", RATIOS)
+@pytest.mark.parametrize("m,n", [(2, 2), (2, 4), (4, 6)])
+@pytest.mark.parametrize("c,r", COSTS)
+def test_rect_symmetric_shift_reaches_the_total_work_bound(ratio, m, n, c, r):
+    got = dag.makespan("symmetric_shift", n, True, heads=m, sms=n, c=c, r=r, ratio=ratio)
+    assert got == dag.closed_form_causal_rect(m, n, ratio, c, r)
+    # ratio 1 is the pages' causal figure
+    assert dag.closed_form_causal_rect(m, n, 1, c, r) == dag.closed_form_causal(m, n, c, r)
+
+
+@pytest.mark.parametrize("c,r", [(1, 1), (3, 1), (1, 3)])
+def test_rect_brute_force_full_mask_optimum_is_shift(c, r):
+    # n = 2 KV tiles, 4 Q tiles: every visiting and reduction order
+    best = dag.brute_force_optimum(2, False, c, r, ratio=2)
+    assert best == 4 * (c + r) == dag.makespan("shift", 2, False, c=c, r=r, ratio=2)
+
+
+def test_rect_brute_force_causal_n2():
+    # KV 0 sees Q 0..3, KV 1 sees Q 2..3: six tasks on two SMs, at least
+    # four on one of them
+    best = dag.brute_force_optimum(2, True, 1, 1, ratio=2)
+    assert best == 8
+    assert dag.makespan("naive", 2, True, c=1, r=1, ratio=2) >= best
