@@ -361,6 +361,24 @@ int attn_sched_get(int n, int causal, int schedule, int* item_begin, int* task_k
  * bad arguments. */
 int attn_sched_min_workers(int n, int causal, int schedule);
 
+/* Rectangular tiles: n KV tiles of Bc rows and ratio * n Q tiles of
+ * Br = Bc / ratio rows (ratio 1..8; ratio 1 is the square case above).  Q
+ * tile q sees KV tile kv under the causal mask when ratio * kv <= q.
+ * NAIVE and DESCENDING keep their orders; SHIFT visits Q tiles
+ * (ratio * kv + t) mod (ratio * n), so a head's items are on distinct Q tiles
+ * at every step, and accumulates dQ in visiting order (no rounds: n <= 256);
+ * SYMMETRIC_SHIFT (causal, n even) folds KV p with KV n-1-p into an item of
+ * ratio * n + ratio tasks: phase 1 (KV p, Q ratio*h + (ratio*p + t) mod
+ * (ratio*h)) for t < ratio*h, h = n/2; phase 2, with x = ratio*p + u for
+ * u < ratio*h + ratio: (KV p, Q x) while x < ratio*h, else (KV n-1-p,
+ * Q 3*ratio*h - 1 - x); dQ in step order.  rank: n * (ratio*n) ints,
+ * [kv * ratio*n + q]; count: ratio*n ints.  Same returns as the square
+ * calls. */
+int attn_sched_size_rect(int n, int ratio, int causal, int schedule, int* num_items, int* num_tasks);
+int attn_sched_get_rect(int n, int ratio, int causal, int schedule, int* item_begin, int* task_kv, int* task_q,
+                        int* rank, int* count);
+int attn_sched_min_workers_rect(int n, int ratio, int causal, int schedule);
+
 /* ------------------------------------------------------------------------
  * DAG critical-path simulator (host).  Models the pages' DAG: every task is
  * a compute phase of cost c followed by a reduction phase of cost r; the
@@ -390,6 +408,12 @@ int attn_dagsim(int n, int causal, int schedule, int heads, int workers, int pla
 int attn_dagsim_edge(int n, int causal, int schedule, int heads, int workers, int placement,
                      double c, double r, double e, double* makespan, double* wait_time,
                      double* busy_time);
+
+/* attn_dagsim_edge for rectangular tiles (n KV tiles, ratio Q tiles per KV
+ * tile, as for attn_sched_get_rect); c and r are the costs of one
+ * rectangular task. */
+int attn_dagsim_rect(int n, int ratio, int causal, int schedule, int heads, int workers, int placement,
+                     double c, double r, double e, double* makespan, double* wait_time, double* busy_time);
 
 /* ------------------------------------------------------------------------
  * Schedule selection (host).  The review page ("If this is right") calls the

@@ -285,3 +285,57 @@ def test_shift_rounds_simulate_to_the_total_work_bound():
     with pytest.raises(tsa.AttnError) as e:
         tsa.attn_dagsim(512, False, "shift", 1, 255, 1, c, r)
     assert e.value.code == -7
+
+
+# --------------------------------------------------------------------------
+# Rectangular tiles (n KV tiles, ratio Q tiles per KV tile)
+# --------------------------------------------------------------------------
+@pytest.mark.parametrize("ratio", [2, 3, 4])
+@pytest.mark.parametrize("name", SCHEDS + ("atomic",))
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("n", [1, 2, 3, 4, 6, 8, 16, 64])
+def test_rect_tables_match_oracle(ratio, name, causal, n):
+    if name == "symmetric_shift" and causal and n % 2:
+        with pytest.raises(tsa.AttnError) as e:
+            tsa.attn_sched_get_rect(n, ratio, causal, name)
+        assert e.value.code == -2
+        return
+    got = tsa.attn_sched_get_rect(n, ratio, causal, name)
+    items = dag.head_items("naive" if name == "atomic" else name, n, causal, ratio)
+    assert len(got["item_begin"]) == len(items) + 1
+    for x, tasks in enumerate(items):
+        a, b = got["item_begin"][x], got["item_begin"][x + 1]
+        assert list(zip(got["task_kv"][a:b].tolist(), got["task_q"][a:b].tolist())) == tasks
+    if name == "atomic":
+        assert (got["rank"] == -1).all()
+    else:
+        assert got["rank"].tolist() == dag.rank_table(name, n, causal, None, ratio)
+    assert got["count"].tolist() == [len(o) for o in dag.dq_orders("naive", n, causal, None, ratio)]
+    want_workers = 1 if name in ("naive", "descending", "atomic") else len(items)
+    assert tsa.lib.attn_sched_min_workers_rect(n, ratio, int(causal), tsa._sched_id(name)) == want_workers
+
+
+@pytest.mark.parametrize("ratio", [2, 4])
+@pytest.mark.parametrize("name", SCHEDS)
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("n,heads,workers", [(2, 1, 2), (4, 2, 4), (4, 3, 5), (6, 2, 6), (8, 4, 8)])
+@pytest.mark.parametrize("c,r", [(1, 1), (3, 1), (2.5, 0.25)])
+def test_rect_simulator_matches_oracle_critical_path(ratio, name, causal, n, heads, workers, c, r):
+    want = dag.makespan(name, n, causal, heads=heads, sms=workers, c=Fraction(c), r=Fraction(r), ratio=ratio)
+    if want is None:
+        with pytest.raises(tsa.AttnError) as e:
+            tsa.attn_dagsim_rect(n, ratio, causal, name, heads, workers, 0, c, r)
+        assert e.value.code == -7
+        return
+    got, wait, busy = tsa.attn_dagsim_rect(n, ratio, causal, name, heads, workers, 0, c, r)
+    assert got == float(want)
+    ntasks = heads * sum(1 for i in range(n) for j in range(ratio * n) if dag.allowed(causal, i, j, ratio))
+    assert busy == pytest.approx(ntasks * (c + r))
+
+
+def test_rect_shapes_outside_the_supported_range_are_refused():
+    assert tsa.lib.attn_sched_size_rect(4, 0, 0, 0, None, None) == -1       # ratio < 1
+    assert tsa.lib.attn_sched_size_rect(4, 9, 0, 0, None, None) == -2       # ratio > 8
+    assert tsa.lib.attn_sched_size_rect(300, 2, 0, 2, None, None) == -2     # Shift rounds are square only
+    assert tsa.lib.attn_sched_size_rect(1025, 2, 0, 0, None, None) == -2    # more than 2048 Q tiles
+    assert tsa.lib.attn_sched_size_rect(300, 2, 0, 0, None, None) == 0      # naive has no rounds

@@ -32,7 +32,8 @@ EXPORTS = ("attn_fwd", "attn_bwd_deterministic", "attn_bwd_deterministic_ex", "a
            "attn_sched_fit", "attn_bwd_get_call_times", "attn_bwd_get_clock", "attn_bwd_set_debug",
            "attn_bwd_resolve_schedule", "attn_bwd_deterministic_noalloc", "attn_bwd_noalloc_capacity",
            "attn_bwd_set_tile", "attn_bwd_atomic_rate", "attn_bwd_get_wait_hist",
-           "attn_bwd_handoff_latency", "attn_bwd_handoff_bytes")
+           "attn_bwd_handoff_latency", "attn_bwd_handoff_bytes", "attn_sched_size_rect", "attn_sched_get_rect",
+           "attn_sched_min_workers_rect", "attn_dagsim_rect")
 
 
 class AttnError(RuntimeError):
@@ -106,6 +107,14 @@ def _load():
     lib.attn_bwd_handoff_latency.restype = i
     lib.attn_bwd_handoff_bytes.argtypes = []
     lib.attn_bwd_handoff_bytes.restype = sz
+    lib.attn_sched_size_rect.argtypes = [i, i, i, i, ip, ip]
+    lib.attn_sched_size_rect.restype = i
+    lib.attn_sched_get_rect.argtypes = [i, i, i, i, ip, ip, ip, ip, ip]
+    lib.attn_sched_get_rect.restype = i
+    lib.attn_sched_min_workers_rect.argtypes = [i, i, i, i]
+    lib.attn_sched_min_workers_rect.restype = i
+    lib.attn_dagsim_rect.argtypes = [i, i, i, i, i, i, i, d, d, d, dp, dp, dp]
+    lib.attn_dagsim_rect.restype = i
     lib.attn_bwd_resolve_schedule.argtypes = [i] * 6
     lib.attn_bwd_resolve_schedule.restype = i
     lib.attn_bwd_deterministic_noalloc.argtypes = [vp] * 9 + [i] * 7 + [f, vp]
@@ -344,6 +353,33 @@ def attn_dagsim_edge(n, causal, schedule, heads, workers, placement, c, r, e):
     _check(lib.attn_dagsim_edge(n, int(causal), _sched_id(schedule), heads, workers, placement, float(c),
                                 float(r), float(e), ctypes.byref(m), ctypes.byref(w), ctypes.byref(b_)),
            "attn_dagsim_edge")
+    return m.value, w.value, b_.value
+
+
+def attn_sched_get_rect(n, ratio, causal, schedule):
+    """Rectangular tiles: n KV tiles, ratio Q tiles per KV tile.  Returns
+    dict of NumPy int32 arrays: item_begin, task_kv, task_q, rank
+    (n x ratio*n), count (ratio*n)."""
+    ni, nt = ctypes.c_int(), ctypes.c_int()
+    _check(lib.attn_sched_size_rect(n, ratio, int(causal), _sched_id(schedule), ctypes.byref(ni), ctypes.byref(nt)),
+           "attn_sched_size_rect")
+    out = {"item_begin": np.zeros(ni.value + 1, np.int32), "task_kv": np.zeros(nt.value, np.int32),
+           "task_q": np.zeros(nt.value, np.int32), "rank": np.zeros((n, ratio * n), np.int32),
+           "count": np.zeros(ratio * n, np.int32)}
+    P = lambda a: a.ctypes.data_as(ctypes.POINTER(ctypes.c_int))
+    _check(lib.attn_sched_get_rect(n, ratio, int(causal), _sched_id(schedule), P(out["item_begin"]),
+                                   P(out["task_kv"]), P(out["task_q"]), P(out["rank"]), P(out["count"])),
+           "attn_sched_get_rect")
+    return out
+
+
+def attn_dagsim_rect(n, ratio, causal, schedule, heads, workers, placement, c, r, e=0.0):
+    """attn_dagsim_edge for rectangular tiles.  Returns (makespan, wait_time,
+    busy_time); raises AttnError on deadlock."""
+    m, w, b_ = ctypes.c_double(), ctypes.c_double(), ctypes.c_double()
+    _check(lib.attn_dagsim_rect(n, ratio, int(causal), _sched_id(schedule), heads, workers, placement, float(c),
+                                float(r), float(e), ctypes.byref(m), ctypes.byref(w), ctypes.byref(b_)),
+           "attn_dagsim_rect")
     return m.value, w.value, b_.value
 
 

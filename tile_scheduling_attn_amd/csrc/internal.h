@@ -20,13 +20,14 @@ constexpr int kMaxWorkers = 1 << 20;
 
 // One head's schedule pattern (see attn_sched_get in attn_bwd.h).
 struct Schedule {
-    int n = 0;
+    int n = 0;                    // KV tiles (items' tiles)
+    int nq = 0;                   // Q tiles: ratio * n (n for square tiles)
     bool causal = false;
     int schedule = 0;
     std::vector<int> item_begin;  // num_items + 1
     std::vector<int> task_kv, task_q;
-    std::vector<int> rank;        // n*n, -1 = masked (or ATOMIC)
-    std::vector<int> count;       // n
+    std::vector<int> rank;        // [kv * nq + q], -1 = masked (or ATOMIC)
+    std::vector<int> count;       // nq: contributors per Q tile
     int round_size = 0;           // Shift: KV tiles per round (0: not Shift)
     int num_items() const { return (int)item_begin.size() - 1; }
 };
@@ -36,7 +37,8 @@ struct Schedule {
 // which wait on each other cyclically, always run together.
 constexpr int kShiftRound = 256;
 
-int build_schedule(int n, bool causal, int schedule, Schedule& out);
+// n KV tiles, `ratio` Q tiles per KV tile (Bc = ratio * Br; 1 = square tiles)
+int build_schedule(int n, bool causal, int schedule, Schedule& out, int ratio = 1);
 int min_workers(const Schedule& sc);
 int simulate(const Schedule& sc, int heads, int workers, int placement, double c, double r, double e,
              double* makespan, double* wait_time, double* busy_time);

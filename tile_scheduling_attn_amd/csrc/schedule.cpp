@@ -34,22 +34,28 @@
 
 namespace attn {
 
-static bool visible(bool causal, int kv, int q) { return !causal || kv <= q; }
+// Q tile q sees KV tile kv unless the causal mask removes every pair: with
+// `ratio` Q tiles per KV tile, when ratio * kv <= q
+static bool visible(bool causal, int kv, int q, int ratio) { return !causal || ratio * kv <= q; }
 
-int build_schedule(int n, bool causal, int schedule, Schedule& out) {
-    if (n < 0) return ATTN_ERR_INVALID_ARG;
-    if (n > kMaxTiles) return ATTN_ERR_UNSUPPORTED;
+int build_schedule(int n, bool causal, int schedule, Schedule& out, int ratio) {
+    if (n < 0 || ratio < 1) return ATTN_ERR_INVALID_ARG;
+    if (n > kMaxTiles || ratio > 8 || (long long)ratio * n > kMaxTiles) return ATTN_ERR_UNSUPPORTED;
     if (schedule < ATTN_SCHED_NAIVE || schedule > ATTN_SCHED_ATOMIC) return ATTN_ERR_INVALID_ARG;
     int kind = schedule;
     if (kind == ATTN_SCHED_SYMMETRIC_SHIFT && !causal) kind = ATTN_SCHED_SHIFT;  // empty fold
     if (kind == ATTN_SCHED_SYMMETRIC_SHIFT && (n % 2) != 0) return ATTN_ERR_UNSUPPORTED;
+    // rounds are defined for square tiles only
+    if (kind == ATTN_SCHED_SHIFT && ratio > 1 && n > kShiftRound) return ATTN_ERR_UNSUPPORTED;
+    const int nq = ratio * n;
 
     out = Schedule{};
     out.n = n;
+    out.nq = nq;
     out.causal = causal;
     out.schedule = schedule;
-    out.rank.assign((size_t)n * n, -1);
-    out.count.assign(n, 0);
+    out.rank.assign((size_t)n * nq, -1);
+    out.count.assign(nq, 0);
     out.item_begin.push_back(0);
 
     auto close_item = [&]() { out.item_begin.push_back((int)out.task_kv.size()); };
@@ -60,69 +66,73 @@ int build_schedule(int n, bool causal, int schedule, Schedule& out) {
 
     if (kind == ATTN_SCHED_NAIVE || kind == ATTN_SCHED_DESCENDING || kind == ATTN_SCHED_ATOMIC) {
         for (int kv = 0; kv < n; ++kv) {
-            for (int t = 0; t < n; ++t) {
-                int q = (kind == ATTN_SCHED_DESCENDING) ? n - 1 - t : t;
-                if (visible(causal, kv, q)) add(kv, q);
+            for (int t = 0; t < nq; ++t) {
+                int q = (kind == ATTN_SCHED_DESCENDING) ? nq - 1 - t : t;
+                if (visible(causal, kv, q, ratio)) add(kv, q);
             }
             close_item();
         }
         // ascending KV order inside every dQ tile
-        for (int q = 0; q < n; ++q) {
+        for (int q = 0; q < nq; ++q) {
             int pos = 0;
             for (int kv = 0; kv < n; ++kv)
-                if (visible(causal, kv, q)) out.rank[(size_t)kv * n + q] = pos++;
+                if (visible(causal, kv, q, ratio)) out.rank[(size_t)kv * nq + q] = pos++;
         }
     } else if (kind == ATTN_SCHED_SHIFT) {
         for (int kv = 0; kv < n; ++kv) {
-            for (int t = 0; t < n; ++t) {
-                int q = (kv + t) % n;
-                if (visible(causal, kv, q)) add(kv, q);
+            for (int t = 0; t < nq; ++t) {
+                int q = (ratio * kv + t) % nq;
+                if (visible(causal, kv, q, ratio)) add(kv, q);
             }
             close_item();
         }
-        // KV kv reaches Q q after (q - kv) mod n steps; the dQ order of q is
-        // the order in which its contributors visit it, round by round
+        // KV kv reaches Q q after (q - ratio * kv) mod nq steps; the dQ order
+        // of q is the order in which its contributors visit it, round by round
         const int rounds = (n + kShiftRound - 1) / kShiftRound;
         const int w = n > 0 ? (n + rounds - 1) / rounds : 0;
         out.round_size = w;
-        for (int q = 0; q < n; ++q) {
-            int pos = 0;
-            for (int rd = 0; rd < rounds; ++rd)
-                for (int t = 0; t < n; ++t) {
-                    int kv = ((q - t) % n + n) % n;
-                    if (kv / w == rd && visible(causal, kv, q)) out.rank[(size_t)kv * n + q] = pos++;
-                }
+        for (int q = 0; q < nq; ++q) {
+            std::vector<std::pair<int, int>> order;  // (round, step) of each contributor
+            for (int kv = 0; kv < n; ++kv)
+                if (visible(causal, kv, q, ratio)) order.push_back({(kv / w) * nq + ((q - ratio * kv) % nq + nq) % nq, kv});
+            std::sort(order.begin(), order.end());
+            for (size_t pos = 0; pos < order.size(); ++pos) out.rank[(size_t)order[pos].second * nq + q] = (int)pos;
         }
     } else {  // symmetric shift, causal, n even
-        const int h = n / 2;
-        std::vector<int> step((size_t)n * n, -1);
+        const int h = n / 2, rh = ratio * h;
+        std::vector<int> step((size_t)n * nq, -1);
         for (int p = 0; p < h; ++p) {
             int t = 0;
-            for (int u = 0; u < h; ++u, ++t) {
-                int q = h + (p + u) % h;
+            // phase 1: the dense block of Q tiles rh .. nq-1 against KV 0 .. h-1
+            for (int u = 0; u < rh; ++u, ++t) {
+                int q = rh + (ratio * p + u) % rh;
                 add(p, q);
-                step[(size_t)p * n + q] = t;
+                step[(size_t)p * nq + q] = t;
             }
-            for (int u = 0; u <= h; ++u, ++t) {
+            // phase 2: KV p from its diagonal up to Q rh-1, then KV n-1-p from
+            // the last Q tile back to its diagonal
+            for (int u = 0; u < rh + ratio; ++u, ++t) {
+                const int x = ratio * p + u;
                 int kv, q;
-                if (u < h - p) { kv = p; q = p + u; }
-                else { kv = n - 1 - p; q = n - 1 + h - p - u; }
+                if (x < rh) { kv = p; q = x; }
+                else { kv = n - 1 - p; q = 3 * rh - 1 - x; }
                 add(kv, q);
-                step[(size_t)kv * n + q] = t;
+                step[(size_t)kv * nq + q] = t;
             }
             close_item();
         }
-        for (int q = 0; q < n; ++q) {
+        for (int q = 0; q < nq; ++q) {
             std::vector<std::pair<int, int>> by_step;
-            for (int kv = 0; kv <= q; ++kv) by_step.push_back({step[(size_t)kv * n + q], kv});
+            for (int kv = 0; kv < n; ++kv)
+                if (visible(causal, kv, q, ratio)) by_step.push_back({step[(size_t)kv * nq + q], kv});
             std::sort(by_step.begin(), by_step.end());
             for (size_t pos = 0; pos < by_step.size(); ++pos)
-                out.rank[(size_t)by_step[pos].second * n + q] = (int)pos;
+                out.rank[(size_t)by_step[pos].second * nq + q] = (int)pos;
         }
     }
-    for (int q = 0; q < n; ++q)
+    for (int q = 0; q < nq; ++q)
         for (int kv = 0; kv < n; ++kv)
-            if (visible(causal, kv, q)) out.count[q]++;
+            if (visible(causal, kv, q, ratio)) out.count[q]++;
     if (schedule == ATTN_SCHED_ATOMIC) std::fill(out.rank.begin(), out.rank.end(), -1);
     return ATTN_OK;
 }
@@ -203,7 +213,8 @@ int simulate(const Schedule& sc, int heads, int workers, int placement, double c
         return ATTN_ERR_INVALID_ARG;
     if (workers > kMaxWorkers || (long long)heads * (long long)sc.task_kv.size() > kMaxSimTasks)
         return ATTN_ERR_UNSUPPORTED;
-    const int n = sc.n, items_per_head = sc.num_items();
+    // per-(head, Q tile) state: n is the Q tile count here
+    const int n = sc.nq, items_per_head = sc.num_items();
     const long long total_items = (long long)heads * items_per_head;
     const bool ordered = sc.schedule != ATTN_SCHED_ATOMIC;
 
@@ -351,23 +362,31 @@ int simulate(const Schedule& sc, int heads, int workers, int placement, double c
 
 }  // namespace attn
 
-extern "C" int attn_sched_size(int n, int causal, int schedule, int* num_items, int* num_tasks) {
+static const char* kSchedErr =
+    "invalid or unsupported schedule (n < 0, more than 2048 Q tiles, ratio outside 1..8, an odd n for the causal "
+    "fold, or ratio > 1 with more than 256 KV tiles under Shift)";
+
+extern "C" int attn_sched_size_rect(int n, int ratio, int causal, int schedule, int* num_items, int* num_tasks) {
     return attn::guarded([&]() -> int {
         attn::Schedule sc;
-        int rc = attn::build_schedule(n, causal != 0, schedule, sc);
-        if (rc != ATTN_OK) return attn::fail(rc, "attn_sched_size: invalid or unsupported schedule (n < 0, n > 2048, or an odd n for the causal fold)");
+        int rc = attn::build_schedule(n, causal != 0, schedule, sc, ratio);
+        if (rc != ATTN_OK) return attn::fail(rc, kSchedErr);
         if (num_items) *num_items = sc.num_items();
         if (num_tasks) *num_tasks = (int)sc.task_kv.size();
         return ATTN_OK;
     });
 }
 
-extern "C" int attn_sched_get(int n, int causal, int schedule, int* item_begin, int* task_kv,
-                              int* task_q, int* rank, int* count) {
+extern "C" int attn_sched_size(int n, int causal, int schedule, int* num_items, int* num_tasks) {
+    return attn_sched_size_rect(n, 1, causal, schedule, num_items, num_tasks);
+}
+
+extern "C" int attn_sched_get_rect(int n, int ratio, int causal, int schedule, int* item_begin, int* task_kv,
+                                   int* task_q, int* rank, int* count) {
     return attn::guarded([&]() -> int {
         attn::Schedule sc;
-        int rc = attn::build_schedule(n, causal != 0, schedule, sc);
-        if (rc != ATTN_OK) return attn::fail(rc, "attn_sched_get: invalid or unsupported schedule (n < 0, n > 2048, or an odd n for the causal fold)");
+        int rc = attn::build_schedule(n, causal != 0, schedule, sc, ratio);
+        if (rc != ATTN_OK) return attn::fail(rc, kSchedErr);
         if (item_begin) std::memcpy(item_begin, sc.item_begin.data(), sc.item_begin.size() * sizeof(int));
         if (task_kv) std::memcpy(task_kv, sc.task_kv.data(), sc.task_kv.size() * sizeof(int));
         if (task_q) std::memcpy(task_q, sc.task_q.data(), sc.task_q.size() * sizeof(int));
@@ -377,13 +396,22 @@ extern "C" int attn_sched_get(int n, int causal, int schedule, int* item_begin, 
     });
 }
 
-extern "C" int attn_sched_min_workers(int n, int causal, int schedule) {
+extern "C" int attn_sched_get(int n, int causal, int schedule, int* item_begin, int* task_kv,
+                              int* task_q, int* rank, int* count) {
+    return attn_sched_get_rect(n, 1, causal, schedule, item_begin, task_kv, task_q, rank, count);
+}
+
+extern "C" int attn_sched_min_workers_rect(int n, int ratio, int causal, int schedule) {
     return attn::guarded([&]() -> int {
         attn::Schedule sc;
-        int rc = attn::build_schedule(n, causal != 0, schedule, sc);
-        if (rc != ATTN_OK) return attn::fail(rc, "attn_sched_min_workers: invalid or unsupported schedule (n < 0, n > 2048, or an odd n for the causal fold)");
+        int rc = attn::build_schedule(n, causal != 0, schedule, sc, ratio);
+        if (rc != ATTN_OK) return attn::fail(rc, kSchedErr);
         return attn::min_workers(sc);
     });
+}
+
+extern "C" int attn_sched_min_workers(int n, int causal, int schedule) {
+    return attn_sched_min_workers_rect(n, 1, causal, schedule);
 }
 
 extern "C" int attn_dagsim(int n, int causal, int schedule, int heads, int workers, int placement,
@@ -395,18 +423,25 @@ extern "C" int attn_dagsim(int n, int causal, int schedule, int heads, int worke
     });
 }
 
-extern "C" int attn_dagsim_edge(int n, int causal, int schedule, int heads, int workers, int placement,
+extern "C" int attn_dagsim_rect(int n, int ratio, int causal, int schedule, int heads, int workers, int placement,
                                 double c, double r, double e, double* makespan, double* wait_time,
                                 double* busy_time) {
     return attn::guarded([&]() -> int {
         attn::Schedule sc;
-        int rc = attn::build_schedule(n, causal != 0, schedule, sc);
-        if (rc != ATTN_OK) return attn::fail(rc, "attn_dagsim: invalid or unsupported schedule (n < 0, n > 2048, or an odd n for the causal fold)");
+        int rc = attn::build_schedule(n, causal != 0, schedule, sc, ratio);
+        if (rc != ATTN_OK) return attn::fail(rc, kSchedErr);
         rc = attn::simulate(sc, heads, workers, placement, c, r, e, makespan, wait_time, busy_time);
         if (rc == ATTN_ERR_DEADLOCK) return attn::fail(rc, "attn_dagsim: the schedule deadlocks with this many workers");
         if (rc != ATTN_OK) return attn::fail(rc, "attn_dagsim: invalid arguments, or more heads * tasks or workers than the simulator accepts");
         return ATTN_OK;
     });
+}
+
+extern "C" int attn_dagsim_edge(int n, int causal, int schedule, int heads, int workers, int placement,
+                                double c, double r, double e, double* makespan, double* wait_time,
+                                double* busy_time) {
+    return attn_dagsim_rect(n, 1, causal, schedule, heads, workers, placement, c, r, e, makespan, wait_time,
+                            busy_time);
 }
 
 // ---------------------------------------------------------------------------
