@@ -182,8 +182,8 @@ int attn_bwd_query_status(void* stream);
  * The string is owned by the library and valid until the next call. */
 const char* attn_bwd_last_error(void);
 
-/* Tile edge T the backward uses for `dtype` (bf16: 128 unless
- * attn_bwd_set_tile chose 64; fp32: 64). */
+/* KV tile rows Bc the backward uses for `dtype` (bf16: 128 unless
+ * attn_bwd_set_tile or attn_bwd_set_tile_shape chose 64; fp32: 64). */
 int attn_bwd_tile_size(int dtype);
 
 /* Tile granularity of later bf16 calls (review page, "What would settle it"
@@ -196,6 +196,25 @@ int attn_bwd_tile_size(int dtype);
  * and so the bits, never determinism.  Returns ATTN_OK,
  * ATTN_ERR_UNSUPPORTED (dtype not bf16) or ATTN_ERR_INVALID_ARG. */
 int attn_bwd_set_tile(int dtype, int tile);
+
+/* Rectangular tiles for later bf16 calls: Q tiles of Br rows against KV
+ * tiles of Bc rows (the survey's variable tile shapes: Br != Bc; the pages
+ * draw square tiles).  (Br, Bc) = (128, 128) (the default; (0, 0) selects
+ * it), (64, 64), or (64, 128): then every KV tile meets ratio = 2 Q tiles
+ * of its rows, the schedules run over n = ceil(s/Bc) KV tiles and 2n Q
+ * tiles as attn_sched_get_rect defines them (Symmetric Shift folds KV p
+ * with KV n-1-p into 2n + 2 tasks), the kernel takes one 64-row sub-step
+ * per task and accumulates dQ per 64-row Q tile.  The ordered dQ traffic,
+ * s^2 * d * 8 / Bc bytes per head, depends on Bc alone, so it is that of the
+ * square 128-row tiles (and half that of the 64-row ones), with twice their
+ * tasks and flag hand-offs.  attn_bwd_set_tile(dtype, T)
+ * equals attn_bwd_set_tile_shape(dtype, T, T).  Returns ATTN_OK,
+ * ATTN_ERR_UNSUPPORTED (dtype not bf16) or ATTN_ERR_INVALID_ARG. */
+int attn_bwd_set_tile_shape(int dtype, int br, int bc);
+
+/* The (Br, Bc) tile shape the backward uses for `dtype`; either pointer may
+ * be NULL.  Returns ATTN_OK or ATTN_ERR_INVALID_ARG (unknown dtype). */
+int attn_bwd_tile_shape(int dtype, int* br, int* bc);
 
 /* Kernel timing.  attn_bwd_set_timing(1) starts a recording: every later
  * backward call (up to 4096) records HIP events on its own stream around

@@ -272,3 +272,17 @@ def test_handoff_latency_validates_arguments_before_any_gpu_call():
     assert r(ctypes.c_void_p(256), n, 64, 100, 0, None, None, None, None) == -1
     assert r(ctypes.c_void_p(256), n, 8, 1, 0, None, None, None, None) == -1           # one turn
     assert r(ctypes.c_void_p(256), n, 8, 100, 3, None, None, None, None) == -1         # unknown mode
+
+
+def test_set_tile_shape_validates_and_restores_the_default():
+    assert tsa.lib.attn_bwd_set_tile_shape(1, 64, 128) == -2      # fp32 has no choice
+    for br, bc in ((128, 64), (32, 128), (64, 256), (96, 96)):
+        assert tsa.lib.attn_bwd_set_tile_shape(0, br, bc) == -1
+    assert tsa.lib.attn_bwd_set_tile_shape(0, 64, 128) == 0
+    assert tsa.attn_bwd_tile_shape("bf16") == (64, 128)
+    assert tsa.attn_bwd_tile_size("bf16") == 128                   # the KV tile
+    assert tsa.lib.attn_bwd_set_tile(0, 64) == 0                   # square 64 x 64
+    assert tsa.attn_bwd_tile_shape("bf16") == (64, 64)
+    assert tsa.lib.attn_bwd_set_tile_shape(0, 0, 0) == 0
+    assert tsa.attn_bwd_tile_shape("bf16") == (128, 128)
+    assert tsa.attn_bwd_tile_shape("fp32") == (64, 64)

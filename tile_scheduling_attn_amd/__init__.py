@@ -33,7 +33,7 @@ EXPORTS = ("attn_fwd", "attn_bwd_deterministic", "attn_bwd_deterministic_ex", "a
            "attn_bwd_resolve_schedule", "attn_bwd_deterministic_noalloc", "attn_bwd_noalloc_capacity",
            "attn_bwd_set_tile", "attn_bwd_atomic_rate", "attn_bwd_get_wait_hist",
            "attn_bwd_handoff_latency", "attn_bwd_handoff_bytes", "attn_sched_size_rect", "attn_sched_get_rect",
-           "attn_sched_min_workers_rect", "attn_dagsim_rect")
+           "attn_sched_min_workers_rect", "attn_dagsim_rect", "attn_bwd_set_tile_shape", "attn_bwd_tile_shape")
 
 
 class AttnError(RuntimeError):
@@ -115,6 +115,10 @@ def _load():
     lib.attn_sched_min_workers_rect.restype = i
     lib.attn_dagsim_rect.argtypes = [i, i, i, i, i, i, i, d, d, d, dp, dp, dp]
     lib.attn_dagsim_rect.restype = i
+    lib.attn_bwd_set_tile_shape.argtypes = [i, i, i]
+    lib.attn_bwd_set_tile_shape.restype = i
+    lib.attn_bwd_tile_shape.argtypes = [i, ip, ip]
+    lib.attn_bwd_tile_shape.restype = i
     lib.attn_bwd_resolve_schedule.argtypes = [i] * 6
     lib.attn_bwd_resolve_schedule.restype = i
     lib.attn_bwd_deterministic_noalloc.argtypes = [vp] * 9 + [i] * 7 + [f, vp]
@@ -208,6 +212,21 @@ def attn_bwd_set_tile(dtype, tile) -> None:
     """Tile edge of later bf16 calls: 128 (default, or 0) or 64."""
     dt = DTYPES[dtype] if isinstance(dtype, str) else int(dtype)
     _check(lib.attn_bwd_set_tile(dt, int(tile)), "attn_bwd_set_tile")
+
+
+def attn_bwd_set_tile_shape(dtype, br, bc) -> None:
+    """Q tile rows Br and KV tile rows Bc of later bf16 calls: (128, 128)
+    (default, or (0, 0)), (64, 64) or (64, 128)."""
+    dt = DTYPES[dtype] if isinstance(dtype, str) else int(dtype)
+    _check(lib.attn_bwd_set_tile_shape(dt, int(br), int(bc)), "attn_bwd_set_tile_shape")
+
+
+def attn_bwd_tile_shape(dtype):
+    """(Br, Bc) of later calls in `dtype`."""
+    dt = DTYPES[dtype] if isinstance(dtype, str) else int(dtype)
+    br, bc = ctypes.c_int(), ctypes.c_int()
+    _check(lib.attn_bwd_tile_shape(dt, ctypes.byref(br), ctypes.byref(bc)), "attn_bwd_tile_shape")
+    return br.value, bc.value
 
 
 def attn_bwd_set_timing(on: bool) -> int:

@@ -99,7 +99,7 @@ struct DevState {
     void* ws_stream = nullptr;
     bool ws_used = false;
     unsigned* status = nullptr;
-    std::map<std::tuple<int, int, int>, DevSchedule> schedules;
+    std::map<std::tuple<int, int, int, int>, DevSchedule> schedules;
     // ATTN_SCHED_AUTO: the schedule picked per (n, causal, heads, d, dtype)
     std::map<std::tuple<int, int, long long, int, int>, int> auto_pick;
     // kernel timing: 4 events per recorded call (before preprocess, before
@@ -148,8 +148,10 @@ static int dev_init(int dev, DevState& ds, void* probe_buf = nullptr) {
 
 // The schedule tables of (n, mask, schedule), built once per device and
 // cached; `upload` also makes the device copy (an allocation).
-static int get_schedule(DevState& ds, int n, bool causal, int schedule, DevSchedule** out, bool upload = true) {
-    auto key = std::make_tuple(n, (int)causal, schedule);
+// n KV tiles, `ratio` Q tiles per KV tile.
+static int get_schedule(DevState& ds, int n, int ratio, bool causal, int schedule, DevSchedule** out,
+                        bool upload = true) {
+    auto key = std::make_tuple(n, ratio, (int)causal, schedule);
     auto it = ds.schedules.find(key);
     if (it != ds.schedules.end()) {
         DevSchedule& d = it->second;
@@ -166,22 +168,24 @@ static int get_schedule(DevState& ds, int n, bool causal, int schedule, DevSched
         return ATTN_OK;
     }
     Schedule sc;
-    int rc = build_schedule(n, causal, schedule, sc);
+    int rc = build_schedule(n, causal, schedule, sc, ratio);
     if (rc == ATTN_ERR_UNSUPPORTED)
-        return fail(rc, "symmetric shift under the causal mask needs an even number of tiles");
+        return fail(rc, "unsupported schedule shape (symmetric shift under the causal mask needs an even number of "
+                        "KV tiles; rectangular tiles allow at most 256 KV tiles under Shift and 2048 Q tiles)");
     if (rc != ATTN_OK) return fail(rc, "invalid schedule");
+    const int nq = sc.nq;
     std::vector<int> host(sc.item_begin.begin(), sc.item_begin.end());
     host.resize((host.size() + 3) / 4 * 4, 0);
     // item that makes contribution `rank` to Q tile q: item_of[q * n + rank]
-    std::vector<int> item_of((size_t)n * n, -1);
+    std::vector<int> item_of((size_t)nq * n, -1);
     for (int it = 0; it < sc.num_items(); ++it)
         for (int t = sc.item_begin[it]; t < sc.item_begin[it + 1]; ++t) {
-            const int r = sc.rank[(size_t)sc.task_kv[t] * n + sc.task_q[t]];
+            const int r = sc.rank[(size_t)sc.task_kv[t] * nq + sc.task_q[t]];
             if (r >= 0) item_of[(size_t)sc.task_q[t] * n + r] = it;
         }
     for (size_t t = 0; t < sc.task_kv.size(); ++t) {
         const int kv = sc.task_kv[t], q = sc.task_q[t];
-        const int r = sc.rank[(size_t)kv * n + q];
+        const int r = sc.rank[(size_t)kv * nq + q];
         host.push_back(kv);
         host.push_back(q);
         host.push_back(r);
@@ -201,16 +205,27 @@ static int get_schedule(DevState& ds, int n, bool causal, int schedule, DevSched
     d.items = sc.num_items();
     d.item_begin = sc.item_begin;
     d.tasks = (int)sc.task_kv.size();
-    d.n = n;
+    d.n = nq;
     d.min_workers = min_workers(sc);
     auto res = ds.schedules.emplace(key, d);
     *out = &res.first->second;
     return ATTN_OK;
 }
 
-// Tile edge of later bf16 calls (attn_bwd_set_tile): 128 by default, or 64.
-static std::atomic<int> g_tile_bf16{128};
-static int tile_for(int dtype) { return dtype == ATTN_FP32 ? 64 : g_tile_bf16.load(); }
+// Tile shape of later bf16 calls (attn_bwd_set_tile, attn_bwd_set_tile_shape):
+// Q tile rows Br in the high half, KV tile rows Bc in the low half; 128 x 128
+// by default, or 64 x 64, or 64 x 128.  fp32 runs 64 x 64.
+static std::atomic<int> g_shape_bf16{(128 << 16) | 128};
+struct TileShape {
+    int br, bc;
+    int ratio() const { return bc / br; }
+};
+static TileShape shape_for(int dtype) {
+    if (dtype == ATTN_FP32) return {64, 64};
+    const int v = g_shape_bf16.load();
+    return {v >> 16, v & 0xffff};
+}
+static int tile_for(int dtype) { return shape_for(dtype).bc; }
 
 // Task costs of the DAG model fitted to this kernel on MI355X (microseconds
 // per compute phase c and reduction phase r, and per reduction hand-off e
@@ -223,9 +238,13 @@ static int tile_for(int dtype) { return dtype == ATTN_FP32 ? 64 : g_tile_bf16.lo
 struct FittedCosts {
     double c, r, e;
 };
-static FittedCosts fitted_costs(int d, int tile) {
-    if (tile == 64) return d == 64 ? FittedCosts{0.392, 1.845, 0.0} : FittedCosts{1.185, 2.996, 0.711};
-    return d == 64 ? FittedCosts{3.115, 2.273, 0.0} : FittedCosts{3.297, 3.775, 2.904};
+static FittedCosts fitted_costs(int d, TileShape t) {
+    if (t.bc == 64) return d == 64 ? FittedCosts{0.392, 1.845, 0.0} : FittedCosts{1.185, 2.996, 0.711};
+    const FittedCosts f = d == 64 ? FittedCosts{3.115, 2.273, 0.0} : FittedCosts{3.297, 3.775, 2.904};
+    // 64-row Q tiles against 128-row KV tiles: half the matrix work and half
+    // the accumulator bytes of a square task (no fit of their own)
+    if (t.br != t.bc) return {f.c * t.br / t.bc, f.r * t.br / t.bc, f.e};
+    return f;
 }
 
 // ATTN_SCHED_AUTO.  The review page ("If this is right") has an
@@ -234,20 +253,21 @@ static FittedCosts fitted_costs(int d, int tile) {
 // XCD placement simulates every deterministic schedule the shape admits on
 // the device's resident work groups and takes the shortest makespan.
 static int resolve_auto(DevState& ds, int n, bool causal, long long H, int d, int dtype, int* out) {
-    const auto key = std::make_tuple(n, (int)causal, H, d, dtype * 1000 + tile_for(dtype));
+    const TileShape shape = shape_for(dtype);
+    const auto key = std::make_tuple(n, (int)causal, H, d, (dtype * 1000 + shape.br) * 1000 + shape.bc);
     auto it = ds.auto_pick.find(key);
     if (it != ds.auto_pick.end()) {
         *out = it->second;
         return ATTN_OK;
     }
-    const FittedCosts fc = fitted_costs(d, tile_for(dtype));
+    const FittedCosts fc = fitted_costs(d, shape);
     const int workers = std::max(1, ds.num_cus);
     const int heads = (int)std::min<long long>(H, 1 << 20);
     int pick = -1;
     double best = 0;
     for (int sc : {ATTN_SCHED_NAIVE, ATTN_SCHED_DESCENDING, ATTN_SCHED_SHIFT, ATTN_SCHED_SYMMETRIC_SHIFT}) {
         Schedule sch;
-        if (build_schedule(n, causal, sc, sch) != ATTN_OK) continue;
+        if (build_schedule(n, causal, sc, sch, shape.ratio()) != ATTN_OK) continue;
         if (min_workers(sch) > workers) continue;
         // large problems: simulate a head count that keeps the simulation
         // small but fills every worker several times (the makespan per head
@@ -306,9 +326,11 @@ int backward(const void* q, const void* k, const void* v, const void* o, const v
     if (workspace && ((uintptr_t)workspace & (kAlign - 1)))
         return fail(ATTN_ERR_INVALID_ARG, "workspace must be 256-byte aligned");
 
-    const int tile = tile_for(dtype);
-    // at most kMaxTiles at 128-row tiles; 64-row tiles can exceed it, which
-    // build_schedule rejects as unsupported
+    const TileShape shape = shape_for(dtype);
+    const int tile = shape.bc, ratio = shape.ratio();
+    // KV tiles; the Q tiles are ratio * n (at most kMaxTiles at 128-row
+    // tiles; smaller tiles can exceed it, which build_schedule rejects as
+    // unsupported)
     const int n = (s + tile - 1) / tile;
 
     std::lock_guard<std::mutex> lock(g_mutex);
@@ -323,7 +345,7 @@ int backward(const void* q, const void* k, const void* v, const void* o, const v
         if (rc != ATTN_OK) return rc;
     }
     DevSchedule* sch = nullptr;
-    rc = get_schedule(ds, n, causal != 0, schedule, &sch, na == nullptr);
+    rc = get_schedule(ds, n, ratio, causal != 0, schedule, &sch, na == nullptr);
     if (rc != ATTN_OK) return rc;
     int* table = sch->buf;
     if (na) {
@@ -384,7 +406,7 @@ int backward(const void* q, const void* k, const void* v, const void* o, const v
     BwdArgs a{};
     a.q = q; a.k = k; a.v = v; a.o = o; a.dO = dO; a.lse = lse;
     a.dq = dq; a.dk = dk; a.dv = dv;
-    a.H = (int)H; a.s = s; a.d = d; a.n = n; a.tile = tile;
+    a.H = (int)H; a.s = s; a.d = d; a.n = n * ratio; a.tile = tile; a.br = shape.br;
     a.causal = causal != 0;
     a.schedule = schedule;
     a.dtype = dtype;
@@ -506,7 +528,7 @@ extern "C" size_t attn_bwd_workspace_bytes(int b, int h, int s, int d, int causa
         WsLayout wl;
         if (!ws_layout(H, s, d, H, wl)) return 0;
         size_t total = wl.total;
-        // what XCD placement needs on the current device (either tile edge)
+        // what XCD placement needs on the current device (any tile shape)
         if (H > 0 && s > 0 && (causal == 0 || causal == 1) && schedule >= ATTN_SCHED_NAIVE &&
             schedule <= ATTN_SCHED_AUTO && schedule != ATTN_SCHED_ATOMIC) {
             std::lock_guard<std::mutex> lock(g_mutex);
@@ -514,13 +536,13 @@ extern "C" size_t attn_bwd_workspace_bytes(int b, int h, int s, int d, int causa
             if (hipGetDevice(&dev) == hipSuccess) {
                 DevState& ds = g_dev[dev];
                 if (dev_init(dev, ds) == ATTN_OK) {
-                    for (int tile : {64, 128})
+                    for (const TileShape t : {TileShape{64, 64}, TileShape{128, 128}, TileShape{64, 128}})
                     for (int sched = ATTN_SCHED_NAIVE; sched < ATTN_SCHED_ATOMIC; ++sched) {
                         // AUTO may resolve to any deterministic schedule
                         if (schedule != ATTN_SCHED_AUTO && sched != schedule) continue;
-                        const int n = (s + tile - 1) / tile;
+                        const int n = (s + t.bc - 1) / t.bc;
                         Schedule sc;
-                        if (build_schedule(n, causal != 0, sched, sc) != ATTN_OK) continue;
+                        if (build_schedule(n, causal != 0, sched, sc, t.ratio()) != ATTN_OK) continue;
                         DevSchedule shape;
                         shape.items = sc.num_items();
                         shape.item_begin = sc.item_begin;
@@ -767,13 +789,35 @@ extern "C" int attn_bwd_handoff_latency(void* buf, size_t buf_bytes, int pong, i
 
 extern "C" size_t attn_bwd_handoff_bytes(void) { return kHandoffBytes; }
 
+extern "C" int attn_bwd_set_tile_shape(int dtype, int br, int bc) {
+    return guarded([&]() -> int {
+        if (dtype != ATTN_BF16)
+            return fail(ATTN_ERR_UNSUPPORTED, "attn_bwd_set_tile_shape: only bf16 has a choice of tile");
+        if (br == 0 && bc == 0) br = bc = 128;
+        if (!((br == 128 && bc == 128) || (br == 64 && bc == 64) || (br == 64 && bc == 128)))
+            return fail(ATTN_ERR_INVALID_ARG,
+                        "attn_bwd_set_tile_shape: (Br, Bc) must be (0, 0) (default), (128, 128), (64, 64) or (64, 128)");
+        std::lock_guard<std::mutex> lock(g_mutex);
+        g_shape_bf16 = (br << 16) | bc;
+        return ATTN_OK;
+    });
+}
+
 extern "C" int attn_bwd_set_tile(int dtype, int tile) {
     return guarded([&]() -> int {
         if (dtype != ATTN_BF16) return fail(ATTN_ERR_UNSUPPORTED, "attn_bwd_set_tile: only bf16 has a choice of tile");
         if (tile != 0 && tile != 64 && tile != 128)
             return fail(ATTN_ERR_INVALID_ARG, "attn_bwd_set_tile: tile must be 0 (default), 64 or 128");
-        std::lock_guard<std::mutex> lock(g_mutex);
-        g_tile_bf16 = tile == 0 ? 128 : tile;
+        return attn_bwd_set_tile_shape(dtype, tile, tile);
+    });
+}
+
+extern "C" int attn_bwd_tile_shape(int dtype, int* br, int* bc) {
+    return guarded([&]() -> int {
+        if (dtype != ATTN_BF16 && dtype != ATTN_FP32) return fail(ATTN_ERR_INVALID_ARG, "unknown dtype");
+        const TileShape t = shape_for(dtype);
+        if (br) *br = t.br;
+        if (bc) *bc = t.bc;
         return ATTN_OK;
     });
 }

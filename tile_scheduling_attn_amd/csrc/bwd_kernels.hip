@@ -108,7 +108,10 @@ int probe_xcd_dispatch(int num_cus, bool* ok, unsigned* buf) {
     return ATTN_OK;
 }
 
-template <typename T, int TILE>
+// bf16 d = 64 main kernels (bwd_kernels_d64.hip) for Q tiles of br rows
+int launch_main_bf16_d64_rect(const KParams& kp, const BwdLaunch& L, bool causal, bool det);
+
+template <typename T, int TILE, int BR = TILE>
 static int launch_all(const BwdArgs& a, const BwdLaunch& L, KParams& kp) {
     const T* o = static_cast<const T*>(a.o);
     const T* dO = static_cast<const T*>(a.dO);
@@ -135,15 +138,17 @@ static int launch_all(const BwdArgs& a, const BwdLaunch& L, KParams& kp) {
     // Symmetric Shift (causal; under the full mask it runs Shift) with dS as
     // [key][query] at d = 128 (measured: 8% faster at s = 8192; at d = 64,
     // s = 2048 the row layout is 3% faster)
-    const bool dst = a.schedule == ATTN_SCHED_SYMMETRIC_SHIFT;
+    const bool dst = a.schedule == ATTN_SCHED_SYMMETRIC_SHIFT && BR == TILE;
     int rc;
     if (a.d == 64) {
-        if constexpr (sizeof(T) == 2)
+        if constexpr (sizeof(T) == 2 && BR != TILE)
+            rc = launch_main_bf16_d64_rect(kp, L, a.causal, det);
+        else if constexpr (sizeof(T) == 2)
             rc = launch_main_bf16_d64(kp, L, a.causal, det, TILE);
         else
             rc = launch_main_d<T, 64, TILE>(kp, L, a.causal, det, dst);
     } else {
-        rc = launch_main_d<T, 128, TILE>(kp, L, a.causal, det, dst);
+        rc = launch_main_d<T, 128, TILE, BR>(kp, L, a.causal, det, dst);
     }
     if (rc != ATTN_OK) return rc;
     if (L.ev && hipEventRecord((hipEvent_t)L.ev[2], st) != hipSuccess) return fail(ATTN_ERR_HIP, "hipEventRecord failed");
@@ -189,7 +194,13 @@ int launch_backward(const BwdArgs& a, const BwdLaunch& L) {
     kp.spin_limit = L.spin_limit ? L.spin_limit : kSpinLimit;
     kp.wait_offset = L.wait_offset;
     kp.delay_seed = L.delay_seed;
-    if (a.dtype == ATTN_BF16) return a.tile == 64 ? launch_all<bf16, 64>(a, L, kp) : launch_all<bf16, 128>(a, L, kp);
+    if (a.dtype == ATTN_BF16) {
+        if (a.tile == 64 && a.br == 64) return launch_all<bf16, 64>(a, L, kp);
+        if (a.tile == 128 && a.br == 64) return launch_all<bf16, 128, 64>(a, L, kp);
+        if (a.tile == 128 && a.br == 128) return launch_all<bf16, 128>(a, L, kp);
+        return fail(ATTN_ERR_UNSUPPORTED, "bf16 tile shape must be 128x128, 64x64 or 64x128 (Br x Bc)");
+    }
+    if (a.tile != 64 || a.br != 64) return fail(ATTN_ERR_UNSUPPORTED, "fp32 tiles are 64x64");
     return launch_all<float, 64>(a, L, kp);
 }
 

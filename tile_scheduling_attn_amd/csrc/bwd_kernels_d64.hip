@@ -15,4 +15,9 @@ int launch_main_bf16_d64(const KParams& kp, const BwdLaunch& L, bool causal, boo
     return launch_main_d<bf16, 64, 128>(kp, L, causal, det, false);
 }
 
+// 64-row Q tiles against 128-row KV tiles
+int launch_main_bf16_d64_rect(const KParams& kp, const BwdLaunch& L, bool causal, bool det) {
+    return launch_main_d<bf16, 64, 128, 64>(kp, L, causal, det, false);
+}
+
 }  // namespace attn

@@ -131,13 +131,16 @@ struct KParams {
 // LDS of one work group:
 //   sQ[2], sdO[2]  padded [BQ][D]   query rows of a sub-step (double buffer)
 //   sK             padded [TILE][D] keys of the current KV tile (dQ operand)
-//   sdS            [TILE][TILE] (+pad) dS of the current task as [query][key], or
-//                  (DST, bf16 only) as [key][query]: a lane's four query rows of
-//                  one key are then 8 contiguous bytes, one 64-bit store
+//   sdS            [BR][TILE] (+pad) dS of the current task as [query][key], or
+//                  (DST, bf16 and square tiles only) as [key][query]: a lane's
+//                  four query rows of one key are then 8 contiguous bytes, one
+//                  64-bit store
+// TILE is the KV tile's rows (Bc), BR the Q tile's (Br); BR = TILE but for the
+// rectangular 64-row Q tiles against 128-row KV tiles.
 //   slse[2] (lse * log2 e), sdelta[2] [BQ]
 //   the current item's task records, MAXT at a time (plus the next one)
 //   a 1 KiB sink for copy slots with nothing to copy
-template <typename T, int D, int TILE>
+template <typename T, int D, int TILE, int BR = TILE>
 struct Layout {
     // query rows per sub-step (fp32 at d=128 halves it to stay within LDS)
     static constexpr int BQ = (sizeof(T) == 4 && D == 128) ? 32 : 64;
@@ -146,7 +149,7 @@ struct Layout {
     static constexpr int QB = (BQ * Pad<T, D>::RS + 1023) / 1024 * 1024;    // one Q (or dO) buffer
     static constexpr int KB = (TILE * Pad<T, D>::RS + 1023) / 1024 * 1024;  // sK
     static constexpr int LDSS = TILE + Elem<T>::kPad;
-    static constexpr int SB = TILE * LDSS * (int)sizeof(T);
+    static constexpr int SB = BR * LDSS * (int)sizeof(T);
     static constexpr int OFF_Q = 0, OFF_DO = 2 * QB, OFF_K = 4 * QB, OFF_S = OFF_K + KB;
     static constexpr int OFF_LSE = OFF_S + SB, OFF_DEL = OFF_LSE + 2 * BQ * 4;
     static constexpr int MAXT = 256;  // task records of an item held in LDS at a time
@@ -155,7 +158,7 @@ struct Layout {
     static constexpr int OFF_SINK = OFF_TASK + (MAXT + 1) * 16;
     static constexpr size_t bytes = OFF_SINK + 1024;
     static_assert(bytes <= 160 * 1024 - 64, "LDS budget of a gfx950 work group exceeded");
-    static_assert(TILE % BQ == 0 && BQ % 32 == 0, "sub-step shape");
+    static_assert(BR % BQ == 0 && TILE % BR == 0 && BQ % 32 == 0, "sub-step and tile shapes");
 };
 
 // Four waves per work group and one work group per CU (the LDS above allows
@@ -171,21 +174,21 @@ constexpr int kWaves = 4, kThreads = 64 * kWaves;
 // layouts give the same operands, so the same bits.  Measured, the balance
 // favours it under Symmetric Shift at d = 128 (whose one-step reduction
 // chains carry every sub-step's length) and not under the other schedules.
-template <typename T, int D, int TILE, bool CAUSAL, bool DET, bool DST>
+template <typename T, int D, int TILE, bool CAUSAL, bool DET, bool DST, int BR>
 __global__ __launch_bounds__(kThreads, 1) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void bwd_main_kernel(KParams p) {
-    static_assert(!DST || sizeof(T) == 2, "the [key][query] dS layout is a bf16 layout");
+    static_assert(!DST || (sizeof(T) == 2 && BR == TILE), "the [key][query] dS layout is a bf16 square-tile layout");
     using E = Elem<T>;
     using V8 = typename E::vec8;
     using V4 = typename E::vec4;
-    using L = Layout<T, D, TILE>;
+    using L = Layout<T, D, TILE, BR>;
     constexpr int NW = kWaves;
-    constexpr int BQ = L::BQ, NSUB = TILE / BQ;
+    constexpr int BQ = L::BQ, NSUB = BR / BQ;  // sub-steps per task
     constexpr int RW = TILE / NW, NT = RW / 16;  // KV rows per wave, 16-row tiles
     constexpr int DW = D / NW, NDT = DW / 16;    // dQ columns per wave
     static_assert(RW % 16 == 0 && DW % 16 == 0, "wave shares must be whole 16-wide MFMA tiles");
     constexpr int KSD = D / 32, KSQ = BQ / 32, KSKV = TILE / 32;
-    constexpr int MT = BQ / 16, DT = D / 16, MTT = TILE / 16;
+    constexpr int MT = BQ / 16, DT = D / 16, MTT = BR / 16;  // MTT: 16-row tiles of a Q tile
     constexpr int LDSS = L::LDSS;
 
     extern __shared__ __align__(16) unsigned char smem[];
@@ -490,10 +493,11 @@ void bwd_main_kernel(KParams p) {
                 const i32x4 rec = stask[(t - t_beg) % L::MAXT];
                 const int qt = __builtin_amdgcn_readfirstlane(rec[1]);
 
-                // Causal mask: key column kloc of the tile is kept for query row
-                // qloc when kloc <= qloc + (qt - kv) * TILE, which holds for every
-                // element of a tile below the diagonal.
-                const int diag_off = (qt - kv) * TILE;
+                // Causal mask: key column kloc of the KV tile is kept for query
+                // row qloc of the Q tile when kloc <= qloc + qt * BR - kv * TILE,
+                // which holds for every element once diag_off >= TILE - 1 (the
+                // tasks the mask leaves have diag_off >= 0).
+                const int diag_off = qt * BR - kv * TILE;
 
                 const int rank = DET ? __builtin_amdgcn_readfirstlane(rec[2]) : 0;
                 // item of the Q tile's next contributor (-1: this is the last)
@@ -504,14 +508,14 @@ void bwd_main_kernel(KParams p) {
 
 #pragma unroll 1
                 for (int sub = 0; sub < NSUB; ++sub) {
-                    const int q0 = qt * TILE + sub * BQ;
+                    const int q0 = qt * BR + sub * BQ;
                     // ---- the Q/dO rows [q0, q0+BQ) are in buffer `buf` (prefetched
                     // during the previous sub-step, or loaded now at an item start)
                     if (!staged) issue_q(buf, q0);
                     // first row of the next sub-step (of this task or the next; at
                     // the item's end, a harmless copy of these rows again, which
                     // the item waits for before it ends)
-                    const int q_next = sub + 1 < NSUB ? q0 + BQ : (t + 1 < t_end ? next_q_of(t) * TILE : q0);
+                    const int q_next = sub + 1 < NSUB ? q0 + BQ : (t + 1 < t_end ? next_q_of(t) * BR : q0);
                     // landed for every wave, every wave done with the previous
                     // sub-step's dS, and the previous release's stores acknowledged
                     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
@@ -767,7 +771,7 @@ void bwd_main_kernel(KParams p) {
                         // S starts at 0, or at -inf where P must be 0: key rows
                         // past s, and (on the diagonal tile only) keys after the
                         // query, so the slots below need no mask
-                        const bool diag = CAUSAL && diag_off == 0;
+                        const bool diag = CAUSAL && diag_off < TILE;
 #pragma unroll
                         for (int G = 0; G < 2; ++G)
 #pragma unroll
@@ -787,7 +791,7 @@ void bwd_main_kernel(KParams p) {
                                     for (int nt = 0; nt < NT; ++nt)
 #pragma unroll
                                         for (int i = 0; i < 4; ++i)
-                                            if (w * RW + nt * 16 + c16 > sub * BQ + (2 * G + m) * 16 + 4 * g + i)
+                                            if (w * RW + nt * 16 + c16 > sub * BQ + (2 * G + m) * 16 + 4 * g + i + diag_off)
                                                 S[G][m][nt][i] = -__builtin_inff();
                         }
                         using I0 = std::integral_constant<int, 0>;
@@ -957,7 +961,7 @@ void bwd_main_kernel(KParams p) {
                                     if (rank > 0) v = prev[dtw][mtt] + v;
                                     if constexpr (MODE == 0) {
                                         // dQ = scale * sum in the output type
-                                        const int row = qt * TILE + mtt * 16 + c16;
+                                        const int row = qt * BR + mtt * 16 + c16;
                                         V4 o;
 #pragma unroll
                                         for (int e = 0; e < 4; ++e) o[e] = E::from_f(p.scale * v[e]);
@@ -994,7 +998,7 @@ void bwd_main_kernel(KParams p) {
                             for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
                                 for (int i = 0; i < 4; ++i)
-                                    unsafeAtomicAdd(acc + (size_t)(qt * TILE + part * BQ + mt * 16 + 4 * g + i) * D + w * DW +
+                                    unsafeAtomicAdd(acc + (size_t)(qt * BR + part * BQ + mt * 16 + 4 * g + i) * D + w * DW +
                                                         dtw * 16 + c16,
                                                     dq[part][dtw][mt][i]);
                 }
@@ -1040,10 +1044,10 @@ void bwd_main_kernel(KParams p) {
     }
 }
 
-template <typename T, int D, int TILE, bool CAUSAL, bool DET, bool DST = false>
+template <typename T, int D, int TILE, bool CAUSAL, bool DET, bool DST = false, int BR = TILE>
 static int launch_main_t(const KParams& kp, const BwdLaunch& L) {
-    auto kern = bwd_main_kernel<T, D, TILE, CAUSAL, DET, DST>;
-    const size_t smem = Layout<T, D, TILE>::bytes;
+    auto kern = bwd_main_kernel<T, D, TILE, CAUSAL, DET, DST, BR>;
+    const size_t smem = Layout<T, D, TILE, BR>::bytes;
     static bool attr_set = false;  // per instantiation; attribute is per device-function
     if (!attr_set) {
         if (hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem) != hipSuccess)
@@ -1079,14 +1083,16 @@ static int launch_main_t(const KParams& kp, const BwdLaunch& L) {
     return ATTN_OK;
 }
 
-template <typename T, int D, int TILE>
+template <typename T, int D, int TILE, int BR = TILE>
 static int launch_main_d(const KParams& kp, const BwdLaunch& L, bool causal, bool det, bool dst) {
-    if constexpr (sizeof(T) == 2 && D == 128 && TILE == 128) {
+    if constexpr (sizeof(T) == 2 && D == 128 && TILE == 128 && BR == TILE) {
         if (causal && det && dst) return launch_main_t<T, D, TILE, true, true, true>(kp, L);
     }
     if (causal)
-        return det ? launch_main_t<T, D, TILE, true, true>(kp, L) : launch_main_t<T, D, TILE, true, false>(kp, L);
-    return det ? launch_main_t<T, D, TILE, false, true>(kp, L) : launch_main_t<T, D, TILE, false, false>(kp, L);
+        return det ? launch_main_t<T, D, TILE, true, true, false, BR>(kp, L)
+                   : launch_main_t<T, D, TILE, true, false, false, BR>(kp, L);
+    return det ? launch_main_t<T, D, TILE, false, true, false, BR>(kp, L)
+               : launch_main_t<T, D, TILE, false, false, false, BR>(kp, L);
 }
 
 }  // namespace attn

@@ -68,7 +68,8 @@ struct BwdArgs {
     const void *q, *k, *v, *o, *dO;
     const float* lse;
     void *dq, *dk, *dv;
-    int H, s, d, n, tile;
+    int H, s, d, n, tile;  // n: Q tiles per head; tile: KV tile rows (Bc)
+    int br;                // Q tile rows (Br; = tile for square tiles)
     bool causal;
     int schedule;
     int dtype;
