@@ -91,27 +91,35 @@ def zero_edge_fit(tsa, ss):
     return best
 
 
-def measure(steps, tiles=(128,)):
+def parse_shapes(text):
+    """'128,64,64x128' -> [(128, 128), (64, 64), (64, 128)] as (Br, Bc)."""
+    out = []
+    for tok in text.split(","):
+        br, _, bc = tok.partition("x")
+        out.append((int(br), int(bc or br)))
+    return out
+
+
+def measure(steps, shapes=((128, 128),)):
     import torch
     import tile_scheduling_attn_amd as tsa
     import workloads
 
     workers = torch.cuda.get_device_properties(0).multi_processor_count  # one work group per CU
-    samples = []  # (n, causal, schedule, heads, workers, ms, workload, d, tile)
+    samples = []  # (n KV tiles, causal, schedule, heads, workers, ms, workload, d, Bc, Br)
     for name, causal, scheds in PLAN:
         wl = workloads.WORKLOADS[name]
         args = inputs(wl, torch)
-        for t in tiles:
-            tsa.attn_bwd_set_tile(wl.dtype, t)
+        for br, bc in shapes:
+            tsa.attn_bwd_set_tile_shape(wl.dtype, br, bc)
             try:
-                tile = tsa.attn_bwd_tile_size(wl.dtype)
-                n = -(-wl.s // tile)
+                n = -(-wl.s // bc)
                 for sched in scheds:
                     ms = time_main(tsa, args, sched, causal, steps, torch)
-                    print(f"{name} causal={causal} tile={tile} {sched}: {ms:.4f} ms", file=sys.stderr, flush=True)
-                    samples.append((n, causal, sched, wl.b * wl.h, workers, ms, name, wl.d, tile))
+                    print(f"{name} causal={causal} tile={br}x{bc} {sched}: {ms:.4f} ms", file=sys.stderr, flush=True)
+                    samples.append((n, causal, sched, wl.b * wl.h, workers, ms, name, wl.d, bc, br))
             finally:
-                tsa.attn_bwd_set_tile(wl.dtype, 0)
+                tsa.attn_bwd_set_tile_shape(wl.dtype, 0, 0)
         del args
         torch.cuda.empty_cache()
     return samples
@@ -119,10 +127,35 @@ def measure(steps, tiles=(128,)):
 
 def granularity(tsa, samples, fits):
     """Tile granularity check: 64-row launches against the 128-row costs
-    scaled to 64 rows, a fit of their own, and the closed form m*n*(c+r)."""
+    scaled to 64 rows, a fit of their own, and the closed form m*n*(c+r);
+    64 x 128 launches (Br != Bc) against the 128-row costs scaled to them."""
     out = {}
     for d in sorted({s[7] for s in samples}):
         f = fits.get(f"d{d}")
+        rect = [s for s in samples if s[7] == d and s[8] == 128 and s[9] == 64]
+        if f and rect:
+            c, r, e = f["c_us"] * 1e-3, f["r_us"] * 1e-3, f["e_us"] * 1e-3
+            # a 64 x 128 task: half the matrix work and half the accumulator
+            # bytes of a 128 x 128 one
+            cr, rr = c / 2, r / 2
+            rows = []
+            for n, causal, sched, heads, w, ms, name, _, _, _ in rect:
+                pred = tsa.attn_dagsim_rect(n, 2, causal, sched, heads, w, PLACEMENT, cr, rr, e)[0]
+                row = {"workload": name, "causal": causal, "schedule": sched, "kv_tiles": n, "q_tiles": 2 * n,
+                       "measured_ms": round(ms, 4), "scaled_model_ms": round(pred, 4)}
+                sq = [x for x in samples if x[6] == name and x[1] == causal and x[2] == sched and x[8] == 128
+                      and x[9] == 128]
+                if sq:
+                    row["measured_ms_128x128"] = round(sq[0][5], 4)
+                if not causal and sched == "shift":
+                    # total work per worker: heads * 2n^2 tasks of c/2 + r/2 over w workers
+                    row["closed_form_ms"] = round(heads * 2 * n * n * (cr + rr) / w, 4)
+                rows.append(row)
+            rel = [abs(x["scaled_model_ms"] / x["measured_ms"] - 1) for x in rows]
+            out[f"d{d}_64x128"] = {"scaled_costs_us": {"c": round(cr * 1e3, 4), "r": round(rr * 1e3, 4),
+                                                       "e": round(e * 1e3, 4)},
+                                   "scaled_model_rms_rel_err": round(math.sqrt(sum(x * x for x in rel) / len(rel)), 4),
+                                   "samples": rows}
         s64 = [s for s in samples if s[7] == d and s[8] == 64]
         if not f or not s64:
             continue
@@ -130,7 +163,7 @@ def granularity(tsa, samples, fits):
         c64, r64 = c * 0.25, r * 0.5
         cf, rf, ef, rms = tsa.attn_sched_fit([s[:6] for s in s64], placement=PLACEMENT)
         rows = []
-        for n, causal, sched, heads, w, ms, name, _, _ in s64:
+        for n, causal, sched, heads, w, ms, name, _, _, _ in s64:
             pred = tsa.attn_dagsim_edge(n, causal, sched, heads, w, PLACEMENT, c64, r64, e)[0]
             row = {"workload": name, "causal": causal, "schedule": sched, "n": n, "measured_ms": round(ms, 4),
                    "scaled_model_ms": round(pred, 4)}
@@ -155,10 +188,12 @@ def granularity(tsa, samples, fits):
 def fit(samples):
     import tile_scheduling_attn_amd as tsa
 
+    # older samples: no tile (128), or no Q tile (square)
     samples = [tuple(s) + ((128,) if len(s) < 9 else ()) for s in samples]
+    samples = [tuple(s) + ((s[8],) if len(s) < 10 else ()) for s in samples]
     report = {"fits": {}}
     for d in sorted({s[7] for s in samples}):
-        ss = [tuple(s[:7]) for s in samples if s[7] == d and s[8] == 128]
+        ss = [tuple(s[:7]) for s in samples if s[7] == d and s[8] == 128 and s[9] == 128]
         print(f"fitting d={d} ({len(ss)} samples)", file=sys.stderr, flush=True)
         c, r, e, rms = tsa.attn_sched_fit([s[:6] for s in ss], placement=PLACEMENT)
         c0, r0, _, rms0 = zero_edge_fit(tsa, ss)
@@ -179,7 +214,7 @@ def fit(samples):
                                    "e0": {"c_us": round(c0 * 1e3, 4), "r_us": round(r0 * 1e3, 4),
                                           "rms_rel_err": round(rms0, 4)},
                                    "samples": rows, "selected": picks}
-    if any(s[8] == 64 for s in samples):
+    if any(s[8] == 64 or s[9] != s[8] for s in samples):
         report["granularity"] = granularity(tsa, samples, report["fits"])
     return report
 
@@ -214,7 +249,8 @@ def handoff(iters=2000, reps=3):
 def main():
     ap = argparse.ArgumentParser(description=__doc__)
     ap.add_argument("--steps", type=int, default=5)
-    ap.add_argument("--tiles", default="128", help="comma list of bf16 tile edges to time (128, 64)")
+    ap.add_argument("--tiles", default="128",
+                    help="comma list of bf16 tile shapes to time: 128, 64 (square) or 64x128 (Br x Bc)")
     g = ap.add_mutually_exclusive_group()
     g.add_argument("--measure-only", action="store_true")
     g.add_argument("--samples", metavar="FILE")
@@ -227,7 +263,7 @@ def main():
         with open(a.samples) as f:
             samples = json.load(f)["samples"]
     else:
-        samples = measure(a.steps, tuple(int(t) for t in a.tiles.split(",")))
+        samples = measure(a.steps, parse_shapes(a.tiles))
         if a.measure_only:
             print(json.dumps({"samples": samples}))
             return
