@@ -239,8 +239,8 @@ struct FittedCosts {
     double c, r, e;
 };
 static FittedCosts fitted_costs(int d, TileShape t) {
-    if (t.bc == 64) return d == 64 ? FittedCosts{0.392, 1.845, 0.0} : FittedCosts{1.185, 2.996, 0.711};
-    const FittedCosts f = d == 64 ? FittedCosts{3.115, 2.273, 0.0} : FittedCosts{3.297, 3.775, 2.904};
+    if (t.bc == 64) return d == 64 ? FittedCosts{0.385, 1.859, 0.0} : FittedCosts{0.889, 3.206, 0.348};
+    const FittedCosts f = d == 64 ? FittedCosts{3.529, 1.985, 0.0} : FittedCosts{3.307, 3.639, 3.059};
     // 64-row Q tiles against 128-row KV tiles: half the matrix work and half
     // the accumulator bytes of a square task (no fit of their own)
     if (t.br != t.bc) return {f.c * t.br / t.bc, f.r * t.br / t.bc, f.e};
