@@ -88,3 +88,24 @@ def test_rect_full_size_sampled_parity(rect):
         e = rel_err(to_np_heads(t, heads), ref[name])
         record_error("rect64x128 s8k d128 causal symmetric_shift heads 0,31", name, e, TOL["bf16"])
         assert e <= TOL["bf16"], (name, e)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_rect_injected_delays_keep_the_bits(causal, rect):
+    """Random sleeps before every reduction phase (attn_bwd_set_debug) move the
+    hand-offs of the rectangular rank tables in time; the bits must not move."""
+    pb = Problem(1, 8, 2048, 128, "bf16", 9191, causal)
+    scheds = ("shift", "symmetric_shift", "descending") if causal else ("shift", "naive")
+    try:
+        for sched in scheds:
+            tsa.attn_bwd_set_debug(0, 0, 0)
+            ref = [t.clone() for t in pb.run(sched)]
+            for seed in (3, 0xabcdef):
+                tsa.attn_bwd_set_debug(0, 0, seed)
+                got = pb.run(sched)
+                torch.cuda.synchronize()
+                assert tsa.attn_bwd_query_status() == 0, tsa.last_error()
+                for x, y in zip(ref, got):
+                    assert torch.equal(x.view(torch.int16), y.view(torch.int16)), (sched, seed)
+    finally:
+        tsa.attn_bwd_set_debug(0, 0, 0)
