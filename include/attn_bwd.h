@@ -13,7 +13,9 @@
  *   dS_ij = P_ij (<dO_i, v_j> - D_i),
  *   dV_j = sum_i P_ij dO_i,  dK_j = scale sum_i dS_ij q_i,
  *   dQ_i = scale sum_j dS_ij k_j
- * tiled into square T x T tiles (T = 128 for bf16, 64 for fp32).  Each work
+ * tiled into square T x T tiles (T = 128 for bf16, 64 for fp32; bf16 also
+ * offers 64 x 64 and 64-row Q tiles against 128-row KV tiles, see
+ * attn_bwd_set_tile_shape).  Each work
  * group owns one KV tile at a time (Fig. 1: local dK/dV accumulation) and
  * adds its partial dQ of every Q tile into a global fp32 accumulator in an
  * order fixed by the schedule (Problem section: the serialised dQ
@@ -32,7 +34,8 @@
  *    exception crosses the ABI (every entry point catches them and returns
  *    ATTN_ERR_INTERNAL).  attn_bwd_last_error() gives a message for the last
  *    failure on the calling thread.
- *  - Accepted sizes: s <= 262144 (at most 2048 tiles of 128 rows), b*h below
+ *  - Accepted sizes: s <= 262144 (at most 2048 tiles of 128 rows; with
+ *    64-row tiles, at most 2048 Q tiles, i.e. s <= 131072), b*h below
  *    2^31 and b*h*s*d below 2^40; larger problems return
  *    ATTN_ERR_UNSUPPORTED (s) or ATTN_ERR_INVALID_ARG (the others).
  *  - scale must be a positive finite number (ATTN_ERR_INVALID_ARG
