@@ -286,3 +286,16 @@ def test_set_tile_shape_validates_and_restores_the_default():
     assert tsa.lib.attn_bwd_set_tile_shape(0, 0, 0) == 0
     assert tsa.attn_bwd_tile_shape("bf16") == (128, 128)
     assert tsa.attn_bwd_tile_shape("fp32") == (64, 64)
+
+
+def test_set_main_kernel_validates_and_round_trips():
+    assert tsa.attn_bwd_main_kernel() == "auto"                    # the default
+    for bad in (-1, 3, 7):
+        assert tsa.lib.attn_bwd_set_main_kernel(bad) == -1
+    assert tsa.attn_bwd_main_kernel() == "auto"
+    assert tsa.lib.attn_bwd_set_main_kernel(1) == 0
+    assert tsa.attn_bwd_main_kernel() == "pair"
+    tsa.attn_bwd_set_main_kernel("four_wave")
+    assert tsa.lib.attn_bwd_main_kernel() == 0
+    tsa.attn_bwd_set_main_kernel("auto")
+    assert tsa.lib.attn_bwd_main_kernel() == 2

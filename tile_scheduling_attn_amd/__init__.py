@@ -33,7 +33,8 @@ EXPORTS = ("attn_fwd", "attn_bwd_deterministic", "attn_bwd_deterministic_ex", "a
            "attn_bwd_resolve_schedule", "attn_bwd_deterministic_noalloc", "attn_bwd_noalloc_capacity",
            "attn_bwd_set_tile", "attn_bwd_atomic_rate", "attn_bwd_get_wait_hist",
            "attn_bwd_handoff_latency", "attn_bwd_handoff_bytes", "attn_sched_size_rect", "attn_sched_get_rect",
-           "attn_sched_min_workers_rect", "attn_dagsim_rect", "attn_bwd_set_tile_shape", "attn_bwd_tile_shape")
+           "attn_sched_min_workers_rect", "attn_dagsim_rect", "attn_bwd_set_tile_shape", "attn_bwd_tile_shape",
+           "attn_bwd_set_main_kernel", "attn_bwd_main_kernel")
 
 
 class AttnError(RuntimeError):
@@ -75,6 +76,10 @@ def _load():
     lib.attn_bwd_get_kernel_times.restype = i
     lib.attn_bwd_set_placement.argtypes = [i]
     lib.attn_bwd_set_placement.restype = i
+    lib.attn_bwd_set_main_kernel.argtypes = [i]
+    lib.attn_bwd_set_main_kernel.restype = i
+    lib.attn_bwd_main_kernel.argtypes = []
+    lib.attn_bwd_main_kernel.restype = i
     lib.attn_bwd_set_wait_stats.argtypes = [i]
     lib.attn_bwd_set_wait_stats.restype = i
     lib.attn_bwd_get_wait_stats.argtypes = [ull, ull, ull]
@@ -248,6 +253,23 @@ def attn_bwd_set_placement(mode) -> None:
     the default) or "global" (one queue)."""
     _check(lib.attn_bwd_set_placement(PLACEMENTS[mode] if isinstance(mode, str) else int(mode)),
            "attn_bwd_set_placement")
+
+
+MAIN_KERNELS = {"four_wave": 0, "pair": 1, "auto": 2}
+
+
+def attn_bwd_set_main_kernel(kernel) -> None:
+    """Main kernel of later deterministic bf16 d = 128 calls with 128 x 128
+    tiles: "four_wave", "pair" (eight waves, two per SIMD) or "auto" (the
+    default: pair under the causal mask); all give the same bits."""
+    _check(lib.attn_bwd_set_main_kernel(MAIN_KERNELS[kernel] if isinstance(kernel, str) else int(kernel)),
+           "attn_bwd_set_main_kernel")
+
+
+def attn_bwd_main_kernel() -> str:
+    """The setting of attn_bwd_set_main_kernel ("four_wave", "pair" or "auto")."""
+    code = lib.attn_bwd_main_kernel()
+    return {v: k for k, v in MAIN_KERNELS.items()}[code]
 
 
 def attn_bwd_set_wait_stats(on: bool) -> int:

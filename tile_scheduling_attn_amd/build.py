@@ -13,7 +13,7 @@ CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(HERE, "libattn_bwd.so")
 
-SOURCES = ["api.cpp", "schedule.cpp", "bwd_kernels.hip", "bwd_kernels_d64.hip", "fwd_kernels.hip", "noalloc.hip",
+SOURCES = ["api.cpp", "schedule.cpp", "bwd_kernels.hip", "bwd_kernels_d64.hip", "bwd_pair.hip", "fwd_kernels.hip", "noalloc.hip",
            "measure_kernels.hip"]
 # per-source extra flags: the bf16 d = 64 kernels keep MFMA results in
 # architectural registers (see the comment at the top of that file)

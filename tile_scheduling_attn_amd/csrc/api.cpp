@@ -119,6 +119,7 @@ static std::map<int, DevState> g_dev;
 static bool g_timing = false;
 static bool g_wait_stats = false;
 static bool g_xcd_placement = true;
+static std::atomic<int> g_main_kernel{ATTN_KERNEL_AUTO};
 static int g_last_dev = -1;
 // test hooks (attn_bwd_set_debug)
 static unsigned g_spin_limit = 0;
@@ -448,6 +449,7 @@ int backward(const void* q, const void* k, const void* v, const void* o, const v
     L.spin_limit = g_spin_limit;
     L.wait_offset = g_wait_offset;
     L.delay_seed = g_delay_seed;
+    L.main_kernel = g_main_kernel.load();
 
     rc = launch_backward(a, L);
     if (rc != ATTN_OK) return rc;
@@ -831,6 +833,17 @@ extern "C" int attn_bwd_set_placement(int mode) {
         return ATTN_OK;
     });
 }
+
+extern "C" int attn_bwd_set_main_kernel(int kernel) {
+    return guarded([&]() -> int {
+        if (kernel != ATTN_KERNEL_FOUR_WAVE && kernel != ATTN_KERNEL_PAIR && kernel != ATTN_KERNEL_AUTO)
+            return fail(ATTN_ERR_INVALID_ARG, "attn_bwd_set_main_kernel: unknown kernel");
+        g_main_kernel.store(kernel);
+        return ATTN_OK;
+    });
+}
+
+extern "C" int attn_bwd_main_kernel(void) { return g_main_kernel.load(); }
 
 extern "C" int attn_bwd_set_wait_stats(int on) {
     return guarded([&]() -> int {

@@ -143,6 +143,7 @@ struct BwdLaunch {
     unsigned spin_limit = 0;      // test hooks (attn_bwd_set_debug); 0: default
     int wait_offset = 0;
     unsigned delay_seed = 0;
+    int main_kernel = 2;          // attn_main_kernel_t (bf16 d = 128, 128 x 128 tiles)
 };
 
 // first counter word of the per-XCD work queues
