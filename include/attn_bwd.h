@@ -248,18 +248,18 @@ int attn_bwd_get_kernel_times(float* ms_preprocess, float* ms_main, float* ms_fi
 typedef enum { ATTN_PLACE_GLOBAL = 0, ATTN_PLACE_XCD = 1 } attn_placement_t;
 int attn_bwd_set_placement(int mode);
 
-/* Main kernel of later deterministic bf16 calls with d = 128 and 128 x 128
- * tiles (the other shapes, fp32 and ATOMIC always use the four-wave
- * kernel).  ATTN_KERNEL_FOUR_WAVE: four waves per work group, one per SIMD,
+/* Main kernel of later deterministic bf16 calls with 128 x 128 tiles (the
+ * other tile shapes, fp32 and ATOMIC always use the four-wave kernel).  ATTN_KERNEL_FOUR_WAVE: four waves per work group, one per SIMD,
  * each owning 32 KV rows of the tile.  ATTN_KERNEL_PAIR: eight waves, two
  * per SIMD; the two waves of a SIMD hold the same 32 KV rows and split each
  * 64-row step of query rows by role (one computes S, dP and the softmax of
  * the first 32 query rows and accumulates dV, the other does the same for
  * the last 32 and accumulates dK), exchanging one operand through LDS.
- * ATTN_KERNEL_AUTO (the default): the pair kernel under the causal mask,
- * the four-wave kernel under the full mask (measured on MI355X at s = 8192
- * and 16384: the pair kernel is 1.5-3% faster under the causal mask and
- * 1-4% slower under the full mask).  Both kernels perform every addition in
+ * ATTN_KERNEL_AUTO (the default): the pair kernel under the causal mask at
+ * d = 128, the four-wave kernel otherwise (measured on MI355X: at d = 128,
+ * s = 8192 and 16384, the pair kernel is 1.5-3% faster under the causal
+ * mask and 1-4% slower under the full mask; at d = 64, s = 2048, 8-19%
+ * slower).  Both kernels perform every addition in
  * the same order: the outputs are bitwise the same.  Process-wide; read at
  * each launch.  attn_bwd_main_kernel returns the current setting.  Returns
  * ATTN_OK or ATTN_ERR_INVALID_ARG. */

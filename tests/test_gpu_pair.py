@@ -1,5 +1,5 @@
 """The eight-wave pair kernel (attn_bwd_set_main_kernel("pair"): bf16,
-d = 128, 128 x 128 tiles, deterministic schedules): parity with the fp64
+d = 64 and 128, 128 x 128 tiles, deterministic schedules): parity with the fp64
 oracle on ragged shapes under every deterministic schedule, the bits of the
 four-wave kernel (both perform every addition in the same order), bitwise
 determinism, both work placements, injected reduction-phase delays, and
@@ -34,7 +34,7 @@ def same_bits(a, b):
 
 
 @pytest.mark.parametrize("shape", [(1, 2, 512, 128), (1, 3, 1000, 128), (2, 2, 200, 128), (1, 1, 128, 128),
-                                   (1, 2, 1100, 128)],
+                                   (1, 2, 1100, 128), (1, 2, 512, 64), (2, 2, 200, 64), (1, 3, 1100, 64)],
                          ids=lambda x: "-".join(map(str, x)))
 @pytest.mark.parametrize("causal", [False, True])
 def test_pair_parity_and_four_wave_bits(shape, causal, pair):
@@ -138,6 +138,27 @@ def test_pair_full_size_sampled_parity(causal, sched, pair):
     tsa.attn_bwd_set_main_kernel("four_wave")
     try:
         four = bits(pb.run(sched))
+    finally:
+        tsa.attn_bwd_set_main_kernel("pair")
+    assert same_bits(got, four)
+
+
+def test_pair_d64_s2k_causal_sampled_parity(pair):
+    """b4 h16 s2048 d64 causal, Symmetric Shift: sampled heads against the
+    oracle and the four-wave kernel's bits."""
+    pb = Problem(4, 16, 2048, 64, "bf16", 7805, True)
+    got = bits(pb.run("symmetric_shift"))
+    torch.cuda.synchronize()
+    assert tsa.attn_bwd_query_status() == 0, tsa.last_error()
+    heads = [0, 33, 63]
+    ref = pb.oracle(heads=heads)
+    for name, t in zip(("dq", "dk", "dv"), got):
+        e = rel_err(to_np_heads(t.view(torch.bfloat16), heads), ref[name])
+        record_error("pair s2k d64 causal symmetric_shift heads 0,33,63", name, e, TOL["bf16"])
+        assert e <= TOL["bf16"], (name, e)
+    tsa.attn_bwd_set_main_kernel("four_wave")
+    try:
+        four = bits(pb.run("symmetric_shift"))
     finally:
         tsa.attn_bwd_set_main_kernel("pair")
     assert same_bits(got, four)

@@ -259,9 +259,9 @@ MAIN_KERNELS = {"four_wave": 0, "pair": 1, "auto": 2}
 
 
 def attn_bwd_set_main_kernel(kernel) -> None:
-    """Main kernel of later deterministic bf16 d = 128 calls with 128 x 128
-    tiles: "four_wave", "pair" (eight waves, two per SIMD) or "auto" (the
-    default: pair under the causal mask); all give the same bits."""
+    """Main kernel of later deterministic bf16 calls with 128 x 128 tiles:
+    "four_wave", "pair" (eight waves, two per SIMD) or "auto" (the default:
+    pair under the causal mask at d = 128); all give the same bits."""
     _check(lib.attn_bwd_set_main_kernel(MAIN_KERNELS[kernel] if isinstance(kernel, str) else int(kernel)),
            "attn_bwd_set_main_kernel")
 

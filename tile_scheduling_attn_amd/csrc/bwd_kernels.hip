@@ -110,8 +110,8 @@ int probe_xcd_dispatch(int num_cus, bool* ok, unsigned* buf) {
 
 // bf16 d = 64 main kernels (bwd_kernels_d64.hip) for Q tiles of br rows
 int launch_main_bf16_d64_rect(const KParams& kp, const BwdLaunch& L, bool causal, bool det);
-// deterministic bf16 d = 128, 128 x 128 tiles, eight waves (bwd_pair.hip)
-int launch_main_bf16_pair(const KParams& kp, const BwdLaunch& L, bool causal);
+// deterministic bf16 128 x 128 tiles, eight waves (bwd_pair.hip)
+int launch_main_bf16_pair(const KParams& kp, const BwdLaunch& L, bool causal, int d);
 
 template <typename T, int TILE, int BR = TILE>
 static int launch_all(const BwdArgs& a, const BwdLaunch& L, KParams& kp) {
@@ -142,16 +142,19 @@ static int launch_all(const BwdArgs& a, const BwdLaunch& L, KParams& kp) {
     // s = 2048 the row layout is 3% faster)
     const bool dst = a.schedule == ATTN_SCHED_SYMMETRIC_SHIFT && BR == TILE;
     int rc;
-    if (a.d == 64) {
+    // the eight-wave pair kernel (bf16 128 x 128 tiles, deterministic): forced,
+    // or by default under the causal mask at d = 128
+    const bool pair = sizeof(T) == 2 && TILE == 128 && BR == TILE && det &&
+                      (L.main_kernel == ATTN_KERNEL_PAIR || (L.main_kernel == ATTN_KERNEL_AUTO && a.causal && a.d == 128));
+    if (pair) {
+        rc = launch_main_bf16_pair(kp, L, a.causal, a.d);
+    } else if (a.d == 64) {
         if constexpr (sizeof(T) == 2 && BR != TILE)
             rc = launch_main_bf16_d64_rect(kp, L, a.causal, det);
         else if constexpr (sizeof(T) == 2)
             rc = launch_main_bf16_d64(kp, L, a.causal, det, TILE);
         else
             rc = launch_main_d<T, 64, TILE>(kp, L, a.causal, det, dst);
-    } else if (sizeof(T) == 2 && TILE == 128 && BR == TILE && det &&
-               (L.main_kernel == ATTN_KERNEL_PAIR || (L.main_kernel == ATTN_KERNEL_AUTO && a.causal))) {
-        rc = launch_main_bf16_pair(kp, L, a.causal);
     } else {
         rc = launch_main_d<T, 128, TILE, BR>(kp, L, a.causal, det, dst);
     }

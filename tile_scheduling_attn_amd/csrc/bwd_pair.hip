@@ -1,5 +1,5 @@
-// The deterministic main kernel for bf16, d = 128, 128 x 128 tiles, with two
-// waves per SIMD ("pair" kernel).
+// The deterministic main kernel for bf16, d = 64 or 128, 128 x 128 tiles,
+// with two waves per SIMD ("pair" kernel).
 //
 // Same method, same task records, flags, accumulator layout and XCD
 // placement as bwd_main_kernel (bwd_main.h); what differs is how a work group
@@ -68,8 +68,9 @@ constexpr int kPairWaves = 8, kPairThreads = 64 * kPairWaves;
 //   slse[2], sdelta[2] [64]
 //   the current item's task records, MAXT at a time (plus the next one)
 //   a 1 KiB sink for copy slots with nothing to copy
+template <int D>
 struct PairLayout {
-    using P = Pad<bf16, 128>;
+    using P = Pad<bf16, D>;
     static constexpr int BQ = 64;
     static constexpr int QB = (BQ * P::RS + 1023) / 1024 * 1024;
     static constexpr int KB = (128 * P::RS + 1023) / 1024 * 1024;
@@ -87,18 +88,18 @@ struct PairLayout {
     static_assert(SB >= 128 * P::RS && KB >= 128 * P::RS, "dV and dK staging rows at a run's end");
 };
 
-template <bool CAUSAL>
+template <int D, bool CAUSAL>
 __global__ __launch_bounds__(kPairThreads, 1) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void bwd_pair_kernel(KParams p) {
     using T = bf16;
     using E = Elem<T>;
     using V8 = bf16x8;
     using V4 = bf16x4;
-    using L = PairLayout;
-    using P = Pad<T, 128>;
-    constexpr int D = 128, TILE = 128, BR = 128, BQ = 64, NSUB = 2, NW = kPairWaves;
-    constexpr int KSD = D / 32, DT = D / 16, MTT = BR / 16;
-    constexpr int NDT = 2, MT = 4;  // dQ per wave: 32 d columns x 64 query rows
+    using L = PairLayout<D>;
+    using P = Pad<T, D>;
+    constexpr int TILE = 128, BR = 128, BQ = 64, NSUB = 2, NW = kPairWaves;
+    constexpr int KSD = D / 32, DT = D / 16, MTT = BR / 16, KSKV = TILE / 32;  // 32-wide steps over d and over keys
+    constexpr int DW = D / 4, NDT = DW / 16, MT = 4;  // dQ per wave: D/4 d columns x 64 query rows
     constexpr int LDSS = L::LDSS, SRS = LDSS * 2, PRS = L::PSS * 2;
     constexpr int ODO = L::OFF_DO - L::OFF_Q;
     using I0 = std::integral_constant<int, 0>;
@@ -126,7 +127,7 @@ void bwd_pair_kernel(KParams p) {
     __builtin_assume(w >= 0 && w < NW);
     const int sl = w & 3;     // the pair: KV rows [32 sl, 32 sl + 32) of the tile
     const int role = w >> 2;  // query group of each sub-step; 0: dV, 1: dK
-    const int dblk = w & 3, part = w >> 2;  // dQ: d columns [32 dblk, +32), query rows [64 part, +64)
+    const int dblk = w & 3, part = w >> 2;  // dQ: d columns [DW dblk, +DW), query rows [64 part, +64)
     const T* gK = static_cast<const T*>(p.k);
     const T* gV = static_cast<const T*>(p.v);
     T* gdQ = static_cast<T*>(p.dq);
@@ -467,7 +468,7 @@ void bwd_pair_kernel(KParams p) {
                 }
 
                 // ---- R phase: wait for the tile's turn, dQ^T of this wave's
-                // 32 d columns and 64 query rows, the ordered sum, the release
+                // D/4 d columns and 64 query rows, the ordered sum, the release
                 const KParams& pr = kpar();
                 if (pr.delay_seed && tid == 0) {
                     const unsigned nap = mix32(pr.delay_seed ^ mix32((unsigned)item * 0x9e3779b9u + (unsigned)t)) & 31u;
@@ -509,7 +510,7 @@ void bwd_pair_kernel(KParams p) {
                     if (rank > 0 && !same && !(pflag & kWroteThrough) && tid == 0) atomicOr(pr.status, 2u);
                     const __amdgpu_buffer_rsrc_t rprev = acc_copy((pflag >> 28) & 7u), racc = acc_copy(queue);
                     const bool wt = !pr.chunks || succ < pr.bounds[queue & (pr.chunks - 1)] || succ >= pr.bounds[(queue & (pr.chunks - 1)) + 1];
-                    const int col0 = dblk * 32 + 4 * g;
+                    const int col0 = dblk * DW + 4 * g;
                     // the accumulator as 16x16 tiles in MFMA output order, as in
                     // bwd_main_kernel (lane l's 4 values at 16*l bytes of a tile); a
                     // tile's offset is the access's scalar offset, the lane's 16
@@ -542,7 +543,7 @@ void bwd_pair_kernel(KParams p) {
                     // transposed reads of [key][query]), then the sums: the output dQ
                     // (last contributor, MODE 0), written through to memory (MODE 1)
                     // or into this XCD's L2 (MODE 2)
-                    const lds_u8* tk = lsm + L::OFF_K + (8 * g + (c16 >> 2)) * P::RS + (dblk * 32 + 4 * (c16 & 3)) * 2;
+                    const lds_u8* tk = lsm + L::OFF_K + (8 * g + (c16 >> 2)) * P::RS + (dblk * DW + 4 * (c16 & 3)) * 2;
                     const lds_u8* ts = lsm + L::OFF_S + (8 * g + (c16 >> 2)) * SRS + 8 * (c16 & 3) + part * BQ * 2;
                     auto sum_out = [&](auto modec) {
                         constexpr int MODE = decltype(modec)::value;
@@ -551,7 +552,7 @@ void bwd_pair_kernel(KParams p) {
                         for (int dtw = 0; dtw < NDT; ++dtw)
 #pragma unroll
                             for (int j = 0; j < MT; ++j) dq[dtw][j] = zero_vec<f32x4>();
-                        static_for<0, KSD>([&](auto ksc) {
+                        static_for<0, KSKV>([&](auto ksc) {
                             constexpr int ks = decltype(ksc)::value;
                             V8 a[NDT], b[MT];
                             static_for<0, NDT>([&](auto jc) {
@@ -632,10 +633,10 @@ void bwd_pair_kernel(KParams p) {
     }
 }
 
-template <bool CAUSAL>
+template <int D, bool CAUSAL>
 int launch_pair_t(const KParams& kp, const BwdLaunch& L) {
-    auto kern = bwd_pair_kernel<CAUSAL>;
-    const size_t smem = PairLayout::bytes;
+    auto kern = bwd_pair_kernel<D, CAUSAL>;
+    const size_t smem = PairLayout<D>::bytes;
     static bool attr_set = false;
     if (!attr_set) {
         if (hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem) != hipSuccess)
@@ -668,9 +669,10 @@ int launch_pair_t(const KParams& kp, const BwdLaunch& L) {
 
 }  // namespace
 
-// The deterministic bf16 d = 128, 128 x 128 backward through the pair kernel.
-int launch_main_bf16_pair(const KParams& kp, const BwdLaunch& L, bool causal) {
-    return causal ? launch_pair_t<true>(kp, L) : launch_pair_t<false>(kp, L);
+// The deterministic bf16 128 x 128 backward through the pair kernel (d = 64 or 128).
+int launch_main_bf16_pair(const KParams& kp, const BwdLaunch& L, bool causal, int d) {
+    if (d == 64) return causal ? launch_pair_t<64, true>(kp, L) : launch_pair_t<64, false>(kp, L);
+    return causal ? launch_pair_t<128, true>(kp, L) : launch_pair_t<128, false>(kp, L);
 }
 
 }  // namespace attn
