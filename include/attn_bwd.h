@@ -257,7 +257,7 @@ int attn_bwd_set_placement(int mode);
  * the last 32 and accumulates dK), exchanging one operand through LDS.
  * ATTN_KERNEL_AUTO (the default): the pair kernel under the causal mask at
  * d = 128, the four-wave kernel otherwise (measured on MI355X: at d = 128,
- * s = 8192 and 16384, the pair kernel is 1.5-3% faster under the causal
+ * s = 8192 and 16384, the pair kernel is about 3% faster under the causal
  * mask and 1-4% slower under the full mask; at d = 64, s = 2048, 8-19%
  * slower).  Both kernels perform every addition in
  * the same order: the outputs are bitwise the same.  Process-wide; read at
