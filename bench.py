@@ -63,6 +63,16 @@ def kernel_source_sha():
     return h.hexdigest()
 
 
+def main_kernel_name(tsa, wl, causal, schedule, choice):
+    """The main kernel a call of this workload and schedule runs: the eight-wave
+    pair kernel for deterministic bf16 calls with 128 x 128 tiles when chosen,
+    or by default under the causal mask at d = 128; bwd_main_kernel otherwise."""
+    square128 = wl.dtype == "bf16" and tsa.attn_bwd_tile_shape("bf16") == (128, 128)
+    det = schedule != "atomic"
+    pair = square128 and det and (choice == "pair" or (choice == "auto" and causal and wl.d == 128))
+    return "bwd_pair_kernel" if pair else "bwd_main_kernel"
+
+
 def traffic_per_launch(workload, schedule):
     """HBM bytes per launch of the main kernel from the committed rocprofv3
     PMC summary, if it was taken on the current kernel source."""
@@ -177,7 +187,7 @@ def cpu_baseline(pb, heads, flops_per_head):
                       f"{dt:.1f} s; same FLOP convention"}
 
 
-def config_records(tsa, torch, steps, warmup):
+def config_records(tsa, torch, steps, warmup, main_kernel="auto"):
     """One record per (workload, mask, schedule) of the task's list."""
     import workloads
     from tests.support import Problem
@@ -205,7 +215,8 @@ def config_records(tsa, torch, steps, warmup):
                    "tflops": round(tfl, 2), "pct_of_peak": round(100 * tfl / peak, 2),
                    "clock_mhz": clock,
                    "pct_of_peak_at_clock": round(100 * tfl / (peak * clock / NOMINAL_MHZ), 2) if clock else None,
-                   "flag_wait_fraction": waits["fraction"]}
+                   "flag_wait_fraction": waits["fraction"],
+                   "main_kernel": main_kernel_name(tsa, wl, causal, sched, main_kernel)}
             if sched == "atomic":
                 atomic_ms = med
             rows.append(rec)
@@ -254,6 +265,8 @@ def main():
     ap.add_argument("--cpu-heads", type=int, default=16, help="heads in the CPU oracle sample (0: skip)")
     ap.add_argument("--placement", default="xcd", choices=("xcd", "global"),
                     help="work placement of the deterministic kernel (per-XCD queues or one global queue)")
+    ap.add_argument("--main-kernel", default="auto", choices=("auto", "four_wave", "pair"),
+                    help="main kernel of deterministic bf16 128 x 128 calls (auto: pair under the causal mask at d = 128)")
     ap.add_argument("--wait-hist", metavar="FILE", default=None,
                     help="write the headline schedule's flag-wait histogram (item mod 64 x step) to FILE")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
@@ -284,6 +297,7 @@ def main():
     from tests.support import Problem
 
     tsa.attn_bwd_set_placement(args.placement)
+    tsa.attn_bwd_set_main_kernel(args.main_kernel)
     wl = workloads.WORKLOADS[args.workload]
     causal = (wl.masks[0] == "causal") if args.causal is None else bool(args.causal)
     schedule = args.schedule
@@ -319,7 +333,7 @@ def main():
     roofline = {"bound": "mfma", "achieved": round(main_tflops, 2), "peak": peak,
                 "unit": "TFLOP/s", "frac": round(main_tflops / peak, 4),
                 "traffic": traffic_per_launch(wl.name, schedule),
-                "kernel": "bwd_main_kernel",
+                "kernel": main_kernel_name(tsa, wl, causal, schedule, args.main_kernel),
                 "algorithmic_flop_per_launch": flops}
 
     fwd = time_forward(tsa, pb, max(5, args.steps // 2), torch)
@@ -338,7 +352,7 @@ def main():
     del pb
     torch.cuda.empty_cache()
 
-    per_config = config_records(tsa, torch, args.steps, args.warmup) if args.per_config else []
+    per_config = config_records(tsa, torch, args.steps, args.warmup, args.main_kernel) if args.per_config else []
 
     clock = waits["clock_mhz"]
     line = {
@@ -358,7 +372,8 @@ def main():
                                f"{'causal' if causal else 'full'} mask, schedule {args.schedule} -> {schedule}",
                    "b": wl.b, "h": wl.h, "s": wl.s, "d": wl.d, "causal": causal,
                    "schedule": schedule, "schedule_requested": args.schedule,
-                   "tile": tsa.attn_bwd_tile_size(wl.dtype), "placement": args.placement},
+                   "tile": tsa.attn_bwd_tile_size(wl.dtype), "placement": args.placement,
+                   "main_kernel": roofline["kernel"]},
         "pct_of_peak": round(100 * tflops / peak, 2),
         "pct_of_peak_at_clock": round(100 * tflops / (peak * clock / NOMINAL_MHZ), 2) if clock else None,
         "clock_mhz": clock,
