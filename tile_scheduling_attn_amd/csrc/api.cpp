@@ -228,9 +228,11 @@ static TileShape shape_for(int dtype) {
 }
 static int tile_for(int dtype) { return shape_for(dtype).bc; }
 
-// Task costs of the DAG model fitted to this kernel on MI355X (microseconds
-// per compute phase c and reduction phase r, and per reduction hand-off e
-// between XCDs; simulator placement 2), per head dimension and tile edge.
+// Task costs of the DAG model fitted to the main kernels on MI355X
+// (microseconds per compute phase c and reduction phase r, and per reduction
+// hand-off e between XCDs; simulator placement 2), per head dimension and
+// tile edge.  The 128 x 128 fits come from launches with the default kernel
+// choice (the pair kernel under the causal mask at d = 128).
 // Each tile edge has a fit of its own: scaling the 128-row costs to 64 rows
 // (c by the T^2 d matrix work, r by the T d accumulator bytes) predicts the
 // 64-row makespans 30-50% short, because at 64 rows the ordered dQ traffic
@@ -241,7 +243,7 @@ struct FittedCosts {
 };
 static FittedCosts fitted_costs(int d, TileShape t) {
     if (t.bc == 64) return d == 64 ? FittedCosts{0.385, 1.859, 0.0} : FittedCosts{0.889, 3.206, 0.348};
-    const FittedCosts f = d == 64 ? FittedCosts{3.529, 1.985, 0.0} : FittedCosts{3.307, 3.639, 3.059};
+    const FittedCosts f = d == 64 ? FittedCosts{3.117, 2.320, 0.0} : FittedCosts{3.315, 3.565, 2.948};
     // 64-row Q tiles against 128-row KV tiles: half the matrix work and half
     // the accumulator bytes of a square task (no fit of their own)
     if (t.br != t.bc) return {f.c * t.br / t.bc, f.r * t.br / t.bc, f.e};
