@@ -37,13 +37,15 @@
 // accumulators (64) stay resident, and the rest of a phase must fit beside
 // them, which is why per-lane addresses are re-derived at each phase and the
 // kernel parameters of the reduction phase are read where they are used.
-// Measured on MI355X at s = 8192, d = 128, against bwd_main_kernel: without
-// the reduction phase the sub-steps are 11-13% slower (the single wave's
-// explicit instruction schedule hides its softmax under its own MFMAs, while
-// here the two waves of a SIMD meet the exchange barrier together), the
-// reduction phase is about 10% faster (eight waves keep more accumulator
-// loads and stores in flight), and whole launches are level (causal
-// Symmetric Shift and Descending) to 2-5% slower (full mask).
+// Measured on MI355X at s = 8192 and 16384, d = 128, against bwd_main_kernel:
+// without the reduction phase the sub-steps are 11-13% slower (the single
+// wave's explicit instruction schedule hides its softmax under its own MFMAs,
+// while here the two waves of a SIMD meet the exchange barrier together), the
+// reduction phase is faster (eight waves keep more accumulator loads and
+// stores in flight), and whole launches are about 3% faster under the causal
+// mask and 1-3% slower under the full mask, hence the default choice of the
+// library (the pair kernel under the causal mask at d = 128).  At d = 64 it
+// is 8-19% slower than the four-wave kernel of that head dimension.
 //
 // Method: DASH (Deterministic Attention Scheduling), Fig. 1 of the paper as
 // captioned on the pith.science review page (tiled backward: dK/dV local to
