@@ -63,14 +63,11 @@ def kernel_source_sha():
     return h.hexdigest()
 
 
-def main_kernel_name(tsa, wl, causal, schedule, choice):
-    """The main kernel a call of this workload and schedule runs: the eight-wave
-    pair kernel for deterministic bf16 calls with 128 x 128 tiles when chosen,
-    or by default under the causal mask at d = 128; bwd_main_kernel otherwise."""
-    square128 = wl.dtype == "bf16" and tsa.attn_bwd_tile_shape("bf16") == (128, 128)
-    det = schedule != "atomic"
-    pair = square128 and det and (choice == "pair" or (choice == "auto" and causal and wl.d == 128))
-    return "bwd_pair_kernel" if pair else "bwd_main_kernel"
+def main_kernel_name(tsa, wl, causal, schedule):
+    """The main kernel a call of this workload and schedule runs under the
+    library's current settings (the library's own rule)."""
+    k = tsa.attn_bwd_resolve_main_kernel(wl.d, causal, wl.dtype, schedule)
+    return "bwd_pair_kernel" if k == "pair" else "bwd_main_kernel"
 
 
 def traffic_per_launch(workload, schedule):
@@ -187,7 +184,7 @@ def cpu_baseline(pb, heads, flops_per_head):
                       f"{dt:.1f} s; same FLOP convention"}
 
 
-def config_records(tsa, torch, steps, warmup, main_kernel="auto"):
+def config_records(tsa, torch, steps, warmup):
     """One record per (workload, mask, schedule) of the task's list."""
     import workloads
     from tests.support import Problem
@@ -216,7 +213,7 @@ def config_records(tsa, torch, steps, warmup, main_kernel="auto"):
                    "clock_mhz": clock,
                    "pct_of_peak_at_clock": round(100 * tfl / (peak * clock / NOMINAL_MHZ), 2) if clock else None,
                    "flag_wait_fraction": waits["fraction"],
-                   "main_kernel": main_kernel_name(tsa, wl, causal, sched, main_kernel)}
+                   "main_kernel": main_kernel_name(tsa, wl, causal, sched)}
             if sched == "atomic":
                 atomic_ms = med
             rows.append(rec)
@@ -333,7 +330,7 @@ def main():
     roofline = {"bound": "mfma", "achieved": round(main_tflops, 2), "peak": peak,
                 "unit": "TFLOP/s", "frac": round(main_tflops / peak, 4),
                 "traffic": traffic_per_launch(wl.name, schedule),
-                "kernel": main_kernel_name(tsa, wl, causal, schedule, args.main_kernel),
+                "kernel": main_kernel_name(tsa, wl, causal, schedule),
                 "algorithmic_flop_per_launch": flops}
 
     fwd = time_forward(tsa, pb, max(5, args.steps // 2), torch)
@@ -352,7 +349,7 @@ def main():
     del pb
     torch.cuda.empty_cache()
 
-    per_config = config_records(tsa, torch, args.steps, args.warmup, args.main_kernel) if args.per_config else []
+    per_config = config_records(tsa, torch, args.steps, args.warmup) if args.per_config else []
 
     clock = waits["clock_mhz"]
     line = {

@@ -267,6 +267,13 @@ typedef enum { ATTN_KERNEL_FOUR_WAVE = 0, ATTN_KERNEL_PAIR = 1, ATTN_KERNEL_AUTO
 int attn_bwd_set_main_kernel(int kernel);
 int attn_bwd_main_kernel(void);
 
+/* The main kernel a later call with this head dimension, mask, element type
+ * and schedule runs under the current settings (attn_bwd_set_main_kernel
+ * and the tile shape): ATTN_KERNEL_FOUR_WAVE or ATTN_KERNEL_PAIR; host only,
+ * launches nothing.  Returns ATTN_ERR_INVALID_ARG for a bad mask, dtype or
+ * schedule and ATTN_ERR_UNSUPPORTED for d not 64 or 128. */
+int attn_bwd_resolve_main_kernel(int d, int causal, int dtype, int schedule);
+
 /* Per-call times of the recording started by attn_bwd_set_timing(1): for
  * the first min(calls recorded, max_calls) calls, ms_total[i] (preprocess to
  * the end of the last kernel) and ms_main[i] (main kernel), either array may

@@ -299,3 +299,30 @@ def test_set_main_kernel_validates_and_round_trips():
     assert tsa.lib.attn_bwd_main_kernel() == 0
     tsa.attn_bwd_set_main_kernel("auto")
     assert tsa.lib.attn_bwd_main_kernel() == 2
+
+
+def test_resolve_main_kernel_follows_the_settings():
+    r = tsa.attn_bwd_resolve_main_kernel
+    assert tsa.attn_bwd_main_kernel() == "auto"
+    assert r(128, True, "bf16", "symmetric_shift") == "pair"       # default: pair under the causal mask at d = 128
+    assert r(128, True, "bf16", "auto") == "pair"
+    assert r(128, False, "bf16", "shift") == "four_wave"
+    assert r(64, True, "bf16", "symmetric_shift") == "four_wave"
+    assert r(128, True, "bf16", "atomic") == "four_wave"           # no pair form of ATOMIC
+    assert r(128, True, "fp32", "descending") == "four_wave"
+    tsa.attn_bwd_set_main_kernel("pair")
+    try:
+        assert r(128, False, "bf16", "shift") == "pair"
+        assert r(64, False, "bf16", "naive") == "pair"
+        tsa.attn_bwd_set_tile_shape("bf16", 64, 128)
+        try:
+            assert r(128, True, "bf16", "shift") == "four_wave"    # 128 x 128 tiles only
+        finally:
+            tsa.attn_bwd_set_tile_shape("bf16", 0, 0)
+        tsa.attn_bwd_set_main_kernel("four_wave")
+        assert r(128, True, "bf16", "symmetric_shift") == "four_wave"
+    finally:
+        tsa.attn_bwd_set_main_kernel("auto")
+    assert tsa.lib.attn_bwd_resolve_main_kernel(96, 1, 0, 1) == -2
+    assert tsa.lib.attn_bwd_resolve_main_kernel(128, 2, 0, 1) == -1
+    assert tsa.lib.attn_bwd_resolve_main_kernel(128, 1, 0, 9) == -1

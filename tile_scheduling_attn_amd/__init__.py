@@ -34,7 +34,7 @@ EXPORTS = ("attn_fwd", "attn_bwd_deterministic", "attn_bwd_deterministic_ex", "a
            "attn_bwd_set_tile", "attn_bwd_atomic_rate", "attn_bwd_get_wait_hist",
            "attn_bwd_handoff_latency", "attn_bwd_handoff_bytes", "attn_sched_size_rect", "attn_sched_get_rect",
            "attn_sched_min_workers_rect", "attn_dagsim_rect", "attn_bwd_set_tile_shape", "attn_bwd_tile_shape",
-           "attn_bwd_set_main_kernel", "attn_bwd_main_kernel")
+           "attn_bwd_set_main_kernel", "attn_bwd_main_kernel", "attn_bwd_resolve_main_kernel")
 
 
 class AttnError(RuntimeError):
@@ -80,6 +80,8 @@ def _load():
     lib.attn_bwd_set_main_kernel.restype = i
     lib.attn_bwd_main_kernel.argtypes = []
     lib.attn_bwd_main_kernel.restype = i
+    lib.attn_bwd_resolve_main_kernel.argtypes = [i, i, i, i]
+    lib.attn_bwd_resolve_main_kernel.restype = i
     lib.attn_bwd_set_wait_stats.argtypes = [i]
     lib.attn_bwd_set_wait_stats.restype = i
     lib.attn_bwd_get_wait_stats.argtypes = [ull, ull, ull]
@@ -264,6 +266,15 @@ def attn_bwd_set_main_kernel(kernel) -> None:
     pair under the causal mask at d = 128); all give the same bits."""
     _check(lib.attn_bwd_set_main_kernel(MAIN_KERNELS[kernel] if isinstance(kernel, str) else int(kernel)),
            "attn_bwd_set_main_kernel")
+
+
+def attn_bwd_resolve_main_kernel(d, causal, dtype="bf16", schedule="shift") -> str:
+    """The main kernel ("four_wave" or "pair") a call with this head dimension,
+    mask, element type and schedule runs under the current settings."""
+    dt = DTYPES[dtype] if isinstance(dtype, str) else int(dtype)
+    sc = SCHEDULES[schedule] if isinstance(schedule, str) else int(schedule)
+    code = _check(lib.attn_bwd_resolve_main_kernel(int(d), int(bool(causal)), dt, sc), "attn_bwd_resolve_main_kernel")
+    return {v: k for k, v in MAIN_KERNELS.items()}[code]
 
 
 def attn_bwd_main_kernel() -> str:

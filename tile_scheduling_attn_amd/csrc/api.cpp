@@ -847,6 +847,23 @@ extern "C" int attn_bwd_set_main_kernel(int kernel) {
 
 extern "C" int attn_bwd_main_kernel(void) { return g_main_kernel.load(); }
 
+// The rule the launch applies (launch_all in bwd_kernels.hip): the pair kernel
+// for deterministic bf16 calls with 128 x 128 tiles, when forced or, by
+// default, under the causal mask at d = 128.
+extern "C" int attn_bwd_resolve_main_kernel(int d, int causal, int dtype, int schedule) {
+    return guarded([&]() -> int {
+        if ((causal != 0 && causal != 1) || (dtype != ATTN_BF16 && dtype != ATTN_FP32) || schedule < ATTN_SCHED_NAIVE ||
+            schedule > ATTN_SCHED_AUTO)
+            return fail(ATTN_ERR_INVALID_ARG, "invalid mask, dtype or schedule");
+        if (d != 64 && d != 128) return fail(ATTN_ERR_UNSUPPORTED, "head dimension must be 64 or 128");
+        const TileShape t = shape_for(dtype);
+        const int mk = g_main_kernel.load();
+        const bool pair = dtype == ATTN_BF16 && t.br == 128 && t.bc == 128 && schedule != ATTN_SCHED_ATOMIC &&
+                          (mk == ATTN_KERNEL_PAIR || (mk == ATTN_KERNEL_AUTO && causal && d == 128));
+        return pair ? ATTN_KERNEL_PAIR : ATTN_KERNEL_FOUR_WAVE;
+    });
+}
+
 extern "C" int attn_bwd_set_wait_stats(int on) {
     return guarded([&]() -> int {
         std::lock_guard<std::mutex> lock(g_mutex);
