@@ -890,6 +890,16 @@ void bwd_main_kernel(KParams p) {
                     }
                     s_prev = seen;
                 }
+                // d = 128: settle the early flag read in every lane here.  Left
+                // pending (lanes other than thread 0 never use it), it makes the
+                // compiler wait for every outstanding memory operation at the
+                // next task's first LDS read, which then also waits for this R
+                // phase's accumulator stores instead of letting them drain
+                // behind the task setup (full-mask Shift at s = 8192 runs 2-3%
+                // faster).  The d = 64 kernels have no such wait, and there the
+                // settling wait, which also covers the prefetch of the next
+                // rows, measured 2-9% slower.
+                if constexpr (D == 128) asm volatile("" ::"v"(early));
                 __syncthreads();
                 if (DET) {
                     // this head's accumulator in the copy of queue qc
