@@ -858,9 +858,9 @@ extern "C" int attn_bwd_resolve_main_kernel(int d, int causal, int dtype, int sc
         if (d != 64 && d != 128) return fail(ATTN_ERR_UNSUPPORTED, "head dimension must be 64 or 128");
         const TileShape t = shape_for(dtype);
         const int mk = g_main_kernel.load();
-        const bool pair = dtype == ATTN_BF16 && t.br == 128 && t.bc == 128 && schedule != ATTN_SCHED_ATOMIC &&
-                          (mk == ATTN_KERNEL_PAIR || (mk == ATTN_KERNEL_AUTO && causal && d == 128));
-        return pair ? ATTN_KERNEL_PAIR : ATTN_KERNEL_FOUR_WAVE;
+        return runs_pair_kernel(dtype == ATTN_BF16, t.br, t.bc, schedule != ATTN_SCHED_ATOMIC, mk, causal != 0, d)
+                   ? ATTN_KERNEL_PAIR
+                   : ATTN_KERNEL_FOUR_WAVE;
     });
 }
 

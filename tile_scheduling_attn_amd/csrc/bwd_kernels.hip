@@ -144,8 +144,7 @@ static int launch_all(const BwdArgs& a, const BwdLaunch& L, KParams& kp) {
     int rc;
     // the eight-wave pair kernel (bf16 128 x 128 tiles, deterministic): forced,
     // or by default under the causal mask at d = 128
-    const bool pair = sizeof(T) == 2 && TILE == 128 && BR == TILE && det &&
-                      (L.main_kernel == ATTN_KERNEL_PAIR || (L.main_kernel == ATTN_KERNEL_AUTO && a.causal && a.d == 128));
+    const bool pair = runs_pair_kernel(sizeof(T) == 2, BR, TILE, det, L.main_kernel, a.causal, a.d);
     if (pair) {
         rc = launch_main_bf16_pair(kp, L, a.causal, a.d);
     } else if (a.d == 64) {

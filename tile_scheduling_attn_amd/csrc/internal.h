@@ -5,6 +5,8 @@
 #include <new>
 #include <vector>
 
+#include "attn_bwd.h"
+
 namespace attn {
 
 // Largest number of tiles per sequence the host side accepts: a head's task
@@ -145,6 +147,15 @@ struct BwdLaunch {
     unsigned delay_seed = 0;
     int main_kernel = 2;          // attn_main_kernel_t (bf16 d = 128, 128 x 128 tiles)
 };
+
+// Whether a launch runs the eight-wave pair kernel: bf16, 128 x 128 tiles, an
+// ordered (deterministic) schedule, and the pair kernel either forced or, by
+// default, the causal mask at d = 128.  The launch and
+// attn_bwd_resolve_main_kernel both decide through this one rule.
+inline bool runs_pair_kernel(bool bf16, int br, int bc, bool det, int main_kernel, bool causal, int d) {
+    return bf16 && br == 128 && bc == 128 && det &&
+           (main_kernel == ATTN_KERNEL_PAIR || (main_kernel == ATTN_KERNEL_AUTO && causal && d == 128));
+}
 
 // first counter word of the per-XCD work queues
 constexpr int kQueueWord = 48;
