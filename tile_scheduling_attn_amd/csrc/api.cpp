@@ -243,7 +243,7 @@ struct FittedCosts {
 };
 static FittedCosts fitted_costs(int d, TileShape t) {
     if (t.bc == 64) return d == 64 ? FittedCosts{0.385, 1.859, 0.0} : FittedCosts{0.889, 3.206, 0.348};
-    const FittedCosts f = d == 64 ? FittedCosts{3.117, 2.320, 0.0} : FittedCosts{3.315, 3.565, 2.948};
+    const FittedCosts f = d == 64 ? FittedCosts{3.144, 2.358, 0.0} : FittedCosts{3.430, 3.430, 3.022};
     // 64-row Q tiles against 128-row KV tiles: half the matrix work and half
     // the accumulator bytes of a square task (no fit of their own)
     if (t.br != t.bc) return {f.c * t.br / t.bc, f.r * t.br / t.bc, f.e};
