@@ -201,8 +201,8 @@ int attn_bwd_tile_size(int dtype);
 int attn_bwd_set_tile(int dtype, int tile);
 
 /* Rectangular tiles for later bf16 calls: Q tiles of Br rows against KV
- * tiles of Bc rows (the survey's variable tile shapes: Br != Bc; the pages
- * draw square tiles).  (Br, Bc) = (128, 128) (the default; (0, 0) selects
+ * tiles of Bc rows (variable tile shapes, Br != Bc; the pages draw square
+ * tiles).  (Br, Bc) = (128, 128) (the default; (0, 0) selects
  * it), (64, 64), or (64, 128): then every KV tile meets ratio = 2 Q tiles
  * of its rows, the schedules run over n = ceil(s/Bc) KV tiles and 2n Q
  * tiles as attn_sched_get_rect defines them (Symmetric Shift folds KV p
@@ -323,8 +323,8 @@ int attn_bwd_get_clock(double* mhz);
 int attn_bwd_atomic_rate(void* acc, size_t acc_bytes, int tasks, void* stream, float* ms, double* adds);
 
 /* Latency of one dQ hand-off between two work groups, for calibrating the
- * DAG model's reduction cost r and release edge e (the survey of the
- * review page's model asks for the flag latency per XCD distance).  Work
+ * DAG model's reduction cost r and release edge e (the flag latency per
+ * XCD distance, which the review page's cost model leaves open).  Work
  * group 0 and work group `pong` (1..63) take turns `iters` times (2..2^20):
  * a turn waits for a flag in device memory to reach its number (relaxed
  * agent-scope loads), then, for mode 1 or 2, reads the previous turn's
