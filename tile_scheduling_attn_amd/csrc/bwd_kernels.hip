@@ -8,9 +8,10 @@ namespace attn {
 // bf16 d = 64 main kernels (bwd_kernels_d64.hip)
 int launch_main_bf16_d64(const KParams& kp, const BwdLaunch& L, bool causal, bool det, int tile);
 
-// D[head][row] = <dO_row, O_row> in fp32 and lse2[head][row] = lse * log2(e)
-// (both zero for padded rows, the softmax's exp2 argument then needs no
-// multiply per use); clears the flags and counters of the call and, for the
+// -D[head][row] = -<dO_row, O_row> in fp32 (negated: at d = 64 the main
+// kernels start dP's accumulation from it, so dP - D needs no subtraction)
+// and lse2[head][row] = lse * log2(e) (both zero for padded rows, the
+// softmax's exp2 argument then needs no multiply per use); clears the flags and counters of the call and, for the
 // atomic variant, the dQ accumulator.  16 lanes per row.
 template <typename T, int D>
 __global__ __launch_bounds__(256) void bwd_preprocess_kernel(const T* __restrict__ o, const T* __restrict__ dO,
@@ -34,7 +35,7 @@ __global__ __launch_bounds__(256) void bwd_preprocess_kernel(const T* __restrict
 #pragma unroll
         for (int m = 8; m >= 1; m >>= 1) acc += __shfl_xor(acc, m, 16);
         if (part == 0) {
-            delta[row] = acc;
+            delta[row] = -acc;
             lse2[row] = r < s ? lse[(size_t)hh * s + r] * kLog2e : 0.f;
         }
     }

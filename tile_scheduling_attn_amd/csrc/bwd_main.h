@@ -102,7 +102,7 @@ constexpr unsigned kRankMask = 0xffffffu, kWroteThrough = 1u << 31;
 struct KParams {
     const void *q, *k, *v, *dO;
     const float* lse2;   // lse * log2(e) [H][s_pad] (workspace; zero past s)
-    const float* delta;
+    const float* delta;  // -D = -rowsum(dO * O) [H][s_pad] (workspace; zero past s)
     void *dq, *dk, *dv;
     float* dq_acc;
     unsigned* flags;
@@ -137,7 +137,7 @@ struct KParams {
 //                  64-bit store
 // TILE is the KV tile's rows (Bc), BR the Q tile's (Br); BR = TILE but for the
 // rectangular 64-row Q tiles against 128-row KV tiles.
-//   slse[2] (lse * log2 e), sdelta[2] [BQ]
+//   slse[2] (lse * log2 e), sdelta[2] (-D) [BQ]
 //   the current item's task records, MAXT at a time (plus the next one)
 //   a 1 KiB sink for copy slots with nothing to copy
 template <typename T, int D, int TILE, int BR = TILE>
@@ -190,6 +190,12 @@ void bwd_main_kernel(KParams p) {
     constexpr int KSD = D / 32, KSQ = BQ / 32, KSKV = TILE / 32;
     constexpr int MT = BQ / 16, DT = D / 16, MTT = BR / 16;  // MTT: 16-row tiles of a Q tile
     constexpr int LDSS = L::LDSS;
+    // d = 64 (bf16 sub-step schedule): dP's accumulation starts at -D instead of
+    // 0, so dS = P (dP - D) is one multiply per element.  The VALU work of the
+    // softmax does not shrink with d, and at d = 64 it is the larger share of a
+    // sub-step.  (At d = 128, where S and dP live in accumulation registers,
+    // -D would first have to be copied there; it stays a separate add.)
+    constexpr bool kDPFromD = D == 64;
 
     extern __shared__ __align__(16) unsigned char smem[];
     lds_u8* const lsm = (lds_u8*)smem;  // LDS address space: no per-use conversion
@@ -594,14 +600,14 @@ void bwd_main_kernel(KParams p) {
 #pragma unroll
                             for (int i = 0; i < 4; ++i) {
                                 const int ql = (2 * GQ + m) * 16 + 4 * g + i;
-                                const float l2 = slse[ql], dl = sdelta[ql];
+                                const float l2 = slse[ql], dl = sdelta[ql];  // dl = -D
 #pragma unroll
                                 for (int nt = 0; nt < NT; ++nt) {
                                     float pv = __builtin_amdgcn_exp2f(S[GQ][m][nt][i] * p.scale_log2 - l2);
                                     if constexpr (CAUSAL)
                                         pv = (w * RW + nt * 16 + c16 <= sub * BQ + ql + diag_off) ? pv : 0.f;
                                     aP[GQ][nt][4 * m + i] = E::from_f(pv);
-                                    aS[GQ][nt][4 * m + i] = E::from_f(pv * (dP[GQ][m][nt][i] - dl));
+                                    aS[GQ][nt][4 * m + i] = E::from_f(pv * (dP[GQ][m][nt][i] + dl));
                                 }
                             }
                     };
@@ -687,7 +693,7 @@ void bwd_main_kernel(KParams p) {
                         // several steps in flight.
                         constexpr int PF2 = 4, R2 = PF2 + 1;
                         s16x4 t2[R2][2][2];
-                        f32x4 lsev[2][2], delv[2][2];  // [group][m]: lse * log2 e and D of rows 4g..4g+3
+                        f32x4 lsev[2][2], delv[2][2];  // [group][m]: lse * log2 e and -D of rows 4g..4g+3
                         const lds_u8* tq = (const lds_u8*)sQ + (4 * g + (c16 >> 2)) * P::RS + 8 * (c16 & 3);
                         // read k (0..3) of phase-1 step j = (group, 32-wide d step)
                         auto rd1 = [&](auto jc, auto kc) {
@@ -713,7 +719,7 @@ void bwd_main_kernel(KParams p) {
                             constexpr int G = decltype(Gc)::value, k = decltype(kc)::value, m = k % 2;
                             if constexpr (k < 2)
                                 lsev[G][m] = *reinterpret_cast<const f32x4*>(slse + (2 * G + m) * 16 + 4 * g);
-                            else
+                            else if constexpr (!kDPFromD)
                                 delv[G][m] = *reinterpret_cast<const f32x4*>(sdelta + (2 * G + m) * 16 + 4 * g);
                         };
                         // softmax pair k (0..7) of group G: rows (m, 2ip..2ip+1), key tile nt
@@ -724,7 +730,10 @@ void bwd_main_kernel(KParams p) {
                             for (int i = 2 * ip; i < 2 * ip + 2; ++i) {
                                 const float pv = __builtin_amdgcn_exp2f(S[G][m][nt][i] * p.scale_log2 - lsev[G][m][i]);
                                 aP[G][nt][4 * m + i] = E::from_f(pv);
-                                aS[G][nt][4 * m + i] = E::from_f(pv * (dP[G][m][nt][i] - delv[G][m][i]));
+                                if constexpr (kDPFromD)
+                                    aS[G][nt][4 * m + i] = E::from_f(pv * dP[G][m][nt][i]);
+                                else
+                                    aS[G][nt][4 * m + i] = E::from_f(pv * (dP[G][m][nt][i] + delv[G][m][i]));
                             }
                         };
                         // dS stores.  DST ([key][query]): store k (0..7) = group, m, key
@@ -775,13 +784,18 @@ void bwd_main_kernel(KParams p) {
 #pragma unroll
                         for (int G = 0; G < 2; ++G)
 #pragma unroll
-                            for (int m = 0; m < 2; ++m)
+                            for (int m = 0; m < 2; ++m) {
+                                // d = 64: dP starts at -D of the lane's rows
+                                f32x4 d0 = zero_vec<f32x4>();
+                                if constexpr (kDPFromD)
+                                    d0 = *reinterpret_cast<const f32x4*>(sdelta + (2 * G + m) * 16 + 4 * g);
 #pragma unroll
                                 for (int nt = 0; nt < NT; ++nt) {
 #pragma unroll
                                     for (int i = 0; i < 4; ++i) S[G][m][nt][i] = s_init[nt];
-                                    dP[G][m][nt] = zero_vec<f32x4>();
+                                    dP[G][m][nt] = d0;
                                 }
+                            }
                         if (diag) {
 #pragma unroll
                             for (int G = 0; G < 2; ++G)
