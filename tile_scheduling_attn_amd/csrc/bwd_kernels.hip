@@ -8,8 +8,8 @@ namespace attn {
 // bf16 d = 64 main kernels (bwd_kernels_d64.hip)
 int launch_main_bf16_d64(const KParams& kp, const BwdLaunch& L, bool causal, bool det, int tile);
 
-// -D[head][row] = -<dO_row, O_row> in fp32 (negated: at d = 64 the main
-// kernels start dP's accumulation from it, so dP - D needs no subtraction)
+// -D[head][row] = -<dO_row, O_row> in fp32 (negated: the bf16 main kernels
+// start dP's accumulation from it, so dP - D needs no subtraction)
 // and lse2[head][row] = lse * log2(e) (both zero for padded rows, the
 // softmax's exp2 argument then needs no multiply per use); clears the flags and counters of the call and, for the
 // atomic variant, the dQ accumulator.  16 lanes per row.

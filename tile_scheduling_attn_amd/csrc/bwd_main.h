@@ -190,12 +190,6 @@ void bwd_main_kernel(KParams p) {
     constexpr int KSD = D / 32, KSQ = BQ / 32, KSKV = TILE / 32;
     constexpr int MT = BQ / 16, DT = D / 16, MTT = BR / 16;  // MTT: 16-row tiles of a Q tile
     constexpr int LDSS = L::LDSS;
-    // d = 64 (bf16 sub-step schedule): dP's accumulation starts at -D instead of
-    // 0, so dS = P (dP - D) is one multiply per element.  The VALU work of the
-    // softmax does not shrink with d, and at d = 64 it is the larger share of a
-    // sub-step.  (At d = 128, where S and dP live in accumulation registers,
-    // -D would first have to be copied there; it stays a separate add.)
-    constexpr bool kDPFromD = D == 64;
 
     extern __shared__ __align__(16) unsigned char smem[];
     lds_u8* const lsm = (lds_u8*)smem;  // LDS address space: no per-use conversion
@@ -693,7 +687,7 @@ void bwd_main_kernel(KParams p) {
                         // several steps in flight.
                         constexpr int PF2 = 4, R2 = PF2 + 1;
                         s16x4 t2[R2][2][2];
-                        f32x4 lsev[2][2], delv[2][2];  // [group][m]: lse * log2 e and -D of rows 4g..4g+3
+                        f32x4 lsev[2][2];  // [group][m]: lse * log2 e of rows 4g..4g+3
                         const lds_u8* tq = (const lds_u8*)sQ + (4 * g + (c16 >> 2)) * P::RS + 8 * (c16 & 3);
                         // read k (0..3) of phase-1 step j = (group, 32-wide d step)
                         auto rd1 = [&](auto jc, auto kc) {
@@ -719,8 +713,6 @@ void bwd_main_kernel(KParams p) {
                             constexpr int G = decltype(Gc)::value, k = decltype(kc)::value, m = k % 2;
                             if constexpr (k < 2)
                                 lsev[G][m] = *reinterpret_cast<const f32x4*>(slse + (2 * G + m) * 16 + 4 * g);
-                            else if constexpr (!kDPFromD)
-                                delv[G][m] = *reinterpret_cast<const f32x4*>(sdelta + (2 * G + m) * 16 + 4 * g);
                         };
                         // softmax pair k (0..7) of group G: rows (m, 2ip..2ip+1), key tile nt
                         auto sm_pair = [&](auto Gc, auto kc) {
@@ -730,10 +722,7 @@ void bwd_main_kernel(KParams p) {
                             for (int i = 2 * ip; i < 2 * ip + 2; ++i) {
                                 const float pv = __builtin_amdgcn_exp2f(S[G][m][nt][i] * p.scale_log2 - lsev[G][m][i]);
                                 aP[G][nt][4 * m + i] = E::from_f(pv);
-                                if constexpr (kDPFromD)
-                                    aS[G][nt][4 * m + i] = E::from_f(pv * dP[G][m][nt][i]);
-                                else
-                                    aS[G][nt][4 * m + i] = E::from_f(pv * (dP[G][m][nt][i] + delv[G][m][i]));
+                                aS[G][nt][4 * m + i] = E::from_f(pv * dP[G][m][nt][i]);  // dP holds dP - D
                             }
                         };
                         // dS stores.  DST ([key][query]): store k (0..7) = group, m, key
@@ -785,10 +774,10 @@ void bwd_main_kernel(KParams p) {
                         for (int G = 0; G < 2; ++G)
 #pragma unroll
                             for (int m = 0; m < 2; ++m) {
-                                // d = 64: dP starts at -D of the lane's rows
-                                f32x4 d0 = zero_vec<f32x4>();
-                                if constexpr (kDPFromD)
-                                    d0 = *reinterpret_cast<const f32x4*>(sdelta + (2 * G + m) * 16 + 4 * g);
+                                // dP's accumulation starts at -D of the lane's rows, so
+                                // dS = P (dP - D) is one multiply per element in the
+                                // softmax (the VALU work there does not shrink with d)
+                                const f32x4 d0 = *reinterpret_cast<const f32x4*>(sdelta + (2 * G + m) * 16 + 4 * g);
 #pragma unroll
                                 for (int nt = 0; nt < NT; ++nt) {
 #pragma unroll

@@ -346,10 +346,9 @@ void bwd_pair_kernel(KParams p) {
                     f32x4 S[2][2], dP[2][2];  // [m][nt]: rows qr0 + 16m.., keys 16nt..
 #pragma unroll
                     for (int m = 0; m < 2; ++m) {
-                        // d = 64: dP starts at -D of the lane's rows (as in the
-                        // four-wave kernel, so the two give the same bits)
-                        f32x4 d0 = zero_vec<f32x4>();
-                        if constexpr (D == 64) d0 = *reinterpret_cast<const f32x4*>(sdelta + qr0 + m * 16 + 4 * g);
+                        // dP starts at -D of the lane's rows (as in the four-wave
+                        // kernel, so the two give the same bits)
+                        const f32x4 d0 = *reinterpret_cast<const f32x4*>(sdelta + qr0 + m * 16 + 4 * g);
 #pragma unroll
                         for (int nt = 0; nt < 2; ++nt) {
 #pragma unroll
@@ -398,20 +397,15 @@ void bwd_pair_kernel(KParams p) {
                     V8 aP[2], aS[2];
 #pragma unroll
                     for (int m = 0; m < 2; ++m) {
-                        // lse * log2 e and -D of the lane's four rows of this half
+                        // lse * log2 e of the lane's four rows of this half
                         const f32x4 lsev = *reinterpret_cast<const f32x4*>(slse + qr0 + m * 16 + 4 * g);
-                        const f32x4 delv =
-                            D == 64 ? zero_vec<f32x4>() : *reinterpret_cast<const f32x4*>(sdelta + qr0 + m * 16 + 4 * g);
 #pragma unroll
                         for (int i = 0; i < 4; ++i)
 #pragma unroll
                             for (int nt = 0; nt < 2; ++nt) {
                                 const float pv = __builtin_amdgcn_exp2f(S[m][nt][i] * p.scale_log2 - lsev[i]);
                                 aP[nt][4 * m + i] = E::from_f(pv);
-                                if constexpr (D == 64)
-                                    aS[nt][4 * m + i] = E::from_f(pv * dP[m][nt][i]);
-                                else
-                                    aS[nt][4 * m + i] = E::from_f(pv * (dP[m][nt][i] + delv[i]));
+                                aS[nt][4 * m + i] = E::from_f(pv * dP[m][nt][i]);  // dP holds dP - D
                             }
                         __builtin_amdgcn_sched_barrier(0);
                     }
