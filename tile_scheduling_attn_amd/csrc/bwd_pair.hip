@@ -42,10 +42,11 @@
 // wave's explicit instruction schedule hides its softmax under its own MFMAs,
 // while here the two waves of a SIMD meet the exchange barrier together), the
 // reduction phase is faster (eight waves keep more accumulator loads and
-// stores in flight), and whole launches are about 3% faster under the causal
-// mask and 1-3% slower under the full mask, hence the default choice of the
-// library (the pair kernel under the causal mask at d = 128).  At d = 64 it
-// is 8-19% slower than the four-wave kernel of that head dimension.
+// stores in flight), and whole launches are 0-2% faster under the causal mask
+// (Descending most) and about 4% slower under the full mask, hence the
+// default choice of the library (the pair kernel under the causal mask at
+// d = 128).  At d = 64 it is 8-19% slower than the four-wave kernel of that
+// head dimension.
 //
 // Method: DASH (Deterministic Attention Scheduling), Fig. 1 of the paper as
 // captioned on the pith.science review page (tiled backward: dK/dV local to
