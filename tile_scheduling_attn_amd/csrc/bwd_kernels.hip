@@ -12,11 +12,13 @@ int launch_main_bf16_d64(const KParams& kp, const BwdLaunch& L, bool causal, boo
 // start dP's accumulation from it, so dP - D needs no subtraction)
 // and lse2[head][row] = lse * log2(e) (both zero for padded rows, the
 // softmax's exp2 argument then needs no multiply per use); clears the flags and counters of the call and, for the
-// atomic variant, the dQ accumulator.  Each lane reads 16 bytes of a row of
-// O and of dO (kPreLanes<T, D> lanes per row: 8 for bf16 at d = 64, where
-// 16 lanes of 8-byte reads took 12.4 us against 10.2 us at s = 2048, b*h = 64).
+// atomic variant, the dQ accumulator.  Each lane reads 32 bytes of a row of
+// O and of dO (kPreLanes<T, D> lanes per row: 4 for bf16 at d = 64, 8 at
+// d = 128).  Measured at s = 2048, d = 64, b*h = 64: 16 lanes of 8-byte reads
+// 12.4 us, 8 lanes of 16 bytes 10.2 us, 4 of 32 bytes 9.2 us; at s = 8192,
+// d = 128, b*h = 32: 31.5 us with 16-byte reads, 29.5 us with 32-byte ones.
 template <typename T, int D>
-constexpr int kPreLanes = D * (int)sizeof(T) / 16;
+constexpr int kPreLanes = D * (int)sizeof(T) / 32;
 template <typename T, int D>
 __global__ __launch_bounds__(256) void bwd_preprocess_kernel(const T* __restrict__ o, const T* __restrict__ dO,
                                                               const float* __restrict__ lse, float* __restrict__ delta,
