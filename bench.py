@@ -274,7 +274,7 @@ def main():
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print("bench.py measures one GPU only: heads are independent, so the path would shard "
-              "by heads across GPUs without communication, and this build runs on one GPU.",
+              "by heads across GPUs without communication; the benchmark is a one-GPU measurement.",
               file=sys.stderr)
         sys.exit(2)
 
